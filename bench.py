@@ -1,0 +1,264 @@
+"""Throughput of the W4A16 hot path on one MI355X.
+
+One step = one pass of every stage of the path over synthetic inputs shaped
+like the gate projection of a Qwen2.5-3B decoder layer (K = 2048, N = 11008,
+group 64):
+
+  pack     aq_quantize_pack of the bf16 weight                   (quantize + pack)
+  gemv     aq_w4a16_gemv at M = 1, once on each of 40 distinct   (decode; 40 copies =
+           packed weight copies, so every launch reads HBM         520 MB > the 256 MB MALL)
+  gemm     aq_w4a16_gemm at M = 4096                             (prefill, bf16 MFMA)
+  absmean  aq_act_absmean over 65536 x 2048 calibration tokens   (AWQ statistic)
+  search   aq_awq_search, 4096 tokens, 20 alphas, final pack     (AWQ search)
+  fp4      aq_fp4_gemm at M = 1 and M = 2048 on W[14336, 4096]   (FP4 decode)
+
+Every launch is bracketed by HIP events on the stream it runs on (torch's
+current stream, which the binding passes to the library).  The headline value
+is the decode GEMV's HBM throughput (algorithmic bytes / average launch
+duration); the GEMM's TFLOP/s and the other stages are reported beside it.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W4A16 GEMV GB/s (M=1) + GEMM TFLOP/s (M=4096), K=2048 N=11008 g=64"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+K_, N_, G_ = 2048, 11008, 64
+M_GEMM = 4096
+N_COPIES = 40
+FP4_N, FP4_K, FP4_M = 14336, 4096, 2048
+CAL_T, CAL_SUB = 65536, 4096
+
+
+def gemv_bytes(m, n, k, g):
+    return n * k // 2 + (n * k // g) * 5 + 2 * m * k + 4 * m * n
+
+
+def pack_bytes(n, k, g):
+    return 2 * n * k + n * k // 2 + (n * k // g) * 5
+
+
+def fp4_bytes(m, n, k):
+    return n * k // 2 + n * k // 16 + 2 * m * k + 4 * m * n
+
+
+def _source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_key, files, launches_bytes):
+    """HBM bytes per launch from the committed counter summary, if it matches the current source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(kernel_key)
+    if not ent or ent.get("source_hash") != _source_hash(files):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(budget_s=12.0):
+    """The CPU oracle, untuned, on a bounded sample of the same workload (decode GEMV at M = 1)."""
+    from oracle import int4
+    from weight_only_bit_group_amd import synth
+    try:
+        import threadpoolctl
+        threads = max(i["num_threads"] for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:  # pragma: no cover
+        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    wb = synth.layer_weight_bf16(1, "gate_proj")
+    w = synth.bf16_bits_to_f32(wb)
+    p, s, z = int4.quantize_pack(w, G_)
+    x = synth.bf16_bits_to_f32(synth.layer_activations_bf16(1, 1, K_))
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        int4.forward(x, p, s, z, G_)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or calls >= 200:
+            break
+    gbs = calls * gemv_bytes(1, N_, K_, G_) / el / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"oracle.int4.forward (fp64 dequantize + matvec) on the gate shape at M=1, "
+                      f"{calls} calls in {el:.1f} s on {len(os.sched_getaffinity(0))} visible host cores "
+                      f"(numpy elementwise single-threaded, BLAS {threads} threads)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the W4A16 path has no multi-GPU mode here (asked for --gpus {args.gpus}); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from weight_only_bit_group_amd import binding as B
+    from weight_only_bit_group_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    print("[bench] setup", flush=True)
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+
+    def weight_bf16(n, k):
+        w = torch.randn((n, k), generator=gen, device=dev, dtype=torch.float32) * 0.02
+        idx = torch.randint(0, n * k, (max(1, n * k // 1000),), generator=gen, device=dev)
+        w.view(-1)[idx] *= 10.0
+        return w.to(torch.bfloat16)
+
+    def acts_bf16(m, k, outlier_ch, scale=20.0):
+        x = torch.randn((m, k), generator=gen, device=dev, dtype=torch.float32)
+        ch = torch.randperm(k, generator=gen, device=dev)[:outlier_ch]
+        x[:, ch] *= scale
+        return x.to(torch.bfloat16)
+
+    # weights: the gate projection and 40 distinct packed copies for the rotating GEMV
+    w_gate = weight_bf16(N_, K_)
+    copies = []
+    for i in range(N_COPIES):
+        copies.append(B.aq_quantize_pack(w_gate if i == 0 else weight_bf16(N_, K_), G_))
+    torch.cuda.synchronize()
+    x1 = acts_bf16(1, K_, round(0.01 * K_))
+    y1 = torch.empty((1, N_), dtype=torch.float32, device=dev)
+    xg = acts_bf16(M_GEMM, K_, round(0.01 * K_))
+    yg = torch.empty((M_GEMM, N_), dtype=torch.float32, device=dev)
+    pk = [torch.empty_like(t) for t in copies[0]]
+    # calibration activations: z * c_k, c_k = exp(1.5 N(0,1))
+    ck = torch.exp(1.5 * torch.randn(K_, generator=gen, device=dev))
+    xcal = (torch.randn((CAL_T, K_), generator=gen, device=dev) * ck).to(torch.bfloat16)
+    sum_abs = torch.zeros(K_, dtype=torch.float64, device=dev)
+    mean = torch.empty(K_, dtype=torch.float32, device=dev)
+    ws_abs = torch.empty(B.aq_act_absmean_workspace(CAL_T, K_), dtype=torch.uint8, device=dev)
+    B.aq_act_absmean(xcal, sum_abs, CAL_T, mean, ws_abs)
+    absmean_host = mean.cpu().numpy().copy()
+    xsub = xcal[:CAL_SUB].contiguous()
+    ws_search = torch.empty(B.aq_awq_search_workspace(CAL_SUB, N_, K_, G_, 20), dtype=torch.uint8, device=dev)
+    codes_np, bsc_np, ts = synth.random_fp4_operands(5, FP4_N, FP4_K)
+    codes = torch.from_numpy(codes_np).to(dev)
+    bsc = torch.from_numpy(bsc_np).to(dev)
+    xf1 = acts_bf16(1, FP4_K, round(0.01 * FP4_K))
+    xf2 = acts_bf16(FP4_M, FP4_K, round(0.01 * FP4_K))
+    yf1 = torch.empty((1, FP4_N), dtype=torch.float32, device=dev)
+    yf2 = torch.empty((FP4_M, FP4_N), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    events = {k: [] for k in ("pack", "gemv", "gemm", "absmean", "search", "fp4_gemv", "fp4_gemm")}
+
+    def timed(name, record, fn):
+        if record:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            events[name].append((a, b))
+        else:
+            fn()
+
+    def step(record):
+        timed("pack", record, lambda: B.aq_quantize_pack(w_gate, G_, packed=pk[0], scales=pk[1], zeros=pk[2]))
+        for (p, s, z) in copies:
+            timed("gemv", record, lambda p=p, s=s, z=z: B.aq_w4a16_gemv(x1, p, s, z, G_, out=y1))
+        p, s, z = copies[0]
+        timed("gemm", record, lambda: B.aq_w4a16_gemm(xg, p, s, z, G_, out=yg))
+        sum_abs.zero_()
+        timed("absmean", record, lambda: B.aq_act_absmean(xcal, sum_abs, CAL_T, mean, ws_abs))
+        timed("search", record, lambda: B.aq_awq_search(xsub, absmean_host, w_gate, G_, 20, ws_search))
+        timed("fp4_gemv", record, lambda: B.aq_fp4_gemm(xf1, codes, bsc, ts, out=yf1))
+        timed("fp4_gemm", record, lambda: B.aq_fp4_gemm(xf2, codes, bsc, ts, out=yf2))
+
+    print(f"[bench] warmup {args.warmup}", flush=True)
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", flush=True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print("[bench] timed region done", flush=True)
+
+    ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in events.items()}
+    gemv_b = gemv_bytes(1, N_, K_, G_)
+    gemv_gbs = gemv_b / (ms["gemv"] * 1e-3) / 1e9
+    gemm_flop = 2.0 * M_GEMM * N_ * K_
+    gemm_tf = gemm_flop / (ms["gemm"] * 1e-3) / 1e12
+    search_flop = 20 * 2.0 * CAL_SUB * N_ * K_
+    rows = {
+        "pack": {"us": ms["pack"] * 1e3, "GB/s": pack_bytes(N_, K_, G_) / (ms["pack"] * 1e-3) / 1e9},
+        "gemv_m1": {"us": ms["gemv"] * 1e3, "GB/s": gemv_gbs},
+        "gemm_m4096": {"us": ms["gemm"] * 1e3, "TFLOP/s": gemm_tf},
+        "absmean": {"us": ms["absmean"] * 1e3, "GB/s": 2.0 * CAL_T * K_ / (ms["absmean"] * 1e-3) / 1e9},
+        "awq_search": {"ms": ms["search"], "TFLOP/s": search_flop / (ms["search"] * 1e-3) / 1e12},
+        "fp4_gemv_m1": {"us": ms["fp4_gemv"] * 1e3,
+                        "GB/s": fp4_bytes(1, FP4_N, FP4_K) / (ms["fp4_gemv"] * 1e-3) / 1e9},
+        "fp4_gemm_m2048": {"us": ms["fp4_gemm"] * 1e3,
+                           "TFLOP/s": 2.0 * FP4_M * FP4_N * FP4_K / (ms["fp4_gemm"] * 1e-3) / 1e12},
+    }
+    rows = {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in rows.items()}
+    gemv_src = ["weight_only_bit_group_amd/csrc/w4a16_gemv.hip", "weight_only_bit_group_amd/csrc/aq_device.h"]
+    gemm_src = ["weight_only_bit_group_amd/csrc/mfma_gemm.hip", "weight_only_bit_group_amd/csrc/aq_device.h"]
+    out = {
+        "metric": METRIC,
+        "value": round(gemv_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Qwen2.5-3B gate_proj W4A16: K=2048 N=11008 g=64; GEMV M=1 over 40 rotating "
+                               "packed copies, GEMM M=4096, abs-mean 65536x2048, AWQ search T=4096 x 20 alphas, "
+                               "FP4 [14336,4096] M=1/2048",
+                   "K": K_, "N": N_, "group": G_, "gemv_M": 1, "gemm_M": M_GEMM, "rotating_copies": N_COPIES},
+        "roofline": {"bound": "hbm", "achieved": round(gemv_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gemv_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": _traffic("w4a16_gemv_m1", gemv_src, gemv_b)},
+        "gemm": {"value": round(gemm_tf, 2), "unit": "TFLOP/s",
+                 "roofline": {"bound": "mfma", "achieved": round(gemm_tf, 2), "peak": BF16_PEAK_TFLOPS,
+                              "unit": "TFLOP/s", "frac": round(gemm_tf / BF16_PEAK_TFLOPS, 4),
+                              "traffic": _traffic("w4a16_gemm_m4096", gemm_src, None)}},
+        "rows": rows,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", flush=True)
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,182 @@
+/*
+ * libaq -- group-wise INT4 (W4A16) weight quantization, AWQ calibration and an
+ * FP4 decode path for AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * Conventions shared by every entry point
+ *   - Tensor arguments are DEVICE pointers owned by the caller (the library
+ *     never allocates or frees device memory; calls that need scratch space take
+ *     a caller-provided workspace sized by the matching *_workspace() query).
+ *     The only host pointer is `absmean_host` of aq_awq_search.
+ *   - Every tensor is row-major and dense.  bf16 tensors are passed as uint16_t
+ *     bit patterns.  Weights follow the linear-layer convention W[N, K]
+ *     (N = out features, K = in features, K contiguous).
+ *   - Quantized INT4 weights ("packed triple"):
+ *       packed [N, K/2] uint8 : two 4-bit codes per byte, k even in the low
+ *                               nibble, k odd in the high nibble;
+ *       scales [N, K/g] fp32  : the group step S;
+ *       zeros  [N, K/g] uint8 : the zero point z, 0..15;
+ *     groups are g consecutive k inside one row, g in {32, 64, 128}; the
+ *     dequantized weight is (q - z) * S.
+ *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL is
+ *     the default stream).  Only aq_awq_search synchronises `stream`, once, to
+ *     upload its candidate scales.
+ *   - Status codes mirror the 0 / 1 / 2 exit-code convention of the llm-quantize
+ *     CLI ("模型量化指南", blog.yoooo.fun, section "用 CLI 量化", exit-code convention): AQ_OK; AQ_EINVAL when an
+ *     argument fails validation -- validation runs before any launch, so on
+ *     AQ_EINVAL no output byte is written; AQ_ERUNTIME when the HIP runtime
+ *     reports a launch or copy failure.  aq_last_error() returns a thread-local
+ *     description of the last non-OK status.
+ *   - Pointers must be non-NULL (unless stated) and aligned: 16 bytes for X, W,
+ *     packed, codes, chan_scale and workspaces; 8 for fp64 outputs; 4 for other
+ *     fp32 / int32 tensors.
+ *   - Inputs must be finite (documented precondition, not checked).
+ *   - An empty output dimension (N == 0, or M == 0 for the products) is a valid
+ *     no-op.
+ */
+#ifndef AQ_H_
+#define AQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { AQ_OK = 0, AQ_EINVAL = 1, AQ_ERUNTIME = 2 } aq_status;
+typedef enum { AQ_F32 = 0, AQ_BF16 = 1 } aq_dtype;
+
+/*
+ * Group-wise asymmetric INT4 quantization and packing.
+ * Source: "Quantization：模型量化" (xingyuwang.me), section 2 (asymmetric
+ * quantization q = round(x/s) + z, dequantization (q - z) s, clipping to the
+ * integer range) and section 3 (per-group scales); "Lance-Quant" (zingnex.cn),
+ * grid-search / grouping section (INT4 packed by groups; min-max when no
+ * activation statistics exist; o_proj / down_proj get plain group quantization).
+ *
+ * For every row n and group j of g consecutive k:
+ *   v_k = fl32(w_nk * chan_scale[k])   (v_k = w_nk when chan_scale == NULL)
+ *   S = fl32(fl32(max v - min v) / 15), z = clamp(rne(fl32(-min v / S)), 0, 15),
+ *   q_k = clamp(rne(fl32(v_k / S)) + z, 0, 15); a constant group stores
+ *   S = 0, z = 0, q = 0.  Divisions are IEEE fp32, rounding is half-to-even.
+ *
+ * W          [N, K] fp32 or bf16 (w_dtype), device
+ * chan_scale [K] fp32 AWQ scale, device, or NULL
+ * packed/scales/zeros: the packed triple (outputs), device
+ * Errors: EINVAL for bad dtype, group not in {32,64,128}, K <= 0 or K % group,
+ *         NULL / misaligned pointers, N < 0.
+ */
+aq_status aq_quantize_pack(const void* W, int32_t w_dtype, int64_t N, int64_t K, int32_t group,
+                           const float* chan_scale, uint8_t* packed, float* scales, uint8_t* zeros,
+                           void* stream);
+
+/*
+ * W4A16 decode GEMV, 1 <= M <= 16 activation rows.  VALU kernel, HBM-bound.
+ * Source: "模型量化指南" (blog.yoooo.fun), common conventions (the packed linear
+ * dequantizes in memory and equals the original layer with W replaced by its
+ * dequantized value); "Quantization：模型量化" (xingyuwang.me), sections 4 (W4A16)
+ * and 13 (compressed weights are read, dequantized inside the kernel, then
+ * contracted; decode is memory-bound).
+ *
+ *   Y[m, n] = sum_g S[n,g] * sum_{k in g} X[m,k] * (q[n,k] - z[n,g])  (fp32)
+ *
+ * X [M, K] bf16, device; packed triple for W[N, K]; Y [M, N] fp32 (output).
+ * Errors: EINVAL for M outside 1..16, group not in {32,64,128}, K <= 0 or
+ *         K % group, N < 0, NULL / misaligned pointers, K or N >= 2^30.
+ */
+aq_status aq_w4a16_gemv(const uint16_t* X, int64_t M, int64_t K, const uint8_t* packed, const float* scales,
+                        const uint8_t* zeros, int64_t N, int32_t group, float* Y, void* stream);
+
+/*
+ * W4A16 prefill GEMM, any M >= 0 (tuned for M >= 64): bf16 MFMA on the exact
+ * integer operand (q - z), fp32 group-step rescale per group, fp32 output.
+ * Same sources, arguments and formula as aq_w4a16_gemv.
+ * Errors: EINVAL for M < 0 or M >= 2^30, and as aq_w4a16_gemv otherwise.
+ */
+aq_status aq_w4a16_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_t* packed, const float* scales,
+                        const uint8_t* zeros, int64_t N, int32_t group, float* Y, void* stream);
+
+/*
+ * Per-input-channel |x| statistic for AWQ calibration.
+ * Source: "Lance-Quant" (zingnex.cn), calibration section (hooks store each
+ * input channel's average absolute activation; statistics of several runs are
+ * merged); "BNB/GPTQ/AWQ量化全面支持" (maplevalley.com.cn), AWQ paragraph.
+ *
+ *   sum_abs[k] += sum_{t < T} |X[t, k]|        (fp64, ACCUMULATED: the caller
+ *                                               zeroes sum_abs once, then feeds
+ *                                               chunks / tasks)
+ *   mean_out[k] = fl32(sum_abs[k] / total_count)   (skipped when mean_out == NULL)
+ *
+ * X [T, K] bf16, device; sum_abs [K] fp64, device; mean_out [K] fp32 or NULL;
+ * total_count = tokens accumulated so far including this chunk (>= T);
+ * workspace >= aq_act_absmean_workspace(T, K) bytes, device.
+ * Partial sums are reduced in a fixed order: results are deterministic.
+ * Errors: EINVAL for T <= 0 (empty calibration data), K <= 0 or K % 8,
+ *         total_count < T, small workspace, NULL / misaligned pointers.
+ */
+size_t aq_act_absmean_workspace(int64_t T, int64_t K);
+aq_status aq_act_absmean(const uint16_t* X, int64_t T, int64_t K, double* sum_abs, float* mean_out,
+                         int64_t total_count, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * AWQ alpha-grid search and final packing.
+ * Source: "Lance-Quant" (zingnex.cn), grid-search / grouping section (grid
+ * search of the AWQ scale for a norm and its consuming linears, then INT4 group
+ * packing); "Quantization：模型量化" (xingyuwang.me), section 7 (AWQ uses activation
+ * statistics to protect salient channels by scaling); OmniQuant tutorial
+ * (cyqw.cn), section 2.2.2 (the per-channel equivalent transform is exact).
+ *
+ * For i = 0 .. n_grid-1, alpha = i / n_grid:
+ *   t_k = max(absmean_host[k], 1e-8)^alpha      (fp64 libm pow, on the host)
+ *   s_k = fl32(t_k / sqrt(max t * min t))
+ *   E   = Q(W diag(s)) / s - W                   (Q: aq_quantize_pack + dequant)
+ *   mse[i] = mean over (t, n) of (X_sub E^T)[t, n]^2
+ *          (= output MSE of (X/s) Q(W s)^T against X W^T)
+ * best[0] = first index of the minimum; best_scale = s of that index;
+ * packed/scales/zeros = aq_quantize_pack(W, chan_scale = best_scale).
+ * E is formed in fp32 and split into two bf16 planes (hi + lo, ~16 significant
+ * bits) for the bf16-MFMA product; the MSE is accumulated in fp64 with a fixed
+ * reduction order.
+ *
+ * X_sub [T, K] bf16, device; absmean_host [K] fp32, HOST; W [N, K] fp32/bf16,
+ * device; mse [n_grid] fp64, best [1] int32, best_scale [K] fp32 and the packed
+ * triple are device outputs; workspace >= aq_awq_search_workspace(...) bytes.
+ * Synchronises `stream` once (candidate-scale upload) before the first launch.
+ * Errors: EINVAL for T <= 0 (empty calibration data), n_grid outside 1..64,
+ *         K % group, group not in {32,64,128}, small workspace, NULL /
+ *         misaligned pointers, non-finite or negative absmean values.
+ */
+size_t aq_awq_search_workspace(int64_t T, int64_t N, int64_t K, int32_t group, int32_t n_grid);
+aq_status aq_awq_search(const uint16_t* X_sub, int64_t T, const float* absmean_host, const void* W,
+                        int32_t w_dtype, int64_t N, int64_t K, int32_t group, int32_t n_grid, double* mse,
+                        int32_t* best, float* best_scale, uint8_t* packed, float* scales, uint8_t* zeros,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * FP4 decode product: E2M1 codes with an FP8-E4M3 scale per 16-element block
+ * and an fp32 tensor scale.  M <= 16 runs a VALU GEMV, larger M a bf16-MFMA
+ * GEMM; both use the exact bf16 value e2m1 * e4m3.
+ * Source: "Lance-Quant" (zingnex.cn), grid-search / grouping section (NVFP4 =
+ * E2M1 codes + FP8 E4M3 scale per 16 elements, block_size 16);
+ * "Quantization：模型量化" (xingyuwang.me), section 12 (E4M3 = 1 + 4 + 3 bits).
+ *
+ *   Y[m, n] = tensor_scale * sum_k X[m, k] * e2m1(c[n, k]) * e4m3(b[n, k / 16])
+ *
+ * X [M, K] bf16; codes [N, K/2] uint8 (k even in the low nibble; bit 3 of a
+ * code is the sign, bits 2..1 the exponent with bias 1, bit 0 the mantissa);
+ * block_scales [N, K/16] uint8 E4M3 (OCP "FN": bias 7, no infinities, 0x7F /
+ * 0xFF are NaN); Y [M, N] fp32 output.
+ * Errors: EINVAL for M < 0, K <= 0 or K % 32, non-finite tensor_scale, N < 0,
+ *         NULL / misaligned pointers, K or N >= 2^30.
+ */
+aq_status aq_fp4_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes, const uint8_t* block_scales,
+                      float tensor_scale, int64_t N, float* Y, void* stream);
+
+/* Thread-local text for the last non-OK status of this thread ("" if none). */
+const char* aq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AQ_H_ */

@@ -1,0 +1,172 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library loads, exports every entry point the header declares, rejects
+invalid arguments with AQ_EINVAL before touching the GPU, and reports the
+injected runtime failure with AQ_ERUNTIME.  None of these calls launches a
+kernel: validation precedes every launch, and the fault switch returns before
+any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from weight_only_bit_group_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "aq.h")
+
+FAKE = 0x10000          # 64 KiB-aligned fake device address (never dereferenced)
+FAKE_ODD = 0x10002      # misaligned fake address
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(aq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("aq_quantize_pack", "aq_w4a16_gemv", "aq_w4a16_gemm", "aq_act_absmean", "aq_awq_search",
+              "aq_fp4_gemm", "aq_last_error"):
+        assert n in names
+    assert set(names) == set(_lib.SIGNATURES), "binding prototypes must mirror the header"
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+    out = os.popen(f"nm -D --defined-only {_lib.LIB_PATH}").read()
+    for name in _declared():
+        assert re.search(rf"\bT {name}\b", out), name
+
+
+def _qp(lib, **kw):
+    a = dict(W=FAKE, dt=1, N=16, K=128, g=64, s=None, p=FAKE, sc=FAKE, z=FAKE)
+    a.update(kw)
+    return lib.aq_quantize_pack(a["W"], a["dt"], a["N"], a["K"], a["g"], a["s"], a["p"], a["sc"], a["z"], None)
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(g=48), "group"), (dict(g=256), "group"), (dict(K=96), "multiple"), (dict(K=0), "K"),
+    (dict(N=-1), "N"), (dict(dt=7), "dtype"), (dict(W=None), "W"), (dict(W=FAKE_ODD), "aligned"),
+    (dict(p=None), "packed"), (dict(s=FAKE_ODD), "chan_scale"), (dict(K=1 << 31), "K"),
+])
+def test_quantize_pack_einval(lib, kw, frag):
+    assert _qp(lib, **kw) == _lib.AQ_EINVAL
+    assert frag in _lib.last_error()
+
+
+def _prod(lib, fn, **kw):
+    a = dict(X=FAKE, M=1, K=256, P=FAKE, S=FAKE, Z=FAKE, N=64, g=64, Y=FAKE)
+    a.update(kw)
+    return getattr(lib, fn)(a["X"], a["M"], a["K"], a["P"], a["S"], a["Z"], a["N"], a["g"], a["Y"], None)
+
+
+@pytest.mark.parametrize("kw", [dict(M=0), dict(M=17), dict(g=16), dict(K=100), dict(X=None), dict(X=FAKE_ODD),
+                                dict(P=FAKE + 8), dict(Y=None), dict(N=-3), dict(Y=FAKE + 2)])
+def test_gemv_einval(lib, kw):
+    assert _prod(lib, "aq_w4a16_gemv", **kw) == _lib.AQ_EINVAL
+
+
+@pytest.mark.parametrize("kw", [dict(M=-1), dict(g=16), dict(K=100), dict(S=None), dict(Z=None), dict(K=0)])
+def test_gemm_einval(lib, kw):
+    assert _prod(lib, "aq_w4a16_gemm", **kw) == _lib.AQ_EINVAL
+
+
+def test_empty_products_are_noops(lib):
+    assert _prod(lib, "aq_w4a16_gemm", M=0) == _lib.AQ_OK
+    assert _prod(lib, "aq_w4a16_gemm", N=0) == _lib.AQ_OK
+    assert _prod(lib, "aq_w4a16_gemv", N=0) == _lib.AQ_OK
+    assert _qp(lib, N=0) == _lib.AQ_OK
+    assert lib.aq_fp4_gemm(FAKE, 0, 64, FAKE, FAKE, 1.0, 8, FAKE, None) == _lib.AQ_OK
+
+
+def test_absmean_einval(lib):
+    ws = lib.aq_act_absmean_workspace(1024, 256)
+    assert ws > 0
+    f = lib.aq_act_absmean
+    assert f(FAKE, 0, 256, FAKE, None, 0, FAKE, ws, None) == _lib.AQ_EINVAL        # empty calibration data
+    assert "empty calibration" in _lib.last_error()
+    assert f(FAKE, 1024, 250, FAKE, None, 1024, FAKE, ws, None) == _lib.AQ_EINVAL   # K % 8
+    assert f(FAKE, 1024, 256, FAKE, None, 100, FAKE, ws, None) == _lib.AQ_EINVAL    # count < T
+    assert f(FAKE, 1024, 256, FAKE, None, 1024, FAKE, ws - 8, None) == _lib.AQ_EINVAL
+    assert f(FAKE, 1024, 256, FAKE + 4, None, 1024, FAKE, ws, None) == _lib.AQ_EINVAL
+    assert f(FAKE, 1024, 256, FAKE, FAKE + 1, 1024, FAKE, ws, None) == _lib.AQ_EINVAL
+
+
+def test_search_einval(lib):
+    T, N, K, g, ng = 64, 32, 128, 64, 20
+    ws = lib.aq_awq_search_workspace(T, N, K, g, ng)
+    assert ws > 0
+    m = np.ones(K, np.float32)
+    mp = m.ctypes.data
+
+    def call(**kw):
+        a = dict(X=FAKE, T=T, m=mp, W=FAKE, dt=1, N=N, K=K, g=g, ng=ng, mse=FAKE, best=FAKE, bs=FAKE,
+                 p=FAKE, sc=FAKE, z=FAKE, ws=FAKE, wsb=ws)
+        a.update(kw)
+        return lib.aq_awq_search(a["X"], a["T"], a["m"], a["W"], a["dt"], a["N"], a["K"], a["g"], a["ng"], a["mse"],
+                                 a["best"], a["bs"], a["p"], a["sc"], a["z"], a["ws"], a["wsb"], None)
+
+    assert call(T=0) == _lib.AQ_EINVAL and "empty calibration" in _lib.last_error()
+    assert call(ng=0) == _lib.AQ_EINVAL
+    assert call(ng=65) == _lib.AQ_EINVAL
+    assert call(K=96) == _lib.AQ_EINVAL
+    assert call(wsb=ws - 1) == _lib.AQ_EINVAL and "workspace" in _lib.last_error()
+    assert call(m=None) == _lib.AQ_EINVAL
+    assert call(ws=FAKE + 16) == _lib.AQ_EINVAL
+    bad = m.copy()
+    bad[5] = np.nan
+    assert call(m=bad.ctypes.data) == _lib.AQ_EINVAL
+    bad[5] = -1
+    assert call(m=bad.ctypes.data) == _lib.AQ_EINVAL
+    assert lib.aq_awq_search_workspace(0, N, K, g, ng) == 0
+
+
+def test_fp4_einval(lib):
+    f = lib.aq_fp4_gemm
+    assert f(FAKE, 1, 48, FAKE, FAKE, 1.0, 8, FAKE, None) == _lib.AQ_EINVAL     # K % 32
+    assert f(FAKE, 1, 64, FAKE, FAKE, float("inf"), 8, FAKE, None) == _lib.AQ_EINVAL
+    assert f(FAKE, 1, 64, FAKE, FAKE, float("nan"), 8, FAKE, None) == _lib.AQ_EINVAL
+    assert f(FAKE, -1, 64, FAKE, FAKE, 1.0, 8, FAKE, None) == _lib.AQ_EINVAL
+    assert f(FAKE, 1, 64, FAKE_ODD, FAKE, 1.0, 8, FAKE, None) == _lib.AQ_EINVAL
+
+
+def test_injected_runtime_failure(lib, monkeypatch):
+    """AQ_FAULT_INJECT=launch: valid arguments, no GPU touched, status 2 (runtime failure)."""
+    monkeypatch.setenv("AQ_FAULT_INJECT", "launch")
+    assert _qp(lib) == _lib.AQ_ERUNTIME
+    assert "injected" in _lib.last_error()
+    assert _prod(lib, "aq_w4a16_gemv") == _lib.AQ_ERUNTIME
+    assert _prod(lib, "aq_w4a16_gemm", M=128) == _lib.AQ_ERUNTIME
+    assert lib.aq_fp4_gemm(FAKE, 1, 64, FAKE, FAKE, 1.0, 8, FAKE, None) == _lib.AQ_ERUNTIME
+    ws = lib.aq_act_absmean_workspace(64, 64)
+    assert lib.aq_act_absmean(FAKE, 64, 64, FAKE, None, 64, FAKE, ws, None) == _lib.AQ_ERUNTIME
+    # validation still wins over the injected fault
+    assert _qp(lib, g=5) == _lib.AQ_EINVAL
+
+
+def test_status_mapping_in_python(lib):
+    with pytest.raises(ValueError):
+        _lib.check(_lib.AQ_EINVAL, "x")
+    with pytest.raises(RuntimeError):
+        _lib.check(_lib.AQ_ERUNTIME, "x")
+    _lib.check(_lib.AQ_OK, "x")
+
+
+def test_last_error_is_thread_local(lib):
+    import threading
+    assert _qp(lib, g=5) == _lib.AQ_EINVAL
+    seen = {}
+
+    def worker():
+        seen["msg"] = ctypes.string_at(lib.aq_last_error()).decode() if lib.aq_last_error() else ""
+    th = threading.Thread(target=worker)
+    th.start()
+    th.join()
+    assert seen["msg"] == ""
+    assert "group" in _lib.last_error()

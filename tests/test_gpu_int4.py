@@ -1,0 +1,216 @@
+"""GPU parity: INT4 quantize/pack (bit-exact) and the W4A16 GEMV / GEMM (tolerance, and
+bit-exact on an exactly representable case), through the C ABI, against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import int4
+from tests.gpu_util import check_close, dev, dev_bf16, host, step
+from weight_only_bit_group_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu(lib):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from weight_only_bit_group_amd import binding
+    globals()["B"] = binding
+
+
+def _pack_gpu(w_dev, g, s_dev=None):
+    p, s, z = B.aq_quantize_pack(w_dev, g, s_dev)
+    return host(p), host(s), host(z)
+
+
+def _assert_pack_equal(got, want, what):
+    (p, s, z), (p0, s0, z0) = got, want
+    bad_p = int(np.count_nonzero(p != p0))
+    bad_s = int(np.count_nonzero(s.view(np.uint32) != s0.view(np.uint32)))
+    bad_z = int(np.count_nonzero(z != z0))
+    print(f"[gpu] {what}: mismatching packed bytes {bad_p}, scales {bad_s}, zeros {bad_z}", flush=True)
+    assert bad_p == 0 and bad_s == 0 and bad_z == 0
+
+
+# ---------------------------------------------------------------- quantize / pack
+
+def test_pack_single_linear_fp32():
+    case = synth.single_linear(0)
+    step("aq_quantize_pack fp32 256x256 g=128")
+    got = _pack_gpu(dev(case["W"]), 128)
+    _assert_pack_equal(got, int4.quantize_pack(case["W"], 128), "single linear")
+
+
+@pytest.mark.parametrize("g", [64, 128])
+def test_pack_decoder_layer_bf16(g):
+    for name, n, k in synth.LAYER_LINEARS:
+        wb = synth.layer_weight_bf16(1, name)
+        step(f"aq_quantize_pack bf16 {name} [{n},{k}] g={g}")
+        got = _pack_gpu(dev_bf16(wb), g)
+        _assert_pack_equal(got, int4.quantize_pack(synth.bf16_bits_to_f32(wb), g), f"{name} g={g}")
+
+
+def _edge_matrix(rng, n, k, g):
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    vg = w.reshape(n, k // g, g)
+    vg[0, 0] = 0.25                                   # constant group
+    if vg.shape[1] > 1:
+        vg[0, 1] = np.abs(vg[0, 1]) + 1.0             # all positive (z clamps to 0)
+    if n > 1:
+        vg[1, 0] = -np.abs(vg[1, 0]) - 1.0            # all negative (z clamps to 15)
+    if n > 2:                                         # half-integer ties with odd zero point
+        vg[2, 0] = (rng.integers(-10, 21, g) * 0.5).astype(np.float32)
+        vg[2, 0, 0], vg[2, 0, 1] = -5.0, 10.0
+    if n > 3:
+        vg[3, 0] = 0.0                                # all-zero group
+        vg[3, -1] *= np.float32(1e-30)                # tiny range
+    return w
+
+
+@pytest.mark.parametrize("n,k,g", [(1, 32, 32), (3, 64, 32), (37, 192, 64), (5, 384, 128), (257, 128, 64)])
+def test_pack_edge_cases(n, k, g):
+    rng = np.random.default_rng(n * 1000 + k + g)
+    w = _edge_matrix(rng, n, k, g)
+    step(f"aq_quantize_pack edge fp32 [{n},{k}] g={g}")
+    _assert_pack_equal(_pack_gpu(dev(w), g), int4.quantize_pack(w, g), f"edge fp32 [{n},{k}] g={g}")
+    wb = synth.f32_to_bf16_bits(w)
+    step(f"aq_quantize_pack edge bf16 [{n},{k}] g={g}")
+    _assert_pack_equal(_pack_gpu(dev_bf16(wb), g), int4.quantize_pack(synth.bf16_bits_to_f32(wb), g),
+                       f"edge bf16 [{n},{k}] g={g}")
+
+
+@pytest.mark.parametrize("wdtype", ["f32", "bf16"])
+def test_pack_with_channel_scale(wdtype):
+    rng = np.random.default_rng(7)
+    n, k, g = 96, 512, 64
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    s = np.exp(rng.standard_normal(k) * 0.7).astype(np.float32)
+    if wdtype == "bf16":
+        wb = synth.f32_to_bf16_bits(w)
+        w = synth.bf16_bits_to_f32(wb)
+        wd = dev_bf16(wb)
+    else:
+        wd = dev(w)
+    step(f"aq_quantize_pack with chan_scale {wdtype} [{n},{k}]")
+    _assert_pack_equal(_pack_gpu(wd, g, dev(s)), int4.quantize_pack(w, g, s), f"scaled {wdtype}")
+
+
+# ---------------------------------------------------------------- GEMV
+
+def _quantized_layer(seed, name, g):
+    wb = synth.layer_weight_bf16(seed, name)
+    p, s, z = int4.quantize_pack(synth.bf16_bits_to_f32(wb), g)
+    return p, s, z
+
+
+def test_gemv_single_linear():
+    case = synth.single_linear(0)
+    p, s, z = int4.quantize_pack(case["W"], 128)
+    step("aq_w4a16_gemv 256x256 g=128 M=8")
+    y = host(B.aq_w4a16_gemv(dev_bf16(case["X"]), dev(p), dev(s), dev(z), 128))
+    check_close(y, int4.forward(synth.bf16_bits_to_f32(case["X"]), p, s, z, 128), "gemv single linear M=8")
+
+
+@pytest.mark.parametrize("g", [64, 128])
+def test_gemv_decoder_layer(g):
+    for name, n, k in synth.LAYER_LINEARS:
+        p, s, z = _quantized_layer(2, name, g)
+        dp, ds, dz = dev(p), dev(s), dev(z)
+        for m in (1, 4, 16):
+            xb = synth.layer_activations_bf16(2, m, k)
+            step(f"aq_w4a16_gemv {name} [{n},{k}] g={g} M={m}")
+            y = host(B.aq_w4a16_gemv(dev_bf16(xb), dp, ds, dz, g))
+            check_close(y, int4.forward(synth.bf16_bits_to_f32(xb), p, s, z, g), f"gemv {name} g={g} M={m}")
+
+
+def _exact_case(rng, m, n, k, g):
+    """Integer X (|x| <= 64) and S = 2^-6: every product and partial sum is exact in fp32."""
+    x = rng.integers(-64, 65, (m, k)).astype(np.float32)
+    q = rng.integers(0, 16, (n, k)).astype(np.uint8)
+    z = rng.integers(0, 16, (n, k // g)).astype(np.uint8)
+    s = np.full((n, k // g), 2.0 ** -6, dtype=np.float32)
+    return synth.f32_to_bf16_bits(x), x, int4.pack_nibbles(q), s, z
+
+
+@pytest.mark.parametrize("m,n,k,g", [(1, 64, 256, 64), (5, 33, 128, 32), (16, 130, 1024, 128)])
+def test_gemv_exact_integer_case(m, n, k, g):
+    xb, x, p, s, z = _exact_case(np.random.default_rng(m + n + k), m, n, k, g)
+    step(f"aq_w4a16_gemv exact-integer M={m} N={n} K={k} g={g}")
+    y = host(B.aq_w4a16_gemv(dev_bf16(xb), dev(p), dev(s), dev(z), g))
+    ref = int4.forward(x, p, s, z, g)
+    assert (y.astype(np.float64) == ref).all()
+
+
+@pytest.mark.parametrize("m,n,k,g", [(1, 1, 32, 32), (2, 7, 96, 32), (3, 4099, 320, 64), (16, 8200, 64, 64)])
+def test_gemv_ragged_shapes(m, n, k, g):
+    rng = np.random.default_rng(n)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    p, s, z = int4.quantize_pack(w, g)
+    xb = synth.f32_to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+    step(f"aq_w4a16_gemv ragged M={m} N={n} K={k} g={g}")
+    y = host(B.aq_w4a16_gemv(dev_bf16(xb), dev(p), dev(s), dev(z), g))
+    check_close(y, int4.forward(synth.bf16_bits_to_f32(xb), p, s, z, g), f"gemv ragged {m}x{n}x{k}")
+
+
+# ---------------------------------------------------------------- GEMM
+
+def test_gemm_single_linear():
+    case = synth.single_linear(0)
+    p, s, z = int4.quantize_pack(case["W"], 128)
+    step("aq_w4a16_gemm 256x256 g=128 M=8")
+    y = host(B.aq_w4a16_gemm(dev_bf16(case["X"]), dev(p), dev(s), dev(z), 128))
+    check_close(y, int4.forward(synth.bf16_bits_to_f32(case["X"]), p, s, z, 128), "gemm single linear M=8")
+
+
+def test_gemm_prefill_layer_m512():
+    for name, n, k in synth.LAYER_LINEARS:
+        p, s, z = _quantized_layer(3, name, 64)
+        xb = synth.layer_activations_bf16(3, 512, k)
+        step(f"aq_w4a16_gemm {name} [{n},{k}] g=64 M=512")
+        y = host(B.aq_w4a16_gemm(dev_bf16(xb), dev(p), dev(s), dev(z), 64))
+        check_close(y, int4.forward(synth.bf16_bits_to_f32(xb), p, s, z, 64), f"gemm {name} M=512")
+
+
+def test_gemm_prefill_gate_m4096_sampled_rows():
+    """The metric shape (M=4096, K=2048, N=11008, g=64) in the benchmarked launch configuration;
+    the oracle checks 192 sampled rows covering every 256-row tile (first, last and interior rows)."""
+    p, s, z = _quantized_layer(3, "gate_proj", 64)
+    xb = synth.layer_activations_bf16(3, 4096, 2048)
+    step("aq_w4a16_gemm gate_proj [11008,2048] g=64 M=4096")
+    y = host(B.aq_w4a16_gemm(dev_bf16(xb), dev(p), dev(s), dev(z), 64))
+    rows = np.unique(np.concatenate([np.arange(0, 4096, 256), np.arange(255, 4096, 256),
+                                     np.random.default_rng(0).choice(4096, 160, replace=False)]))
+    ref = int4.forward(synth.bf16_bits_to_f32(xb[rows]), p, s, z, 64)
+    check_close(y[rows], ref, "gemm gate M=4096 (sampled rows)")
+
+
+@pytest.mark.parametrize("m,n,k,g", [(1, 5, 64, 32), (64, 128, 128, 64), (300, 200, 192, 64), (257, 129, 384, 128),
+                                     (2049, 130, 96, 32)])
+def test_gemm_ragged_shapes(m, n, k, g):
+    rng = np.random.default_rng(m * 7 + n)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    p, s, z = int4.quantize_pack(w, g)
+    xb = synth.f32_to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+    step(f"aq_w4a16_gemm ragged M={m} N={n} K={k} g={g}")
+    y = host(B.aq_w4a16_gemm(dev_bf16(xb), dev(p), dev(s), dev(z), g))
+    check_close(y, int4.forward(synth.bf16_bits_to_f32(xb), p, s, z, g), f"gemm ragged {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m,n,k,g", [(64, 128, 256, 64), (300, 130, 128, 32), (2100, 256, 512, 128)])
+def test_gemm_exact_integer_case(m, n, k, g):
+    xb, x, p, s, z = _exact_case(np.random.default_rng(m + n), m, n, k, g)
+    step(f"aq_w4a16_gemm exact-integer M={m} N={n} K={k} g={g}")
+    y = host(B.aq_w4a16_gemm(dev_bf16(xb), dev(p), dev(s), dev(z), g))
+    assert (y.astype(np.float64) == int4.forward(x, p, s, z, g)).all()
+
+
+def test_pack_then_gemv_round_trip():
+    """Device pack followed by the device GEMV equals the oracle's pack + forward (the module-swap path)."""
+    wb = synth.layer_weight_bf16(4, "o_proj")
+    xb = synth.layer_activations_bf16(4, 1, 2048)
+    step("aq_quantize_pack + aq_w4a16_gemv o_proj")
+    p, s, z = B.aq_quantize_pack(dev_bf16(wb), 64)
+    y = host(B.aq_w4a16_gemv(dev_bf16(xb), p, s, z, 64))
+    p0, s0, z0 = int4.quantize_pack(synth.bf16_bits_to_f32(wb), 64)
+    check_close(y, int4.forward(synth.bf16_bits_to_f32(xb), p0, s0, z0, 64), "pack+gemv o_proj")

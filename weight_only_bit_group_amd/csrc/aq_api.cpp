@@ -1,0 +1,270 @@
+// C ABI of libaq: argument validation, status codes, workspace sizing, the
+// host-side candidate scales of the AWQ search, and dispatch to the gfx950
+// kernels.  Every check runs before the first launch, so a call that returns
+// AQ_EINVAL has written nothing.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/aq.h"
+#include "aq_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+aq_status fail(aq_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+aq_status ok() {
+  g_last_error.clear();
+  return AQ_OK;
+}
+
+// AQ_FAULT_INJECT=launch makes every entry point report a runtime failure after
+// validation, without touching the GPU (exercises the AQ_ERUNTIME path).
+bool fault_injected() {
+  const char* v = std::getenv("AQ_FAULT_INJECT");
+  return v && std::strcmp(v, "launch") == 0;
+}
+
+aq_status runtime_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(AQ_ERUNTIME, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+#define AQ_REQUIRE(cond, ...) \
+  do {                        \
+    if (!(cond)) return fail(AQ_EINVAL, __VA_ARGS__); \
+  } while (0)
+
+#define AQ_PTR(p, a, name)                                                          \
+  do {                                                                              \
+    if ((p) == nullptr) return fail(AQ_EINVAL, "%s must not be NULL", name);        \
+    if (!aligned((p), (a))) return fail(AQ_EINVAL, "%s must be %d-byte aligned", name, (int)(a)); \
+  } while (0)
+
+constexpr int64_t kDimLimit = int64_t(1) << 30;
+
+bool valid_group(int32_t g) { return g == 32 || g == 64 || g == 128; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct SearchLayout {
+  size_t sgrid, e, partial, total;
+  int nblocks;
+};
+
+SearchLayout search_layout(int64_t T, int64_t N, int64_t K, int32_t n_grid) {
+  SearchLayout L;
+  L.nblocks = aq::sumsq_gemm_blocks((int)T, (int)N);
+  L.sgrid = 0;
+  L.e = round_up((size_t)n_grid * (size_t)K * sizeof(float), 256);
+  L.partial = L.e + round_up((size_t)N * (size_t)K * 2 * 2, 256);   // E_hi and E_lo planes
+  L.total = L.partial + (size_t)n_grid * (size_t)L.nblocks * sizeof(double);
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* aq_last_error(void) { return g_last_error.c_str(); }
+
+aq_status aq_quantize_pack(const void* W, int32_t w_dtype, int64_t N, int64_t K, int32_t group,
+                           const float* chan_scale, uint8_t* packed, float* scales, uint8_t* zeros,
+                           void* stream) {
+  AQ_REQUIRE(w_dtype == AQ_F32 || w_dtype == AQ_BF16, "w_dtype must be AQ_F32 or AQ_BF16 (got %d)", w_dtype);
+  AQ_REQUIRE(valid_group(group), "group must be 32, 64 or 128 (got %d)", group);
+  AQ_REQUIRE(N >= 0 && N < kDimLimit, "N out of range (%lld)", (long long)N);
+  AQ_REQUIRE(K > 0 && K < kDimLimit, "K out of range (%lld)", (long long)K);
+  AQ_REQUIRE(K % group == 0, "K (%lld) must be a multiple of group (%d)", (long long)K, group);
+  AQ_PTR(W, 16, "W");
+  if (chan_scale) AQ_REQUIRE(aligned(chan_scale, 16), "chan_scale must be 16-byte aligned");
+  AQ_PTR(packed, 16, "packed");
+  AQ_PTR(scales, 4, "scales");
+  AQ_PTR(zeros, 1, "zeros");
+  if (fault_injected()) return fail(AQ_ERUNTIME, "aq_quantize_pack: injected launch failure");
+  if (N == 0) return ok();
+  return runtime_status(aq::launch_quant_pack(W, w_dtype == AQ_BF16, chan_scale, packed, scales, zeros, N, K, group,
+                                              (hipStream_t)stream),
+                        "aq_quantize_pack");
+}
+
+static aq_status check_product(const char* fn, const uint16_t* X, int64_t M, int64_t K, const uint8_t* packed,
+                               const float* scales, const uint8_t* zeros, int64_t N, int32_t group, float* Y) {
+  AQ_REQUIRE(valid_group(group), "%s: group must be 32, 64 or 128 (got %d)", fn, group);
+  AQ_REQUIRE(K > 0 && K < kDimLimit, "%s: K out of range (%lld)", fn, (long long)K);
+  AQ_REQUIRE(K % group == 0, "%s: K (%lld) must be a multiple of group (%d)", fn, (long long)K, group);
+  AQ_REQUIRE(N >= 0 && N < kDimLimit, "%s: N out of range (%lld)", fn, (long long)N);
+  AQ_PTR(X, 16, "X");
+  AQ_PTR(packed, 16, "packed");
+  AQ_PTR(scales, 4, "scales");
+  AQ_PTR(zeros, 1, "zeros");
+  AQ_PTR(Y, 4, "Y");
+  (void)M;
+  return AQ_OK;
+}
+
+aq_status aq_w4a16_gemv(const uint16_t* X, int64_t M, int64_t K, const uint8_t* packed, const float* scales,
+                        const uint8_t* zeros, int64_t N, int32_t group, float* Y, void* stream) {
+  AQ_REQUIRE(M >= 1 && M <= 16, "aq_w4a16_gemv: M must be in 1..16 (got %lld)", (long long)M);
+  aq_status st = check_product("aq_w4a16_gemv", X, M, K, packed, scales, zeros, N, group, Y);
+  if (st != AQ_OK) return st;
+  if (fault_injected()) return fail(AQ_ERUNTIME, "aq_w4a16_gemv: injected launch failure");
+  if (N == 0) return ok();
+  return runtime_status(aq::launch_w4a16_gemv(X, (int)M, (int)K, packed, scales, zeros, (int)N, group, Y,
+                                              (hipStream_t)stream),
+                        "aq_w4a16_gemv");
+}
+
+aq_status aq_w4a16_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_t* packed, const float* scales,
+                        const uint8_t* zeros, int64_t N, int32_t group, float* Y, void* stream) {
+  AQ_REQUIRE(M >= 0 && M < kDimLimit, "aq_w4a16_gemm: M out of range (%lld)", (long long)M);
+  aq_status st = check_product("aq_w4a16_gemm", X, M, K, packed, scales, zeros, N, group, Y);
+  if (st != AQ_OK) return st;
+  if (fault_injected()) return fail(AQ_ERUNTIME, "aq_w4a16_gemm: injected launch failure");
+  if (N == 0 || M == 0) return ok();
+  return runtime_status(aq::launch_w4a16_gemm(X, (int)M, (int)K, packed, scales, zeros, (int)N, group, Y,
+                                              (hipStream_t)stream),
+                        "aq_w4a16_gemm");
+}
+
+size_t aq_act_absmean_workspace(int64_t T, int64_t K) {
+  if (T <= 0 || K <= 0) return 0;
+  return (size_t)aq::absmean_row_slices(T, K) * (size_t)K * sizeof(double);
+}
+
+aq_status aq_act_absmean(const uint16_t* X, int64_t T, int64_t K, double* sum_abs, float* mean_out,
+                         int64_t total_count, void* workspace, size_t workspace_bytes, void* stream) {
+  AQ_REQUIRE(T > 0, "aq_act_absmean: empty calibration data (T = %lld)", (long long)T);
+  AQ_REQUIRE(T < (int64_t(1) << 40), "aq_act_absmean: T out of range");
+  AQ_REQUIRE(K > 0 && K < kDimLimit && K % 8 == 0, "aq_act_absmean: K must be a positive multiple of 8 (got %lld)",
+             (long long)K);
+  AQ_REQUIRE(total_count >= T, "aq_act_absmean: total_count (%lld) must include this chunk's T (%lld)",
+             (long long)total_count, (long long)T);
+  AQ_PTR(X, 16, "X");
+  AQ_PTR(sum_abs, 8, "sum_abs");
+  if (mean_out) AQ_REQUIRE(aligned(mean_out, 4), "mean_out must be 4-byte aligned");
+  AQ_PTR(workspace, 16, "workspace");
+  const size_t need = aq_act_absmean_workspace(T, K);
+  AQ_REQUIRE(workspace_bytes >= need, "aq_act_absmean: workspace too small (%zu < %zu bytes)", workspace_bytes, need);
+  if (fault_injected()) return fail(AQ_ERUNTIME, "aq_act_absmean: injected launch failure");
+  return runtime_status(aq::launch_act_absmean(X, T, K, sum_abs, mean_out, total_count,
+                                               static_cast<double*>(workspace), (hipStream_t)stream),
+                        "aq_act_absmean");
+}
+
+size_t aq_awq_search_workspace(int64_t T, int64_t N, int64_t K, int32_t group, int32_t n_grid) {
+  if (T <= 0 || N <= 0 || K <= 0 || n_grid < 1 || n_grid > 64 || !valid_group(group)) return 0;
+  if (T >= kDimLimit || N >= kDimLimit || K >= kDimLimit) return 0;
+  return search_layout(T, N, K, n_grid).total;
+}
+
+aq_status aq_awq_search(const uint16_t* X_sub, int64_t T, const float* absmean_host, const void* W,
+                        int32_t w_dtype, int64_t N, int64_t K, int32_t group, int32_t n_grid, double* mse,
+                        int32_t* best, float* best_scale, uint8_t* packed, float* scales, uint8_t* zeros,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  AQ_REQUIRE(T > 0, "aq_awq_search: empty calibration data (T = %lld)", (long long)T);
+  AQ_REQUIRE(T < kDimLimit, "aq_awq_search: T out of range");
+  AQ_REQUIRE(w_dtype == AQ_F32 || w_dtype == AQ_BF16, "aq_awq_search: bad w_dtype %d", w_dtype);
+  AQ_REQUIRE(valid_group(group), "aq_awq_search: group must be 32, 64 or 128 (got %d)", group);
+  AQ_REQUIRE(n_grid >= 1 && n_grid <= 64, "aq_awq_search: n_grid must be in 1..64 (got %d)", n_grid);
+  AQ_REQUIRE(N > 0 && N < kDimLimit, "aq_awq_search: N out of range (%lld)", (long long)N);
+  AQ_REQUIRE(K > 0 && K < kDimLimit && K % group == 0, "aq_awq_search: K (%lld) must be a multiple of group (%d)",
+             (long long)K, group);
+  AQ_PTR(X_sub, 16, "X_sub");
+  AQ_REQUIRE(absmean_host != nullptr, "absmean_host must not be NULL");
+  AQ_PTR(W, 16, "W");
+  AQ_PTR(mse, 8, "mse");
+  AQ_PTR(best, 4, "best");
+  AQ_PTR(best_scale, 16, "best_scale");
+  AQ_PTR(packed, 16, "packed");
+  AQ_PTR(scales, 4, "scales");
+  AQ_PTR(zeros, 1, "zeros");
+  AQ_PTR(workspace, 256, "workspace");
+  const SearchLayout L = search_layout(T, N, K, n_grid);
+  AQ_REQUIRE(workspace_bytes >= L.total, "aq_awq_search: workspace too small (%zu < %zu bytes)", workspace_bytes,
+             L.total);
+  for (int64_t k = 0; k < K; ++k)
+    AQ_REQUIRE(std::isfinite(absmean_host[k]) && absmean_host[k] >= 0.0f,
+               "aq_awq_search: absmean_host[%lld] must be finite and >= 0", (long long)k);
+  if (fault_injected()) return fail(AQ_ERUNTIME, "aq_awq_search: injected launch failure");
+
+  // Candidate scales, fp64 libm on the host: t = max(m, 1e-8)^alpha,
+  // s = fl32(t / sqrt(max t * min t)).
+  std::vector<float> sgrid((size_t)n_grid * (size_t)K);
+  std::vector<double> t((size_t)K);
+  for (int32_t i = 0; i < n_grid; ++i) {
+    const double alpha = (double)i / (double)n_grid;
+    double tmax = -INFINITY, tmin = INFINITY;
+    for (int64_t k = 0; k < K; ++k) {
+      double m = (double)absmean_host[k];
+      if (m < 1e-8) m = 1e-8;
+      t[k] = std::pow(m, alpha);
+      tmax = std::max(tmax, t[k]);
+      tmin = std::min(tmin, t[k]);
+    }
+    const double den = std::sqrt(tmax * tmin);
+    for (int64_t k = 0; k < K; ++k) sgrid[(size_t)i * K + k] = (float)(t[k] / den);
+  }
+  char* ws = static_cast<char*>(workspace);
+  float* d_sgrid = reinterpret_cast<float*>(ws + L.sgrid);
+  uint16_t* d_e = reinterpret_cast<uint16_t*>(ws + L.e);
+  double* d_partial = reinterpret_cast<double*>(ws + L.partial);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(d_sgrid, sgrid.data(), sgrid.size() * sizeof(float), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return runtime_status(e, "aq_awq_search: candidate-scale upload");
+  const bool bf16 = w_dtype == AQ_BF16;
+  for (int32_t i = 0; i < n_grid; ++i) {
+    e = aq::launch_quant_error(W, bf16, d_sgrid + (size_t)i * K, d_e, N, K, group, s);
+    if (e != hipSuccess) return runtime_status(e, "aq_awq_search: error-matrix kernel");
+    e = aq::launch_sumsq_gemm(X_sub, (int)T, (int)K, d_e, (int)N, d_partial + (size_t)i * L.nblocks, s);
+    if (e != hipSuccess) return runtime_status(e, "aq_awq_search: error GEMM");
+  }
+  e = aq::launch_search_select(d_partial, L.nblocks, n_grid, (double)T * (double)N, d_sgrid, (int)K, mse, best,
+                               best_scale, s);
+  if (e != hipSuccess) return runtime_status(e, "aq_awq_search: select kernel");
+  return runtime_status(aq::launch_quant_pack(W, bf16, best_scale, packed, scales, zeros, N, K, group, s),
+                        "aq_awq_search: final pack");
+}
+
+aq_status aq_fp4_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes, const uint8_t* block_scales,
+                      float tensor_scale, int64_t N, float* Y, void* stream) {
+  AQ_REQUIRE(M >= 0 && M < kDimLimit, "aq_fp4_gemm: M out of range (%lld)", (long long)M);
+  AQ_REQUIRE(K > 0 && K < kDimLimit && K % 32 == 0, "aq_fp4_gemm: K must be a positive multiple of 32 (got %lld)",
+             (long long)K);
+  AQ_REQUIRE(N >= 0 && N < kDimLimit, "aq_fp4_gemm: N out of range (%lld)", (long long)N);
+  AQ_REQUIRE(std::isfinite(tensor_scale), "aq_fp4_gemm: tensor_scale must be finite");
+  AQ_PTR(X, 16, "X");
+  AQ_PTR(codes, 16, "codes");
+  AQ_PTR(block_scales, 2, "block_scales");
+  AQ_PTR(Y, 4, "Y");
+  if (fault_injected()) return fail(AQ_ERUNTIME, "aq_fp4_gemm: injected launch failure");
+  if (N == 0 || M == 0) return ok();
+  hipError_t e;
+  if (M <= 16)
+    e = aq::launch_fp4_gemv(X, (int)M, (int)K, codes, block_scales, tensor_scale, (int)N, Y, (hipStream_t)stream);
+  else
+    e = aq::launch_fp4_gemm(X, (int)M, (int)K, codes, block_scales, tensor_scale, (int)N, Y, (hipStream_t)stream);
+  return runtime_status(e, "aq_fp4_gemm");
+}
+
+}  // extern "C"

@@ -1,0 +1,32 @@
+// Internal launch functions of libaq (host side).  Each enqueues its kernels on
+// `stream` and returns the launch status; arguments are validated by the C ABI
+// layer before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace aq {
+
+hipError_t launch_quant_pack(const void* W, bool w_bf16, const float* chan_scale, uint8_t* packed, float* scales,
+                             uint8_t* zeros, int64_t N, int64_t K, int group, hipStream_t stream);
+hipError_t launch_quant_error(const void* W, bool w_bf16, const float* chan_scale, uint16_t* E, int64_t N, int64_t K,
+                              int group, hipStream_t stream);
+hipError_t launch_w4a16_gemv(const uint16_t* X, int M, int K, const uint8_t* P, const float* S, const uint8_t* Z,
+                             int N, int group, float* Y, hipStream_t stream);
+hipError_t launch_w4a16_gemm(const uint16_t* X, int M, int K, const uint8_t* P, const float* S, const uint8_t* Z,
+                             int N, int group, float* Y, hipStream_t stream);
+hipError_t launch_fp4_gemv(const uint16_t* X, int M, int K, const uint8_t* codes, const uint8_t* bscale, float ts,
+                           int N, float* Y, hipStream_t stream);
+hipError_t launch_fp4_gemm(const uint16_t* X, int M, int K, const uint8_t* codes, const uint8_t* bscale, float ts,
+                           int N, float* Y, hipStream_t stream);
+int sumsq_gemm_blocks(int M, int N);
+hipError_t launch_sumsq_gemm(const uint16_t* X, int M, int K, const uint16_t* E, int N, double* partial,
+                             hipStream_t stream);
+int absmean_row_slices(int64_t T, int64_t K);
+hipError_t launch_act_absmean(const uint16_t* X, int64_t T, int64_t K, double* sum_abs, float* mean, int64_t count,
+                              double* work, hipStream_t stream);
+hipError_t launch_search_select(const double* partial, int nblocks, int n_grid, double count, const float* sgrid,
+                                int K, double* mse, int32_t* best, float* best_scale, hipStream_t stream);
+
+}  // namespace aq

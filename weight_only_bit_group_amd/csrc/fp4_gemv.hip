@@ -1,0 +1,121 @@
+// FP4 decode GEMV (M = 1..16), gfx950, VALU only.
+//
+// What it computes: Y[m, n] = ts * sum_k X[m, k] * e2m1(c[n, k]) * e4m3(b[n, k / 16])
+// for E2M1 codes with one E4M3 scale per 16-element block and an fp32 tensor
+// scale ("Lance-Quant", zingnex.cn, grid-search / grouped packing section: E2M1
+// codes plus an FP8 E4M3 scale for every 16-element block; "Quantization：模型量化",
+// xingyuwang.me, section 12: E4M3 = 1 + 4 + 3 bits).
+//
+// Design: as the INT4 GEMV -- one wave per R output rows, lane l reading the
+// 16-byte code chunks c = l, l + 64, ... (32 codes = two scale blocks).  gfx950's
+// v_cvt_scalef32_pk_bf16_fp4 (unit scale) turns one code byte into the exact bf16
+// pair (k, k + 1), which lines up with the activation pairs as loaded, so
+// v_dot2_f32_bf16 accumulates each 16-block and the fp32 block scale multiplies
+// the block sum once.
+#include "aq_device.h"
+#include "aq_kernels.h"
+
+namespace aq {
+
+__device__ __forceinline__ uint32_t fp4_pair(uint32_t src, int sel) {
+  switch (sel) {
+    case 0: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, 1.0f, 0));
+    case 1: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, 1.0f, 1));
+    case 2: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, 1.0f, 2));
+    default: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, 1.0f, 3));
+  }
+}
+
+template <int M, int R>
+__global__ __launch_bounds__(256) void fp4_gemv_kernel(const uint16_t* __restrict__ X,
+                                                        const uint8_t* __restrict__ C,
+                                                        const uint8_t* __restrict__ B,
+                                                        float ts, float* __restrict__ Y, int N, int K) {
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int n0 = wave * R;
+  if (n0 >= N) return;
+  const int kbytes = K >> 1;
+  const int nblk = K >> 4;
+  const int nchunk = K >> 5;
+
+  float acc[M][R];
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[m][r] = 0.0f;
+
+  for (int c = lane; c < nchunk; c += 64) {
+    u32x4 code[R];
+    float bs[R][2];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int row = min(n0 + r, N - 1);
+      code[r] = *reinterpret_cast<const u32x4*>(C + (int64_t)row * kbytes + (c << 4));
+      const uint32_t two = *reinterpret_cast<const uint16_t*>(B + (int64_t)row * nblk + (c << 1));
+      bs[r][0] = __builtin_amdgcn_cvt_f32_fp8((int)two, 0);
+      bs[r][1] = __builtin_amdgcn_cvt_f32_fp8((int)two, 1);
+    }
+    uint32_t deq[R][16];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) deq[r][4 * i + s] = fp4_pair(code[r][i], s);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const u32x4* xp4 = reinterpret_cast<const u32x4*>(X + (int64_t)m * K + (c << 5));
+      uint32_t xw[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32x4 t = xp4[i];
+        xw[4 * i] = t[0]; xw[4 * i + 1] = t[1]; xw[4 * i + 2] = t[2]; xw[4 * i + 3] = t[3];
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) d0 = dot2_bf16(deq[r][j], xw[j], d0);
+#pragma unroll
+        for (int j = 8; j < 16; ++j) d1 = dot2_bf16(deq[r][j], xw[j], d1);
+        acc[m][r] = __builtin_fmaf(bs[r][1], d1, __builtin_fmaf(bs[r][0], d0, acc[m][r]));
+      }
+    }
+  }
+
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float v = wave_sum(acc[m][r]);
+      if (lane == 0 && n0 + r < N) Y[(int64_t)m * N + n0 + r] = v * ts;
+    }
+}
+
+template <int M>
+static hipError_t launch_m(const uint16_t* X, const uint8_t* C, const uint8_t* B, float ts, float* Y, int N,
+                           int K, hipStream_t stream) {
+  int R = 1;
+  if (N >= 8192) R = 4;
+  else if (N >= 4096) R = 2;
+  const int waves = (N + R - 1) / R;
+  const dim3 grid((waves + 3) / 4), block(256);
+  if (R == 4) hipLaunchKernelGGL((fp4_gemv_kernel<M, 4>), grid, block, 0, stream, X, C, B, ts, Y, N, K);
+  else if (R == 2) hipLaunchKernelGGL((fp4_gemv_kernel<M, 2>), grid, block, 0, stream, X, C, B, ts, Y, N, K);
+  else hipLaunchKernelGGL((fp4_gemv_kernel<M, 1>), grid, block, 0, stream, X, C, B, ts, Y, N, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp4_gemv(const uint16_t* X, int M, int K, const uint8_t* codes, const uint8_t* bscale,
+                           float ts, int N, float* Y, hipStream_t stream) {
+  switch (M) {
+#define AQ_CASE(mm) case mm: return launch_m<mm>(X, codes, bscale, ts, Y, N, K, stream);
+    AQ_CASE(1) AQ_CASE(2) AQ_CASE(3) AQ_CASE(4) AQ_CASE(5) AQ_CASE(6) AQ_CASE(7) AQ_CASE(8)
+    AQ_CASE(9) AQ_CASE(10) AQ_CASE(11) AQ_CASE(12) AQ_CASE(13) AQ_CASE(14) AQ_CASE(15) AQ_CASE(16)
+#undef AQ_CASE
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace aq
