@@ -8,38 +8,127 @@
 // the compressed weights, dequantize inside the kernel, then contract; decode is
 // memory-bound, so fewer weight bytes read means a faster step).
 //
-// Design (HBM-bound at M = 1): one wavefront owns R output rows.  A row of
-// packed codes is K/2 bytes; lane l reads the 16-byte chunks c = l, l + 64, ...
-// (32 codes each, always inside one group since g >= 32), so every load
-// instruction of the wave covers 1 KiB of one row with 128-bit accesses.  The
-// R rows' chunks, their S and z are issued before any arithmetic.
-//
-// Exact integer dequantization: for a code dword d (8 nibbles),
-//   ((d >> 4s) & 0x000F000F) | 0x43004300
-// is a pair of bf16 values (128 + q_{s}, 128 + q_{s+4}) -- exact, one op per two
-// weights -- and v_dot2_f32_bf16 accumulates x * (128 + q) in fp32.  The chunk
-// sum is corrected by -(128 + z) * sum(x) before the fp32 group scale is applied,
-// so Y never goes through a rounded bf16 weight.  The activations are permuted
-// once per chunk into the matching (k, k + 4) pairs and reused for all R rows.
+// Design (HBM-bound at M = 1):
+//  * One wavefront owns R output rows.  A row of packed codes is K/2 bytes; lane l
+//    reads the 16-byte chunks c = l, l + 64, ... (32 codes each, always inside one
+//    group since g >= 32), so each load instruction of the wave covers 1 KiB of one
+//    row with 128-bit accesses.  All code / S / z loads of a batch of chunks are
+//    issued before anything waits on them (and are pinned there: the compiler may
+//    otherwise sink them below the block barrier, which serialises the X staging
+//    latency with the weight stream).
+//  * X is staged once per block in LDS, already permuted into the (k, k + 4)
+//    bf16 pairs the dequantized codes come out in, plus the sum of every 8
+//    activations; a raw s_barrier waits only for LDS.  When M * K is too large for
+//    LDS, each lane reads its activation chunk straight from global memory.
+//  * Exact integer dequantization: for a code dword d (8 nibbles)
+//      v_and_or_b32(d >> 4s, 0x000F000F, 0x43004300)
+//    is the bf16 pair (128 + q_s, 128 + q_{s+4}); v_dot2_f32_bf16 accumulates
+//    x * (128 + q) in fp32 and the chunk sum is corrected by -(128 + z) * sum(x)
+//    before the fp32 group step S is applied -- no rounded bf16 weight is formed.
+//  * Each row's 64 lane partials are reduced with DPP (quad perms, row mirrors,
+//    row_bcast:15 / row_bcast:31); lane 63 writes the result.
 #include "aq_device.h"
 #include "aq_kernels.h"
 
 namespace aq {
 
-template <int M, int R>
-__global__ __launch_bounds__(256) void w4a16_gemv_kernel(const uint16_t* __restrict__ X,
-                                                          const uint8_t* __restrict__ P,
-                                                          const float* __restrict__ S,
-                                                          const uint8_t* __restrict__ Z,
-                                                          float* __restrict__ Y,
-                                                          int N, int K, int gshift) {
+namespace {
+
+constexpr int kLdsBytes = 48 * 1024;
+
+__device__ __forceinline__ float dpp_sum_to_lane63(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xC, 0xF, false));
+  return v;  // lane 63 holds the wave total
+}
+
+// (k, k+4) pairing of one 8-activation dword quad: xw = 4 dwords of natural bf16 pairs.
+__device__ __forceinline__ u32x4 permute_pairs(const u32x4 t) {
+  u32x4 p;
+  p[0] = __builtin_amdgcn_perm(t[2], t[0], 0x05040100u);
+  p[1] = __builtin_amdgcn_perm(t[2], t[0], 0x07060302u);
+  p[2] = __builtin_amdgcn_perm(t[3], t[1], 0x05040100u);
+  p[3] = __builtin_amdgcn_perm(t[3], t[1], 0x07060302u);
+  return p;
+}
+
+__device__ __forceinline__ float sum8(const u32x4 t) {
+  float s = dot2_bf16(t[0], 0x3F803F80u, 0.0f);
+  s = dot2_bf16(t[1], 0x3F803F80u, s);
+  s = dot2_bf16(t[2], 0x3F803F80u, s);
+  return dot2_bf16(t[3], 0x3F803F80u, s);
+}
+
+// sum_k x_k * (128 + q_k) over one 32-code chunk; xp = the chunk's 16 permuted pairs.
+__device__ __forceinline__ float chunk_dot(const u32x4 code, const uint32_t* xp, uint32_t mask, uint32_t magic) {
+  float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t w = ((code[i] >> (4 * s)) & mask) | magic;
+      if (s & 1) d1 = dot2_bf16(w, xp[4 * i + s], d1);
+      else d0 = dot2_bf16(w, xp[4 * i + s], d0);
+    }
+  return d0 + d1;
+}
+
+// LDS_X: X [M, K] staged in LDS as permuted pairs (M * K / 2 dwords) + 8-sums (M * K / 8 floats).
+// CPL: 16-byte code chunks per lane loaded per batch (all issued before use).
+template <int M, int R, int CPL, bool LDS_X>
+__global__ __launch_bounds__(256) void w4a16_gemv_kernel(const uint16_t* X, const uint8_t* P, const float* S,
+                                                          const uint8_t* Z, float* __restrict__ Y, int N, int K,
+                                                          int gshift) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int n0 = wave * R;
-  if (n0 >= N) return;  // uniform per wave
   const int kbytes = K >> 1;
   const int nchunk = K >> 5;
   const int ngroups = K >> gshift;
+  const int nbatch = (nchunk + 64 * CPL - 1) / (64 * CPL);
+  uint32_t* xpl = lds;                                    // [M][K/2] permuted pairs
+  float* xsl = reinterpret_cast<float*>(lds + M * (K >> 1));  // [M][K/8] 8-sums
+
+  u32x4 code[R][CPL];
+  float sc[R][CPL];
+  uint32_t zb[R][CPL];
+  auto issue = [&](int b) {
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = min(lane + 64 * (b * CPL + j), nchunk - 1);
+      const int grp = (c << 5) >> gshift;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int row = min(n0 + r, N - 1);
+        code[r][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(P + (int64_t)row * kbytes + (c << 4)));
+        sc[r][j] = S[(int64_t)row * ngroups + grp];
+        zb[r][j] = Z[(int64_t)row * ngroups + grp];
+      }
+    }
+  };
+
+  issue(0);
+  asm volatile("" ::: "memory");  // keep the first weight batch ahead of the X staging
+  if constexpr (LDS_X) {
+    const int n8 = M * (K >> 3);
+    for (int i = threadIdx.x; i < n8; i += 256) {
+      const u32x4 t = reinterpret_cast<const u32x4*>(X)[i];
+      reinterpret_cast<u32x4*>(xpl)[i] = permute_pairs(t);
+      xsl[i] = sum8(t);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are complete
+    __builtin_amdgcn_s_barrier();
+  }
+  if (n0 >= N) return;  // uniform per wave, after the block barrier
+
+  uint32_t mask, magic;
+  asm volatile("s_mov_b32 %0, 0x000f000f" : "=s"(mask));
+  asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(magic));
 
   float acc[M][R];
 #pragma unroll
@@ -47,52 +136,43 @@ __global__ __launch_bounds__(256) void w4a16_gemv_kernel(const uint16_t* __restr
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[m][r] = 0.0f;
 
-  for (int c = lane; c < nchunk; c += 64) {
-    u32x4 code[R];
-    float sc[R], zc[R];
-    const int grp = (c << 5) >> gshift;
+  for (int b = 0; b < nbatch; ++b) {
+    if (b > 0) issue(b);
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int row = min(n0 + r, N - 1);
-      code[r] = *reinterpret_cast<const u32x4*>(P + (int64_t)row * kbytes + (c << 4));
-      sc[r] = S[(int64_t)row * ngroups + grp];
-      zc[r] = 128.0f + (float)Z[(int64_t)row * ngroups + grp];
-    }
-    uint32_t deq[R][16];
+    for (int j = 0; j < CPL; ++j) {
+      const int c = lane + 64 * (b * CPL + j);
+      if (c >= nchunk) break;
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+      for (int m = 0; m < M; ++m) {
+        uint32_t xp[16];
+        float xs;
+        if constexpr (LDS_X) {
+          const u32x4* src = reinterpret_cast<const u32x4*>(xpl + m * (K >> 1)) + 4 * c;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < 4; ++i) {
+            const u32x4 t = src[i];
+            xp[4 * i] = t[0]; xp[4 * i + 1] = t[1]; xp[4 * i + 2] = t[2]; xp[4 * i + 3] = t[3];
+          }
+          const float4 p = reinterpret_cast<const float4*>(xsl + m * (K >> 3))[c];
+          xs = (p.x + p.y) + (p.z + p.w);
+        } else {
+          const u32x4* src = reinterpret_cast<const u32x4*>(X + (int64_t)m * K + (c << 5));
+          float p[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          deq[r][4 * i + s] = ((code[r][i] >> (4 * s)) & 0x000F000Fu) | 0x43004300u;
-
+          for (int i = 0; i < 4; ++i) {
+            const u32x4 t = src[i];
+            const u32x4 q = permute_pairs(t);
+            xp[4 * i] = q[0]; xp[4 * i + 1] = q[1]; xp[4 * i + 2] = q[2]; xp[4 * i + 3] = q[3];
+            p[i] = sum8(t);
+          }
+          xs = (p[0] + p[1]) + (p[2] + p[3]);
+        }
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const u32x4* xp4 = reinterpret_cast<const u32x4*>(X + (int64_t)m * K + (c << 5));
-      uint32_t xw[16];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const u32x4 t = xp4[i];
-        xw[4 * i] = t[0]; xw[4 * i + 1] = t[1]; xw[4 * i + 2] = t[2]; xw[4 * i + 3] = t[3];
-      }
-      uint32_t xp[16];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        xp[4 * i + 0] = __builtin_amdgcn_perm(xw[4 * i + 2], xw[4 * i + 0], 0x05040100u);
-        xp[4 * i + 1] = __builtin_amdgcn_perm(xw[4 * i + 2], xw[4 * i + 0], 0x07060302u);
-        xp[4 * i + 2] = __builtin_amdgcn_perm(xw[4 * i + 3], xw[4 * i + 1], 0x05040100u);
-        xp[4 * i + 3] = __builtin_amdgcn_perm(xw[4 * i + 3], xw[4 * i + 1], 0x07060302u);
-      }
-      float xs = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) xs = dot2_bf16(xw[j], 0x3F803F80u, xs);
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        float d = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) d = dot2_bf16(deq[r][j], xp[j], d);
-        acc[m][r] = __builtin_fmaf(sc[r], __builtin_fmaf(-zc[r], xs, d), acc[m][r]);
+        for (int r = 0; r < R; ++r) {
+          const float d = chunk_dot(code[r][j], xp, mask, magic);
+          const float zc = 128.0f + (float)zb[r][j];
+          acc[m][r] = __builtin_fmaf(sc[r][j], __builtin_fmaf(-zc, xs, d), acc[m][r]);
+        }
       }
     }
   }
@@ -101,25 +181,37 @@ __global__ __launch_bounds__(256) void w4a16_gemv_kernel(const uint16_t* __restr
   for (int m = 0; m < M; ++m)
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const float v = wave_sum(acc[m][r]);
-      if (lane == 0 && n0 + r < N) Y[(int64_t)m * N + n0 + r] = v;
+      const float v = dpp_sum_to_lane63(acc[m][r]);
+      if (lane == 63 && n0 + r < N) Y[(int64_t)m * N + n0 + r] = v;
     }
 }
 
-template <int M>
-static hipError_t launch_m(const uint16_t* X, const uint8_t* P, const float* S, const uint8_t* Z, float* Y,
-                           int N, int K, int gshift, hipStream_t stream) {
-  // Rows per wave: enough waves to keep every CU's memory pipeline full.
-  int R = 1;
-  if (N >= 8192) R = 4;
-  else if (N >= 4096) R = 2;
+template <int M, int R, int CPL, bool LDS_X>
+hipError_t launch_cfg(const uint16_t* X, const uint8_t* P, const float* S, const uint8_t* Z, float* Y, int N, int K,
+                      int gshift, hipStream_t stream) {
   const int waves = (N + R - 1) / R;
-  const dim3 grid((waves + 3) / 4), block(256);
-  if (R == 4) hipLaunchKernelGGL((w4a16_gemv_kernel<M, 4>), grid, block, 0, stream, X, P, S, Z, Y, N, K, gshift);
-  else if (R == 2) hipLaunchKernelGGL((w4a16_gemv_kernel<M, 2>), grid, block, 0, stream, X, P, S, Z, Y, N, K, gshift);
-  else hipLaunchKernelGGL((w4a16_gemv_kernel<M, 1>), grid, block, 0, stream, X, P, S, Z, Y, N, K, gshift);
+  const size_t lds = LDS_X ? (size_t)M * (K >> 1) * 4 + (size_t)M * (K >> 3) * 4 : 0;
+  hipLaunchKernelGGL((w4a16_gemv_kernel<M, R, CPL, LDS_X>), dim3((waves + 3) / 4), dim3(256), lds, stream, X, P, S,
+                     Z, Y, N, K, gshift);
   return hipGetLastError();
 }
+
+template <int M>
+hipError_t launch_m(const uint16_t* X, const uint8_t* P, const float* S, const uint8_t* Z, float* Y, int N, int K,
+                    int gshift, hipStream_t stream) {
+  const size_t lds = (size_t)M * (K >> 1) * 4 + (size_t)M * (K >> 3) * 4;
+  const bool lds_x = lds <= (size_t)kLdsBytes;
+  constexpr int R = M <= 4 ? 2 : 1;
+  const int nchunk = K >> 5;
+  if (lds_x) {
+    if (nchunk <= 64) return launch_cfg<M, R, 1, true>(X, P, S, Z, Y, N, K, gshift, stream);
+    return launch_cfg<M, R, 2, true>(X, P, S, Z, Y, N, K, gshift, stream);
+  }
+  if (nchunk <= 64) return launch_cfg<M, R, 1, false>(X, P, S, Z, Y, N, K, gshift, stream);
+  return launch_cfg<M, R, 2, false>(X, P, S, Z, Y, N, K, gshift, stream);
+}
+
+}  // namespace
 
 hipError_t launch_w4a16_gemv(const uint16_t* X, int M, int K, const uint8_t* P, const float* S,
                              const uint8_t* Z, int N, int group, float* Y, hipStream_t stream) {
