@@ -42,9 +42,14 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libaq)")
 
 
+# Per-file extra flags: the GEMMs keep MFMA accumulators in VGPRs (the fp32
+# group rescale operates on them with plain VALU FMAs).
+FILE_FLAGS = {"mfma_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *COMMON_FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     proc = subprocess.run(cmd, capture_output=True, text=True)
     if proc.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{proc.stdout}\n{proc.stderr}")

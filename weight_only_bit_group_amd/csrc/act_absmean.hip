@@ -73,16 +73,25 @@ __global__ __launch_bounds__(256) void absmean_partial_kernel(const uint16_t* __
   }
 }
 
+// Finish: 32 channels per block, 8 threads per channel each adding every 8th row
+// slice; the 8 partial sums are then combined in a fixed order (deterministic).
 __global__ __launch_bounds__(256) void absmean_finish_kernel(const double* __restrict__ part, int slices, int K,
                                                              double* __restrict__ sum_abs, float* __restrict__ mean,
                                                              double count) {
-  const int k = blockIdx.x * blockDim.x + threadIdx.x;
-  if (k >= K) return;
+  __shared__ double sm[8][32];
+  const int c = threadIdx.x & 31, r = threadIdx.x >> 5;
+  const int k = blockIdx.x * 32 + c;
   double s = 0.0;
-  for (int i = 0; i < slices; ++i) s += part[(int64_t)i * K + k];
-  const double tot = sum_abs[k] + s;
-  sum_abs[k] = tot;
-  if (mean) mean[k] = (float)(tot / count);
+  if (k < K)
+    for (int i = r; i < slices; i += 8) s += part[(int64_t)i * K + k];
+  sm[r][c] = s;
+  __syncthreads();
+  if (r == 0 && k < K) {
+    const double tot_chunk = ((sm[0][c] + sm[1][c]) + (sm[2][c] + sm[3][c])) + ((sm[4][c] + sm[5][c]) + (sm[6][c] + sm[7][c]));
+    const double tot = sum_abs[k] + tot_chunk;
+    sum_abs[k] = tot;
+    if (mean) mean[k] = (float)(tot / count);
+  }
 }
 
 hipError_t launch_act_absmean(const uint16_t* X, int64_t T, int64_t K, double* sum_abs, float* mean,
@@ -93,7 +102,7 @@ hipError_t launch_act_absmean(const uint16_t* X, int64_t T, int64_t K, double* s
   hipLaunchKernelGGL(absmean_partial_kernel, grid, dim3(256), 0, stream, X, T, (int)K, rows, work);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(absmean_finish_kernel, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, stream, work, slices,
+  hipLaunchKernelGGL(absmean_finish_kernel, dim3((unsigned)((K + 31) / 32)), dim3(256), 0, stream, work, slices,
                      (int)K, sum_abs, mean, (double)count);
   return hipGetLastError();
 }

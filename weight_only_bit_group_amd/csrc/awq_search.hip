@@ -13,38 +13,48 @@
 
 namespace aq {
 
-__global__ __launch_bounds__(64) void search_select_kernel(const double* __restrict__ partial, int nblocks, int n_grid,
-                                                           double count, const float* __restrict__ sgrid, int K,
-                                                           double* __restrict__ mse, int32_t* __restrict__ best,
-                                                           float* __restrict__ best_scale) {
-  __shared__ double sm[64];
-  __shared__ int sbest;
+// One block per candidate: the per-tile sums of squares are added by 256 threads
+// (each a fixed stride of tiles) and combined by a fixed-order tree, then divided by
+// the number of outputs.
+__global__ __launch_bounds__(256) void search_mse_kernel(const double* __restrict__ partial, int nblocks,
+                                                         double count, double* __restrict__ mse) {
+  __shared__ double sm[256];
   const int t = threadIdx.x;
-  if (t < n_grid) {
-    double s = 0.0;
-    const double* p = partial + (int64_t)t * nblocks;
-    for (int b = 0; b < nblocks; ++b) s += p[b];
-    s = s / count;
-    sm[t] = s;
-    mse[t] = s;
-  }
+  const double* p = partial + (int64_t)blockIdx.x * nblocks;
+  double s = 0.0;
+  for (int b = t; b < nblocks; b += 256) s += p[b];
+  sm[t] = s;
   __syncthreads();
-  if (t == 0) {
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (t < w) sm[t] = sm[t] + sm[t + w];
+    __syncthreads();
+  }
+  if (t == 0) mse[blockIdx.x] = sm[0] / count;
+}
+
+// Argmin (first minimum wins) and the winning scale vector.
+__global__ __launch_bounds__(256) void search_pick_kernel(const double* __restrict__ mse, int n_grid,
+                                                          const float* __restrict__ sgrid, int K,
+                                                          int32_t* __restrict__ best, float* __restrict__ best_scale) {
+  __shared__ int sbest;
+  if (threadIdx.x == 0) {
     int bi = 0;
     for (int i = 1; i < n_grid; ++i)
-      if (sm[i] < sm[bi]) bi = i;  // strict: the first minimum wins
+      if (mse[i] < mse[bi]) bi = i;
     sbest = bi;
     best[0] = bi;
   }
   __syncthreads();
   const float* src = sgrid + (int64_t)sbest * K;
-  for (int k = t; k < K; k += 64) best_scale[k] = src[k];
+  for (int k = threadIdx.x; k < K; k += 256) best_scale[k] = src[k];
 }
 
 hipError_t launch_search_select(const double* partial, int nblocks, int n_grid, double count, const float* sgrid,
                                 int K, double* mse, int32_t* best, float* best_scale, hipStream_t stream) {
-  hipLaunchKernelGGL(search_select_kernel, dim3(1), dim3(64), 0, stream, partial, nblocks, n_grid, count, sgrid, K,
-                     mse, best, best_scale);
+  hipLaunchKernelGGL(search_mse_kernel, dim3(n_grid), dim3(256), 0, stream, partial, nblocks, count, mse);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(search_pick_kernel, dim3(1), dim3(256), 0, stream, mse, n_grid, sgrid, K, best, best_scale);
   return hipGetLastError();
 }
 
