@@ -12,10 +12,12 @@ group 64):
   search   aq_awq_search, 4096 tokens, 20 alphas, final pack     (AWQ search)
   fp4      aq_fp4_gemm at M = 1 and M = 2048 on W[14336, 4096]   (FP4 decode)
 
-Every launch is bracketed by HIP events on the stream it runs on (torch's
-current stream, which the binding passes to the library).  The headline value
-is the decode GEMV's HBM throughput (algorithmic bytes / average launch
-duration); the GEMM's TFLOP/s and the other stages are reported beside it.
+Launches are bracketed by HIP events on the stream they run on (torch's current
+stream, which the binding passes to the library): one event pair per launch,
+except the 40 decode GEMVs of a step, which run back to back between one pair
+(as a decode stream does) and are averaged per launch.  The headline value is
+the decode GEMV's HBM throughput (algorithmic bytes / average launch duration);
+the GEMM's TFLOP/s and the other stages are reported beside it.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """

@@ -16,7 +16,8 @@ from ._lib import AQ_BF16, AQ_F32, check
 
 
 def _stream(t: torch.Tensor) -> int:
-    return torch.cuda.current_stream(t.device).cuda_stream
+    # raw handle of torch's current stream on the tensor's device (cheap accessor)
+    return torch._C._cuda_getCurrentRawStream(t.device.index)
 
 
 def _ptr(t):

@@ -33,9 +33,10 @@
 //   * LDS rows are 128 bytes (64 bf16, 8 units of 16 bytes) with unit u of row r
 //     stored at u ^ (r & 7): the 8 rows read by each 8-lane phase of a
 //     ds_read_b128 hit 8 different bank groups.
-//   * Block order is XCD-aware: block b runs on XCD b % 8, so consecutive tiles
-//     of the M-major tile order are handed to the same XCD and share its L2 copy
-//     of the activation tile.
+//   * Block order is XCD-aware: block b runs on XCD b % 8; each XCD gets a
+//     contiguous range of a grouped tile order (a few row tiles, all column
+//     tiles), so the blocks it runs together share their activation and weight
+//     tiles in its L2.
 //   * INT4: the MFMAs of one group run block by block into a 4-register
 //     temporary that is rescaled by S[n, g] straight into the VGPR-resident
 //     output (one v_fmac per output element per group); a group wider than a
@@ -118,9 +119,17 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
   const int M = a.M, N = a.N, K = a.K;
   const int tiles_n = (N + BN - 1) / BN;
   const int tiles_m = (M + BM - 1) / BM;
+  // XCD-contiguous linear index, then groups of GM row tiles walked column by column:
+  // the blocks an XCD runs at once cover GM row tiles x (blocks / GM) column tiles,
+  // so their activation and weight tiles stay in that XCD's L2.
   const int t = tile_of_block(blockIdx.x, tiles_m * tiles_n);
-  const int m0 = (t / tiles_n) * BM;
-  const int n0 = (t % tiles_n) * BN;
+  const int GM = max(1, (tiles_m + 7) / 8);
+  const int group = t / (GM * tiles_n);
+  const int first_m = group * GM;
+  const int gm = min(tiles_m - first_m, GM);
+  const int within = t - group * GM * tiles_n;
+  const int m0 = (first_m + within % gm) * BM;
+  const int n0 = (within / gm) * BN;
   const int nfull = K / KS;                    // full 64-wide stages; TAIL adds one 32-wide stage
   const int nstage = nfull + (TAIL ? 1 : 0);
 
