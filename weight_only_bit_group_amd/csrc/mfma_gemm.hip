@@ -21,15 +21,28 @@
 //         the epilogue returns, per block, the fp64 sum of squares of its outputs
 //         (the MSE numerator).
 //
-// Pipeline (per 256-thread block, 4 waves in a 2 x 2 grid, wave tile WM x 64 of
-// 16x16 v_mfma_f32_16x16x32_bf16 blocks):
-//   * K advances in stages of 64 (one INT4 group at g = 64) through two LDS
-//     buffers; one barrier per stage.
-//   * Activation rows (and the SPLIT planes) go global -> LDS directly with
-//     global_load_lds_dwordx4, issued one stage ahead; no registers, no VALU.
-//   * INT4 / FP4 weight codes are loaded one stage ahead into registers and
-//     dequantized exactly once per block into LDS, shared by both waves of a
-//     column.
+// Block: 2 * WGM waves (WGM = 4 for large M: 512 threads, a 256 x 128 tile), the
+// waves in a WGM x 2 grid of 64 x 64 wave tiles, each four 32x32 output blocks of
+// v_mfma_f32_32x32x16_bf16.  K advances in stages of 64 (one INT4 group at
+// g = 64), one workgroup barrier per stage.
+//
+//   * Every global -> LDS transfer is an LDS-DMA load (global_load_lds_*): the
+//     activation rows (and the SPLIT planes) as 16-byte units straight into their
+//     swizzled LDS tile, the packed codes of the weight tile, and the per-row
+//     group steps, zero points or block scales (one dword slot per row).  No
+//     registers, no VALU.  They are issued from inline asm: with the compiler's
+//     own intrinsic it cannot tell which LDS bytes a load in flight writes and
+//     waits for every outstanding load before any LDS read, which would cost the
+//     prefetch depth.  The kernel counts them itself (loads complete in order):
+//     at the end of stage s each wave waits until only the loads it issued in
+//     stage s are outstanding, then the barrier publishes everything older.
+//   * Prefetch distances: activations 2 stages (ring of 3 LDS tiles), codes and
+//     per-row scalars 3 stages (rings of 3 and 4), so each load has about two
+//     stages of MFMA work to land.  SPLIT (no dequantization, twice the MFMAs per
+//     stage) prefetches activations and planes 1 stage ahead (rings of 2).
+//   * INT4 / FP4 weights are dequantized one stage ahead from the LDS codes into
+//     a bf16 LDS tile (two buffers), once per block: each weight row feeds BM
+//     activation rows.
 //   * LDS rows are 128 bytes (64 bf16, 8 units of 16 bytes) with unit u of row r
 //     stored at u ^ (r & 7): the 8 rows read by each 8-lane phase of a
 //     ds_read_b128 hit 8 different bank groups.
@@ -37,13 +50,15 @@
 //     contiguous range of a grouped tile order (a few row tiles, all column
 //     tiles), so the blocks it runs together share their activation and weight
 //     tiles in its L2.
-//   * INT4: the MFMAs of one group run block by block into a 4-register
-//     temporary that is rescaled by S[n, g] straight into the VGPR-resident
-//     output (one v_fmac per output element per group); a group wider than a
-//     stage (g = 128) is rescaled once per stage with the same S.
-// A lane of a 16x16x32 MFMA holds row (lane % 16) and k = 8 (lane / 16) .. +7 of
-// each operand; its 4 results are column (lane % 16), rows 4 (lane / 16) + v,
-// so they share one weight row n and need one S per 16x16 block per group.
+//   * INT4: the MFMAs of one group run block by block into a temporary that is
+//     rescaled by S[n, g] straight into the VGPR-resident output (one v_fma per
+//     output element per group), software-pipelined one block behind the MFMAs.
+//     A group wider than a stage (g = 128) is rescaled once per stage with the
+//     same S.
+// A lane of a 32x32x16 MFMA holds row (lane % 32) and k = 8 (lane / 32) .. +7 of
+// each operand; its 16 results are column (lane % 32), rows
+// 8 (i / 4) + 4 (lane / 32) + (i % 4), so they share one weight row n and need
+// one S per block per group.
 #include <type_traits>
 
 #include "aq_device.h"
@@ -82,14 +97,35 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ int swz(int row, int unit) { return row * ROW_UNITS + (unit ^ (row & 7)); }
 
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(const lds_void*)p; }
+
+// LDS-DMA loads: lane l's bytes land at lds + 16 l (dwordx4) or in the dword slot
+// lds + 4 l, zero-extended (dword / ushort / ubyte).  `base` is wave-uniform (SGPRs),
+// `voff` the lane's 32-bit byte offset.  M0 holds the LDS base; s_nop covers the
+// M0-write -> LDS-DMA hazard.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma2(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_ushort %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma1(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_ubyte %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+
 // gfx9 s_waitcnt immediate that waits for vmcnt <= n and lgkmcnt == 0 (expcnt untouched).
 constexpr int vmcnt_lgkm0_imm(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14); }
 
-// Workgroup barrier for the stage hand-off.  The caller has already waited for
-// what the next stage reads (its own LDS writes: lgkmcnt(0); its direct LDS loads
-// of the next stage: vmcnt(n)).  A __syncthreads() here would also wait for the
-// direct loads of the stage after next (vmcnt(0)) and cost the prefetch depth; the
-// asm's memory clobber keeps the compiler from moving LDS accesses across it.
+// Workgroup barrier for the stage hand-off; the caller has already waited for its
+// own LDS writes and LDS-DMA loads.  The memory clobber keeps the compiler from
+// moving LDS accesses across it.
 __device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // Tile index of block b under the XCD-aware order (b runs on XCD b % 8).
@@ -100,21 +136,34 @@ __device__ __forceinline__ int tile_of_block(int b, int nblk) {
   return start + local;
 }
 
-template <int BK, int MI, int G, bool TAIL>
-__global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
-  constexpr int WM = 16 * MI, BM = 2 * WM;
-  constexpr int PLANES = (BK == B_SPLIT) ? 2 : 1;
-  constexpr int A_INST = BM / 8 / 4;             // direct-load instructions per wave per stage (8 rows each)
-  constexpr int B_INST = BN / 8 / 4;
-  // activation ring: NA buffers, prefetched NA - 1 stages ahead (3 when LDS allows)
-  constexpr int NA = (BK == B_SPLIT) ? 2 : 3;
+template <int BK, int G, bool TAIL, int WGM>
+__global__ __launch_bounds__(128 * WGM, 1) void gemm_kernel(GemmArgs a) {
+  constexpr int NW = 2 * WGM, NT = 64 * NW;
+  constexpr int BM = 64 * WGM;
+  constexpr bool DEQ = BK != B_SPLIT;
+  constexpr int NA = DEQ ? 3 : 2;                   // activation ring
+  constexpr int PD = NA - 1;                        // activation prefetch distance
+  constexpr int CD = 3;                             // code / per-row scalar prefetch distance
+  constexpr int A_DMA = BM / 8 / NW;                // activation loads per wave per stage (8 rows each)
+  constexpr int B_DMA = DEQ ? 0 : 2 * (BN / 8) / NW;  // SPLIT plane loads per wave per stage
+  // code + per-row scalar loads per stage: 4 code loads (1 KB each) and the scalars
+  // (INT4: steps and zero points, two 64-row halves per group, one or two groups per
+  // stage, the zero-point loads repeated at g = 32 so every wave issues the same
+  // number; FP4: two ushorts of block scales per row)
+  constexpr int NAUX = (BK == B_INT4 && G == 32) ? 12 : 4;
+  constexpr int JOBS = DEQ ? 4 + NAUX : 0;
+  constexpr int JPW = JOBS / NW;
+  static_assert(!DEQ || JOBS % NW == 0, "scalar loads must split evenly over the waves");
 
   __shared__ __attribute__((aligned(16))) uint16_t As[NA][BM * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][PLANES][BN * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][DEQ ? 1 : 2][BN * KS];
+  __shared__ __attribute__((aligned(16))) uint8_t Cs[DEQ ? 3 : 1][BN * KS / 2];
+  // per-row scalars: [slot][INT4: 0 = S bits, 1 = zero point | FP4: 0][group in stage or FP4 half][row]
+  __shared__ __attribute__((aligned(16))) uint32_t AX[DEQ ? 4 : 1][2][2][BN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wid = tid >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wid >> 1, wn = wid & 1;
   const int M = a.M, N = a.N, K = a.K;
   const int tiles_n = (N + BN - 1) / BN;
@@ -132,305 +181,313 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
   const int n0 = (within / gm) * BN;
   const int nfull = K / KS;                    // full 64-wide stages; TAIL adds one 32-wide stage
   const int nstage = nfull + (TAIL ? 1 : 0);
+  const int ngroups = K / G;
 
-  // ---- direct global -> LDS loads of the activation tile (and SPLIT planes) ----
-  // instruction j of wave w covers tile rows R0 = (j * 4 + w) * 8 .. + 8; lane l
-  // lands at LDS unit (R0 + l / 8, l % 8) and fetches global unit (l % 8) ^ (row & 7).
-  // Offsets are 32-bit byte offsets of the stage-0 unit (M * K and N * K < 2^30).
-  const int lrow8 = lane >> 3, lunit = lane & 7;
-  const int gunit = lunit ^ lrow8;   // row & 7 == lane / 8 since R0 is a multiple of 8
-  uint32_t aoff[A_INST];
+  // ---- LDS-DMA loads --------------------------------------------------------
+  // Tile rows: load j of wave w covers rows R0 = (j NW + w) 8 .. + 8; lane l lands at
+  // LDS unit (R0 + l / 8, l % 8) and fetches global unit (l % 8) ^ (l / 8), which is
+  // the swizzle since R0 is a multiple of 8.  Offsets are 32-bit (M K, N K < 2^30).
+  // In the 32-wide tail stage the upper four units are folded back onto the lower
+  // four (loaded, never multiplied), so no load runs past a row.
+  const int lrow8 = lane >> 3;
+  const int gunit = (lane & 7) ^ lrow8;
+  const uint32_t tail_fold = (TAIL && gunit >= 4) ? 64u : 0u;
+  uint32_t aoff[A_DMA];
 #pragma unroll
-  for (int j = 0; j < A_INST; ++j) {
-    const int row = (j * 4 + wid) * 8 + lrow8;
+  for (int j = 0; j < A_DMA; ++j) {
+    const int row = (j * NW + wid) * 8 + lrow8;
     aoff[j] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)K * 2u + (uint32_t)gunit * 16u;
   }
-  // byte offset of stage s for this lane's unit; in the 32-wide tail stage the upper
-  // four units are folded back onto the lower four (loaded, never multiplied)
-  auto stage_off = [&](int s) -> uint32_t {
-    const uint32_t base = (uint32_t)s * (KS * 2);
-    return (TAIL && s == nfull && gunit >= 4) ? base - 64u : base;
+  auto issue_a = [&](int s, int slot) {
+    const char* base = reinterpret_cast<const char*>(a.X) + (size_t)s * (KS * 2);
+    const uint32_t fold = (TAIL && s == nfull) ? tail_fold : 0u;
+#pragma unroll
+    for (int j = 0; j < A_DMA; ++j) dma16(base, aoff[j] - fold, lds_addr(&As[slot][(j * NW + wid) * 8 * KS]));
   };
-  auto issue_a = [&](int s, int abuf) {
-    const char* xb = reinterpret_cast<const char*>(a.X);
-    const uint32_t so = stage_off(s);
-    uint16_t* dst = &As[abuf][0];
+  auto issue_planes = [&](int s, int slot) {
+    if constexpr (!DEQ) {
+      const uint32_t fold = (TAIL && s == nfull) ? tail_fold : 0u;
 #pragma unroll
-    for (int j = 0; j < A_INST; ++j) {
-      const int r0 = (j * 4 + wid) * 8;
-      __builtin_amdgcn_global_load_lds((const void*)(xb + aoff[j] + so), (lds_void*)&dst[r0 * KS], 16, 0, 0);
-    }
-  };
-  auto issue_b_planes = [&](int s, int buf) {
-    if constexpr (BK == B_SPLIT) {
-      const uint32_t so = stage_off(s);
+      for (int pl = 0; pl < 2; ++pl) {
+        const char* base = reinterpret_cast<const char*>(pl ? a.B2 : a.B) + (size_t)s * (KS * 2);
 #pragma unroll
-      for (int pl = 0; pl < 2; ++pl)
-#pragma unroll
-        for (int j = 0; j < B_INST; ++j) {
-          const int r0 = (j * 4 + wid) * 8;
+        for (int j = 0; j < BN / 8 / NW; ++j) {
+          const int r0 = (j * NW + wid) * 8;
           const uint32_t off = (uint32_t)min(n0 + r0 + lrow8, N - 1) * (uint32_t)K * 2u + (uint32_t)gunit * 16u;
-          const char* base = reinterpret_cast<const char*>(pl ? a.B2 : a.B);
-          __builtin_amdgcn_global_load_lds((const void*)(base + off + so), (lds_void*)&Bs[buf][pl][r0 * KS], 16, 0, 0);
+          dma16(base, off - fold, lds_addr(&Bs[slot][pl][r0 * KS]));
         }
+      }
+    }
+  };
+  // codes (32 bytes per row and stage, two 16-byte halves per lane pair) and the
+  // per-row scalars of stage s
+  auto issue_codes = [&](int s, int cslot, int xslot) {
+    if constexpr (DEQ) {
+      const bool tail = TAIL && s == nfull;
+#pragma unroll
+      for (int i = 0; i < JPW; ++i) {
+        const int job = wid * JPW + i;   // wave-uniform
+        if (job < 4) {
+          const int r = 32 * job + (lane >> 1);
+          const uint32_t n = (uint32_t)min(n0 + r, N - 1);
+          const uint32_t half = tail ? 0u : (uint32_t)(lane & 1) * 16u;
+          const uint8_t* src = (BK == B_INT4) ? a.P : a.codes;
+          dma16(src + (size_t)s * (KS / 2), n * (uint32_t)(K >> 1) + half, lds_addr(&Cs[cslot][1024 * job]));
+        } else if constexpr (BK == B_INT4) {
+          int x = job - 4;
+          if (x >= 8) x -= 4;                                  // repeated zero-point loads (g = 32)
+          const int is_z = (G == 32) ? (x >= 4) : (x >= 2);
+          const int gi = (G == 32) ? ((x >> 1) & 1) : 0;
+          const int rh = 64 * (x & 1);
+          const uint32_t n = (uint32_t)min(n0 + rh + lane, N - 1);
+          const uint32_t g = (uint32_t)min((s * KS + 32 * gi) / G, ngroups - 1);
+          const uint32_t idx = n * (uint32_t)ngroups + g;
+          if (is_z) dma1(a.Z, idx, lds_addr(&AX[xslot][1][gi][rh]));
+          else dma4(a.S, idx * 4u, lds_addr(&AX[xslot][0][gi][rh]));
+        } else {
+          const int x = job - 4;
+          const int h = x >> 1, rh = 64 * (x & 1);
+          const uint32_t n = (uint32_t)min(n0 + rh + lane, N - 1);
+          const uint32_t byte = (uint32_t)(s * 4 + 2 * (tail ? 0 : h));   // the tail stage has 2 block scales
+          dma2(a.bscale, n * (uint32_t)(K >> 4) + byte, lds_addr(&AX[xslot][0][h][rh]));
+        }
+      }
     }
   };
 
-  // ---- weight codes: one 16-byte load per thread per stage, dequantized into LDS ----
-  const int b_row = tid >> 1;       // tile row (weight row n0 + b_row)
-  const int b_half = tid & 1;       // k half of the stage: 32 values = 4 units
-  const int b_n = min(n0 + b_row, N - 1);
-  u32x4 braw;
-  uint32_t bzb = 0;                 // INT4 zero point of the half's group (raw byte)
-  float bsc0 = 0.0f, bsc1 = 0.0f;   // FP4 block scales of the half's two 16-blocks
-  auto load_b = [&](int s) {
-    if constexpr (BK != B_SPLIT) {
-      int k0 = s * KS + b_half * 32;
-      if (TAIL && k0 >= K) k0 -= 32;
-      if constexpr (BK == B_INT4) {
-        braw = *reinterpret_cast<const u32x4*>(a.P + (int64_t)b_n * (K >> 1) + (k0 >> 1));
-        bzb = a.Z[(int64_t)b_n * (K / G) + k0 / G];
+  // ---- dequantization: codes of one stage -> bf16 weight tile ----------------
+  constexpr int TPR = NT / BN;          // threads per weight row
+  constexpr int KPT = KS / TPR;         // k per thread (16 or 32)
+  constexpr int WPT = KPT / 8;          // 8-code words (= LDS units) per thread
+  const int d_row = tid / TPR, d_part = tid % TPR;
+  // `tail`: stage s is the 32-wide tail (only its first 32 k are dequantized)
+  auto dequant = [&](int cslot, int xslot, int bbuf, bool tail) {
+    if constexpr (DEQ) {
+      if (tail && d_part * KPT >= 32) return;
+      uint32_t w[WPT];
+      const uint8_t* cp = &Cs[cslot][d_row * 32 + d_part * (KPT / 2)];
+      if constexpr (WPT == 2) {
+        const uint2 v = *reinterpret_cast<const uint2*>(cp);
+        w[0] = v.x; w[1] = v.y;
       } else {
-        braw = *reinterpret_cast<const u32x4*>(a.codes + (int64_t)b_n * (K >> 1) + (k0 >> 1));
-        const uint32_t two = *reinterpret_cast<const uint16_t*>(a.bscale + (int64_t)b_n * (K >> 4) + (k0 >> 4));
-        bsc0 = __builtin_amdgcn_cvt_f32_fp8((int)two, 0);
-        bsc1 = __builtin_amdgcn_cvt_f32_fp8((int)two, 1);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(cp);
+        w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
       }
-    }
-  };
-  auto store_b = [&](int buf) {
-    if constexpr (BK != B_SPLIT) {
-      const float bz = (float)bzb;
-      uint32_t w[16];
+      u32x4* dst = reinterpret_cast<u32x4*>(&Bs[bbuf][0][0]);
+      if constexpr (BK == B_INT4) {
+        const int gi = (G == 32) ? (d_part * KPT) / 32 : 0;
+        const float zf = (float)AX[xslot][1][gi][d_row];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t lo = braw[d] & 0x0F0F0F0Fu, hi = (braw[d] >> 4) & 0x0F0F0F0Fu;
+        for (int u = 0; u < WPT; ++u) {
+          uint32_t lo = w[u] & 0x0F0F0F0Fu, hi = (w[u] >> 4) & 0x0F0F0F0Fu;
+          // opaque to the optimizer, so each code converts with one v_cvt_f32_ubyteN
+          asm("" : "+v"(lo), "+v"(hi));
+          uint32_t o[4];
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-          if constexpr (BK == B_INT4) {
-            const float ql = (float)((lo >> (8 * bb)) & 0xFFu), qh = (float)((hi >> (8 * bb)) & 0xFFu);
-            w[4 * d + bb] = pack_bf16_exact(ql - bz, qh - bz);
-          } else {
+          for (int b = 0; b < 4; ++b) {
+            const float ql = (float)((lo >> (8 * b)) & 0xFFu), qh = (float)((hi >> (8 * b)) & 0xFFu);
+            o[b] = pack_bf16_exact(ql - zf, qh - zf);
+          }
+          dst[swz(d_row, d_part * WPT + u)] = u32x4{o[0], o[1], o[2], o[3]};
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < WPT; ++u) {
+          // 16-element block of word u: (d_part KPT + 8 u) / 16 within the stage
+          const int blk = (d_part * KPT + 8 * u) >> 4;
+          const uint32_t two = AX[xslot][0][blk >> 1][d_row];
+          const float sc = (blk & 1) ? __builtin_amdgcn_cvt_f32_fp8((int)two, 1) : __builtin_amdgcn_cvt_f32_fp8((int)two, 0);
+          uint32_t o[4];
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
             uint32_t e2;
-            switch (bb) {
-              case 0: e2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(braw[d], 1.0f, 0)); break;
-              case 1: e2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(braw[d], 1.0f, 1)); break;
-              case 2: e2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(braw[d], 1.0f, 2)); break;
-              default: e2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(braw[d], 1.0f, 3)); break;
+            switch (b) {
+              case 0: e2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[u], 1.0f, 0)); break;
+              case 1: e2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[u], 1.0f, 1)); break;
+              case 2: e2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[u], 1.0f, 2)); break;
+              default: e2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[u], 1.0f, 3)); break;
             }
-            const float sc = d < 2 ? bsc0 : bsc1;
-            w[4 * d + bb] = pack_bf16_exact(bf16_lo(e2) * sc, bf16_hi(e2) * sc);
+            o[b] = pack_bf16_exact(bf16_lo(e2) * sc, bf16_hi(e2) * sc);
           }
+          dst[swz(d_row, d_part * WPT + u)] = u32x4{o[0], o[1], o[2], o[3]};
         }
       }
-      u32x4* dst = reinterpret_cast<u32x4*>(&Bs[buf][0][0]);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        dst[swz(b_row, b_half * 4 + u)] = u32x4{w[4 * u], w[4 * u + 1], w[4 * u + 2], w[4 * u + 3]};
     }
   };
 
-  // ---- accumulators: 16x16 output blocks of v_mfma_f32_16x16x32_bf16 ----------
-  // lane l holds column (l % 16) and k = 8 (l / 16) .. +7 of each operand; its 4
-  // results are rows 4 (l / 16) + v, column (l % 16).
-  constexpr int MB = MI, NB = 4;   // 16x16 blocks per wave tile (wave tile WM x 64)
-  f32x4 acc[MB][NB];
+  // ---- accumulators: 32x32 output blocks (mi, ni) of the 64 x 64 wave tile ----
+  f32x16 acc[2][2];
 #pragma unroll
-  for (int i = 0; i < MB; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.0f;
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  const int l16 = lane & 15;
-  const int lq = lane >> 4;           // k quarter: 8 values of a 32-wide MFMA step
-  const int ngroups = K / G;
-  const int ncol0 = n0 + wn * 64 + l16;
+  const int l32 = lane & 31;
+  const int lh = lane >> 5;           // k half of a 16-wide MFMA step
+  const u32x4* Av = reinterpret_cast<const u32x4*>(&As[0][0]);
   const u32x4* Bv = reinterpret_cast<const u32x4*>(&Bs[0][0][0]);
-  constexpr int A_BUF = BM * KS / 8, B_BUF = PLANES * BN * KS / 8, B_PLANE = BN * KS / 8;  // in 16-byte units
-  // direct loads issued per stage by one wave (activations, plus the SPLIT planes)
-  constexpr int DIRECT = A_INST + (BK == B_SPLIT ? 2 * B_INST : 0);
+  constexpr int A_BUF = BM * KS / 8, B_BUF = (DEQ ? 1 : 2) * BN * KS / 8, B_PLANE = BN * KS / 8;  // 16-byte units
 
-  // group steps S[n, g] of the (one or two) groups a stage touches, per n-block
-  auto load_gs = [&](int s, float (&out)[2][NB]) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int g = min((s * KS + 32 * ks) / G, ngroups - 1);
-#pragma unroll
-      for (int j = 0; j < NB; ++j) out[ks][j] = a.S[(int64_t)min(ncol0 + 16 * j, N - 1) * ngroups + g];
+  // NKS: 16-wide MFMA steps of stage s (4, or 2 in the tail); NXT: the same for the
+  // stage whose weights are dequantized here (0 for the last stage)
+  auto run_stage = [&](int s, auto nk_tag, auto nx_tag) {
+    constexpr int NKS = decltype(nk_tag)::value;
+    constexpr int NXT = decltype(nx_tag)::value;
+    const int abuf = s % NA;
+    const int bbuf = s & 1;
+    const int xs = s & 3;
+    // 1. prefetch: codes / scalars of stage s + 3, activations of stage s + 2 (SPLIT:
+    //    activations and planes of stage s + 1)
+    const bool more_c = DEQ && s + CD < nstage;
+    const bool more_a = s + PD < nstage;
+    if (more_c) issue_codes(s + CD, (s + CD) % 3, (s + CD) & 3);
+    if (more_a) {
+      issue_a(s + PD, (s + PD) % NA);
+      issue_planes(s + PD, (s + PD) & 1);
     }
-  };
-  float gs[2][NB];
-  if constexpr (BK == B_INT4) load_gs(0, gs);
-
-  auto run_stage = [&](int s, auto nk_tag) {
-    constexpr int nk32 = decltype(nk_tag)::value;   // 32-wide MFMA steps in this stage
-    const int abuf = s % NA;                          // activation buffer
-    const int buf = s & 1;                            // weight buffer
-    const u32x4* Av = reinterpret_cast<const u32x4*>(&As[abuf][0]);
-    const bool more = s + 1 < nstage;
-    // register loads of the next stage first (weight codes, zero points, group
-    // steps), pinned ahead of the direct activation loads: loads complete in order,
-    // so waiting for them never waits for the activation prefetch behind them
-    if (more) load_b(s + 1);
-    float gs_next[2][NB];
+    // 2. fragments of this stage
+    bf16x8 af[2][NKS], bf[2][NKS], bf2[2][NKS];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        af[mi][ks] = __builtin_bit_cast(bf16x8, Av[abuf * A_BUF + swz(wm * 64 + 32 * mi + l32, 2 * ks + lh)]);
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int row = wn * 64 + 32 * ni + l32;
+        bf[ni][ks] = __builtin_bit_cast(bf16x8, Bv[bbuf * B_BUF + swz(row, 2 * ks + lh)]);
+        if constexpr (!DEQ) bf2[ni][ks] = __builtin_bit_cast(bf16x8, Bv[bbuf * B_BUF + B_PLANE + swz(row, 2 * ks + lh)]);
+      }
+    // 3. MFMAs
     if constexpr (BK == B_INT4) {
-      if (more) load_gs(s + 1, gs_next);
-    }
-    asm volatile("" ::: "memory");
-    bool issued = false;
-    if constexpr (NA == 3) {
-      if (s + 2 < nstage) {
-        issue_a(s + 2, (s + 2) % NA);
-        issued = true;
-      }
-    } else if (more) {
-      issue_a(s + 1, abuf ^ 1);
-      issue_b_planes(s + 1, buf ^ 1);
-      issued = true;
-    }
-    asm volatile("" ::: "memory");
-    bf16x8 bfr[NB][2], bf2[NB][2];
+      constexpr int NG = (G == 32) ? NKS / 2 : 1;   // group partials per block in this stage
+      constexpr int KPG = NKS / NG;
+      float sc[2][NG];
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
+      for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-      for (int ks = 0; ks < nk32; ++ks) {
-        const int row = wn * 64 + 16 * j + l16;
-        bfr[j][ks] = __builtin_bit_cast(bf16x8, Bv[buf * B_BUF + swz(row, 4 * ks + lq)]);
-        if constexpr (BK == B_SPLIT)
-          bf2[j][ks] = __builtin_bit_cast(bf16x8, Bv[buf * B_BUF + B_PLANE + swz(row, 4 * ks + lq)]);
-      }
-    // software pipeline over the m-blocks: the A fragments of block i + 1 are read
-    // while block i's MFMAs run, and block i - 1 is rescaled after block i's MFMAs
-    // are issued (hides LDS and MFMA latency with one wave per SIMD).
-    auto load_af = [&](int i, bf16x8* af) {
-      const int arow = wm * WM + 16 * i + l16;
+        for (int gi = 0; gi < NG; ++gi) sc[ni][gi] = __builtin_bit_cast(float, AX[xs][0][gi][wn * 64 + 32 * ni + l32]);
+      // (group, block) pairs in order; each block's rescale runs one pair behind its MFMAs
+      f32x16 tprev;
 #pragma unroll
-      for (int ks = 0; ks < nk32; ++ks) af[ks] = __builtin_bit_cast(bf16x8, Av[swz(arow, 4 * ks + lq)]);
-    };
-    bf16x8 afc[2], afn[2];
-    load_af(0, afc);
-    if constexpr (BK == B_INT4) {
-      constexpr bool ONE_GROUP = (G >= KS) && (nk32 == 2);   // both 32-steps share one group
-      constexpr int NT = ONE_GROUP ? 1 : nk32;                // partial sums per block per stage
-      f32x4 tpp[NT][NB];                                      // previous block's partials
+      for (int it = 0; it < 4 * NG; ++it) {
+        const int gi = it >> 2, mi = (it >> 1) & 1, ni = it & 1;
+        f32x16 tp;
 #pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        if (i + 1 < MB) load_af(i + 1, afn);
-        f32x4 tpc[NT][NB];
-#pragma unroll
-        for (int ks = 0; ks < nk32; ++ks) {
-          const int tix = ONE_GROUP ? 0 : ks;
-#pragma unroll
-          for (int j = 0; j < NB; ++j) {
-            const f32x4 zero = {};
-            tpc[tix][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afc[ks], bfr[j][ks],
-                                                                 (ONE_GROUP && ks == 1) ? tpc[tix][j] : zero, 0, 0, 0);
-          }
+        for (int k = 0; k < KPG; ++k) {
+          const int ks = gi * KPG + k;
+          const f32x16 zero = {};
+          tp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi][ks], bf[ni][ks], k == 0 ? zero : tp, 0, 0, 0);
         }
-        if (i > 0) {
+        if (it > 0) {
+          const int pg = (it - 1) >> 2, pm = ((it - 1) >> 1) & 1, pn = (it - 1) & 1;
 #pragma unroll
-          for (int tix = 0; tix < NT; ++tix)
-#pragma unroll
-            for (int j = 0; j < NB; ++j)
-#pragma unroll
-              for (int v = 0; v < 4; ++v)
-                acc[i - 1][j][v] = __builtin_fmaf(gs[tix][j], tpp[tix][j][v], acc[i - 1][j][v]);
+          for (int v = 0; v < 16; ++v) acc[pm][pn][v] = __builtin_fmaf(sc[pn][pg], tprev[v], acc[pm][pn][v]);
         }
-#pragma unroll
-        for (int tix = 0; tix < NT; ++tix)
-#pragma unroll
-          for (int j = 0; j < NB; ++j) tpp[tix][j] = tpc[tix][j];
-        if (i + 1 < MB) {
-          afc[0] = afn[0];
-          afc[1] = afn[1];
-        }
+        tprev = tp;
       }
 #pragma unroll
-      for (int tix = 0; tix < NT; ++tix)
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            acc[MB - 1][j][v] = __builtin_fmaf(gs[tix][j], tpp[tix][j][v], acc[MB - 1][j][v]);
+      for (int v = 0; v < 16; ++v) acc[1][1][v] = __builtin_fmaf(sc[1][NG - 1], tprev[v], acc[1][1][v]);
     } else {
 #pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        if (i + 1 < MB) load_af(i + 1, afn);
+      for (int b = 0; b < 4; ++b) {
+        const int mi = b >> 1, ni = b & 1;
 #pragma unroll
-        for (int ks = 0; ks < nk32; ++ks)
-#pragma unroll
-          for (int j = 0; j < NB; ++j) {
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afc[ks], bfr[j][ks], acc[i][j], 0, 0, 0);
-            if constexpr (BK == B_SPLIT)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afc[ks], bf2[j][ks], acc[i][j], 0, 0, 0);
-          }
-        if (i + 1 < MB) {
-          afc[0] = afn[0];
-          afc[1] = afn[1];
+        for (int ks = 0; ks < NKS; ++ks) {
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi][ks], bf[ni][ks], acc[mi][ni], 0, 0, 0);
+          if constexpr (!DEQ)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi][ks], bf2[ni][ks], acc[mi][ni], 0, 0, 0);
         }
       }
     }
-    if (more) store_b(buf ^ 1);
-    if constexpr (BK == B_INT4) {
-      if (more) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int j = 0; j < NB; ++j) gs[ks][j] = gs_next[ks][j];
-      }
-    }
-    // this wave's direct loads for the next stage have landed (loads return in order;
-    // the ones issued during this stage, for the stage after next, may still fly)
-    if (NA == 3 && issued) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(DIRECT));
+    // 4. weights of the next stage (its codes were published one barrier ago)
+    if constexpr (DEQ && NXT > 0) dequant((s + 1) % 3, (s + 1) & 3, bbuf ^ 1, NXT == 2);
+    // 5. wait until only this stage's loads are outstanding (loads complete in order),
+    //    and for this wave's LDS writes; then publish
+    //    (SPLIT prefetches one stage ahead: everything issued so far is needed next)
+    if (DEQ && more_c) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(JPW + A_DMA));
+    else if (DEQ && more_a) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(A_DMA));
     else __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
     stage_barrier();
   };
 
-  // ---- prologue and main loop ------------------------------------------------
-  load_b(0);
-  issue_a(0, 0);
-  issue_b_planes(0, 0);
-  if (NA == 3 && nstage > 1) issue_a(1, 1);
-  store_b(0);
-  if (NA == 3 && nstage > 1) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(DIRECT));
-  else __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
-  stage_barrier();
-  for (int s = 0; s < nfull; ++s) run_stage(s, std::integral_constant<int, 2>{});
-  if constexpr (TAIL) run_stage(nfull, std::integral_constant<int, 1>{});
+  // ---- prologue --------------------------------------------------------------
+  if constexpr (DEQ) {
+    // P0 = stage 0 (codes, activations), P1 = stage 1 (codes, activations), P2 = codes of stage 2
+    issue_codes(0, 0, 0);
+    issue_a(0, 0);
+    if (nstage > 1) {
+      issue_codes(1, 1, 1);
+      issue_a(1, 1);
+    }
+    if (nstage > 2) issue_codes(2, 2, 2);
+    if (nstage > 2) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(2 * JPW + A_DMA));
+    else if (nstage > 1) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(JPW + A_DMA));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
+    stage_barrier();
+    dequant(0, 0, 0, TAIL && nfull == 0);
+    if (nstage > 2) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(JPW));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
+    stage_barrier();
+  } else {
+    issue_a(0, 0);
+    issue_planes(0, 0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
+    stage_barrier();
+  }
+  using IC4 = std::integral_constant<int, 4>;
+  using IC2 = std::integral_constant<int, 2>;
+  using IC0 = std::integral_constant<int, 0>;
+  for (int s = 0; s + 1 < nfull; ++s) run_stage(s, IC4{}, IC4{});
+  if constexpr (TAIL) {
+    if (nfull > 0) run_stage(nfull - 1, IC4{}, IC2{});
+    run_stage(nfull, IC2{}, IC0{});
+  } else {
+    run_stage(nfull - 1, IC4{}, IC0{});
+  }
 
   // ---- epilogue --------------------------------------------------------------
+  // result i of block (mi, ni): row 8 (i / 4) + 4 lh + (i % 4), column l32
   if constexpr (BK == B_SPLIT) {
     double ss = 0.0;
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
+    for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int n = n0 + wn * 64 + 16 * j + l16;
+      for (int ni = 0; ni < 2; ++ni) {
+        const int n = n0 + wn * 64 + 32 * ni + l32;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int m = m0 + wm * WM + 16 * i + 4 * lq + v;
-          const double d = (double)acc[i][j][v];
+        for (int v = 0; v < 16; ++v) {
+          const int m = m0 + wm * 64 + 32 * mi + 8 * (v >> 2) + 4 * lh + (v & 3);
+          const double d = (double)acc[mi][ni][v];
           if (m < M && n < N) ss = __builtin_fma(d, d, ss);
         }
       }
     ss = wave_sum(ss);
-    __shared__ double wsum[4];
+    __shared__ double wsum[NW];
     if (lane == 0) wsum[wid] = ss;
     __syncthreads();
-    if (tid == 0) a.partial[t] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+    if (tid == 0) {
+      double tot = 0.0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) tot += wsum[w];
+      a.partial[t] = tot;
+    }
   } else {
     const bool full = (m0 + BM <= M) && (n0 + BN <= N);
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
+    for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int n = n0 + wn * 64 + 16 * j + l16;
+      for (int ni = 0; ni < 2; ++ni) {
+        const int n = n0 + wn * 64 + 32 * ni + l32;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int m = m0 + wm * WM + 16 * i + 4 * lq + v;
-          const float y = (BK == B_FP4) ? acc[i][j][v] * a.ts : acc[i][j][v];
-          if (full || (m < M && n < N)) a.Y[(int64_t)m * N + n] = y;
+        for (int v = 0; v < 16; ++v) {
+          const int m = m0 + wm * 64 + 32 * mi + 8 * (v >> 2) + 4 * lh + (v & 3);
+          const float y = (BK == B_FP4) ? acc[mi][ni][v] * a.ts : acc[mi][ni][v];
+          if (full || (m < M && n < N)) __builtin_nontemporal_store(y, &a.Y[(int64_t)m * N + n]);
         }
       }
   }
@@ -438,19 +495,16 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
 
 int tiles(int M, int N, int bm) { return ((M + bm - 1) / bm) * ((N + BN - 1) / BN); }
 
+// 256-row tiles (8 waves) once M fills them; 128-row tiles (4 waves) for small M.
+constexpr int kWideM = 192;
+
 template <int BK, int G, bool TAIL>
 hipError_t launch_tail(const GemmArgs& a, hipStream_t stream) {
-  const dim3 block(256);
-  // INT4 keeps the running output and the group partials in VGPRs: 128-row tiles at
-  // two waves per SIMD.  FP4 / SPLIT accumulate straight into MFMA registers and use
-  // 256-row tiles for large M.
-  if constexpr (BK != B_INT4) {
-    if (a.M >= 2048) {
-      hipLaunchKernelGGL((gemm_kernel<BK, 8, G, TAIL>), dim3(tiles(a.M, a.N, 256)), block, 0, stream, a);
-      return hipGetLastError();
-    }
+  if (a.M > kWideM) {
+    hipLaunchKernelGGL((gemm_kernel<BK, G, TAIL, 4>), dim3(tiles(a.M, a.N, 256)), dim3(512), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((gemm_kernel<BK, G, TAIL, 2>), dim3(tiles(a.M, a.N, 128)), dim3(256), 0, stream, a);
   }
-  hipLaunchKernelGGL((gemm_kernel<BK, 4, G, TAIL>), dim3(tiles(a.M, a.N, 128)), block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -481,7 +535,7 @@ hipError_t launch_fp4_gemm(const uint16_t* X, int M, int K, const uint8_t* codes
   return launch_tiles<B_FP4, 64>(a, stream);
 }
 
-int sumsq_gemm_blocks(int M, int N) { return M >= 2048 ? tiles(M, N, 256) : tiles(M, N, 128); }  // SPLIT tiles
+int sumsq_gemm_blocks(int M, int N) { return M > kWideM ? tiles(M, N, 256) : tiles(M, N, 128); }  // SPLIT tiles
 
 hipError_t launch_sumsq_gemm(const uint16_t* X, int M, int K, const uint16_t* E, int N, double* partial,
                              hipStream_t stream) {
