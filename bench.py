@@ -7,7 +7,8 @@ group 64):
   pack     aq_quantize_pack of the bf16 weight                   (quantize + pack)
   gemv     aq_w4a16_gemv at M = 1, once on each of 40 distinct   (decode; 40 copies =
            packed weight copies, so every launch reads HBM         520 MB > the 256 MB MALL)
-  gemm     aq_w4a16_gemm at M = 4096                             (prefill, bf16 MFMA)
+  gemm     aq_w4a16_gemm at M = 4096                             (prefill, bf16 MFMA; staged
+           path: weights dequantized into a workspace, then the GEMM)
   absmean  aq_act_absmean over 65536 x 2048 calibration tokens   (AWQ statistic)
   search   aq_awq_search, 4096 tokens, 20 alphas, final pack     (AWQ search)
   fp4      aq_fp4_gemm at M = 1 and M = 2048 on W[14336, 4096]   (FP4 decode)
@@ -171,6 +172,8 @@ def main():
     xf2 = acts_bf16(FP4_M, FP4_K, round(0.01 * FP4_K))
     yf1 = torch.empty((1, FP4_N), dtype=torch.float32, device=dev)
     yf2 = torch.empty((FP4_M, FP4_N), dtype=torch.float32, device=dev)
+    ws_gemm = torch.empty(B.aq_w4a16_gemm_workspace(M_GEMM, N_, K_, G_), dtype=torch.uint8, device=dev)
+    ws_fp4 = torch.empty(B.aq_fp4_gemm_workspace(FP4_M, FP4_N, FP4_K), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     events = {k: [] for k in ("pack", "gemv", "gemm", "absmean", "search", "fp4_gemv", "fp4_gemm")}
@@ -195,12 +198,12 @@ def main():
                 B.aq_w4a16_gemv(x1, p, s, z, G_, out=y1)
         timed("gemv", record, gemv_batch)
         p, s, z = copies[0]
-        timed("gemm", record, lambda: B.aq_w4a16_gemm(xg, p, s, z, G_, out=yg))
+        timed("gemm", record, lambda: B.aq_w4a16_gemm(xg, p, s, z, G_, out=yg, workspace=ws_gemm))
         sum_abs.zero_()
         timed("absmean", record, lambda: B.aq_act_absmean(xcal, sum_abs, CAL_T, mean, ws_abs))
         timed("search", record, lambda: B.aq_awq_search(xsub, absmean_host, w_gate, G_, 20, ws_search))
         timed("fp4_gemv", record, lambda: B.aq_fp4_gemm(xf1, codes, bsc, ts, out=yf1))
-        timed("fp4_gemm", record, lambda: B.aq_fp4_gemm(xf2, codes, bsc, ts, out=yf2))
+        timed("fp4_gemm", record, lambda: B.aq_fp4_gemm(xf2, codes, bsc, ts, out=yf2, workspace=ws_fp4))
 
     print(f"[bench] warmup {args.warmup}", flush=True)
     for _ in range(args.warmup):

@@ -91,10 +91,22 @@ aq_status aq_w4a16_gemv(const uint16_t* X, int64_t M, int64_t K, const uint8_t* 
  * W4A16 prefill GEMM, any M >= 0 (tuned for M >= 64): bf16 MFMA on the exact
  * integer operand (q - z), fp32 group-step rescale per group, fp32 output.
  * Same sources, arguments and formula as aq_w4a16_gemv.
- * Errors: EINVAL for M < 0 or M >= 2^30, and as aq_w4a16_gemv otherwise.
+ *
+ * Two paths with identical results (bit-identical outputs): fused (the kernel
+ * dequantizes each weight tile in LDS) and staged (a first kernel writes the
+ * exact bf16 (q - z) of every weight into `workspace`, the GEMM then streams it).
+ * The staged path runs when workspace is not NULL and workspace_bytes is at
+ * least aq_w4a16_gemm_workspace(M, N, K, group) > 0 (large M, where it is
+ * faster); otherwise the fused path runs and workspace is not touched.
+ * workspace: caller-owned device memory, 256-byte aligned, used only during the
+ * call on `stream` (its contents afterwards are unspecified).
+ * Errors: EINVAL for M < 0 or M >= 2^30, K >= 2^22, a misaligned workspace, and
+ *         as aq_w4a16_gemv otherwise.
  */
+size_t aq_w4a16_gemm_workspace(int64_t M, int64_t N, int64_t K, int32_t group);
 aq_status aq_w4a16_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_t* packed, const float* scales,
-                        const uint8_t* zeros, int64_t N, int32_t group, float* Y, void* stream);
+                        const uint8_t* zeros, int64_t N, int32_t group, float* Y, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 /*
  * Per-input-channel |x| statistic for AWQ calibration.
@@ -166,11 +178,16 @@ aq_status aq_awq_search(const uint16_t* X_sub, int64_t T, const float* absmean_h
  * code is the sign, bits 2..1 the exponent with bias 1, bit 0 the mantissa);
  * block_scales [N, K/16] uint8 E4M3 (OCP "FN": bias 7, no infinities, 0x7F /
  * 0xFF are NaN); Y [M, N] fp32 output.
+ * For M > 16 the GEMM has the same fused and staged paths as aq_w4a16_gemm
+ * (staged: the exact bf16 weights written to `workspace` first), selected the
+ * same way with aq_fp4_gemm_workspace(M, N, K).
  * Errors: EINVAL for M < 0, K <= 0 or K % 32, non-finite tensor_scale, N < 0,
- *         NULL / misaligned pointers, K or N >= 2^30.
+ *         NULL / misaligned pointers, K or N >= 2^30, K >= 2^22 when M > 16.
  */
+size_t aq_fp4_gemm_workspace(int64_t M, int64_t N, int64_t K);
 aq_status aq_fp4_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes, const uint8_t* block_scales,
-                      float tensor_scale, int64_t N, float* Y, void* stream);
+                      float tensor_scale, int64_t N, float* Y, void* workspace, size_t workspace_bytes,
+                      void* stream);
 
 /* Thread-local text for the last non-OK status of this thread ("" if none). */
 const char* aq_last_error(void);

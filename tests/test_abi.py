@@ -61,9 +61,16 @@ def test_quantize_pack_einval(lib, kw, frag):
 
 
 def _prod(lib, fn, **kw):
-    a = dict(X=FAKE, M=1, K=256, P=FAKE, S=FAKE, Z=FAKE, N=64, g=64, Y=FAKE)
+    a = dict(X=FAKE, M=1, K=256, P=FAKE, S=FAKE, Z=FAKE, N=64, g=64, Y=FAKE, ws=None, wsb=0)
     a.update(kw)
-    return getattr(lib, fn)(a["X"], a["M"], a["K"], a["P"], a["S"], a["Z"], a["N"], a["g"], a["Y"], None)
+    args = [a["X"], a["M"], a["K"], a["P"], a["S"], a["Z"], a["N"], a["g"], a["Y"]]
+    if fn == "aq_w4a16_gemm":
+        args += [a["ws"], a["wsb"]]
+    return getattr(lib, fn)(*args, None)
+
+
+def _fp4(lib, X=FAKE, M=1, K=64, C=FAKE, B=FAKE, ts=1.0, N=8, Y=FAKE, ws=None, wsb=0):
+    return lib.aq_fp4_gemm(X, M, K, C, B, ts, N, Y, ws, wsb, None)
 
 
 @pytest.mark.parametrize("kw", [dict(M=0), dict(M=17), dict(g=16), dict(K=100), dict(X=None), dict(X=FAKE_ODD),
@@ -72,9 +79,32 @@ def test_gemv_einval(lib, kw):
     assert _prod(lib, "aq_w4a16_gemv", **kw) == _lib.AQ_EINVAL
 
 
-@pytest.mark.parametrize("kw", [dict(M=-1), dict(g=16), dict(K=100), dict(S=None), dict(Z=None), dict(K=0)])
+@pytest.mark.parametrize("kw", [dict(M=-1), dict(g=16), dict(K=100), dict(S=None), dict(Z=None), dict(K=0),
+                                dict(K=1 << 22)])
 def test_gemm_einval(lib, kw):
     assert _prod(lib, "aq_w4a16_gemm", **kw) == _lib.AQ_EINVAL
+
+
+def test_gemm_workspace_selects_the_staged_path(lib, monkeypatch):
+    """The staging matrix is N * K bf16 for large M, 0 below the threshold or for invalid
+    arguments; a large enough but misaligned workspace is rejected, a short one means
+    the fused path (no error)."""
+    need = lib.aq_w4a16_gemm_workspace(4096, 11008, 2048, 64)
+    assert need == 11008 * 2048 * 2
+    assert lib.aq_w4a16_gemm_workspace(64, 11008, 2048, 64) == 0
+    assert lib.aq_w4a16_gemm_workspace(2047, 11008, 2048, 64) == 0
+    assert lib.aq_w4a16_gemm_workspace(4096, 11008, 2048, 48) == 0
+    assert lib.aq_w4a16_gemm_workspace(4096, 11008, 2000, 64) == 0
+    assert lib.aq_fp4_gemm_workspace(2048, 14336, 4096) == 14336 * 4096 * 2
+    assert lib.aq_fp4_gemm_workspace(16, 14336, 4096) == 0
+    kw = dict(M=4096, N=512, K=256)
+    need = lib.aq_w4a16_gemm_workspace(4096, 512, 256, 64)
+    assert _prod(lib, "aq_w4a16_gemm", ws=FAKE + 16, wsb=need, **kw) == _lib.AQ_EINVAL
+    assert "workspace" in _lib.last_error()
+    assert _fp4(lib, M=4096, K=256, N=512, ws=FAKE + 16, wsb=need) == _lib.AQ_EINVAL
+    monkeypatch.setenv("AQ_FAULT_INJECT", "launch")
+    assert _prod(lib, "aq_w4a16_gemm", ws=FAKE + 16, wsb=need - 1, **kw) == _lib.AQ_ERUNTIME   # fused path
+    assert _prod(lib, "aq_w4a16_gemm", ws=FAKE, wsb=need, **kw) == _lib.AQ_ERUNTIME
 
 
 def test_empty_products_are_noops(lib):
@@ -82,7 +112,7 @@ def test_empty_products_are_noops(lib):
     assert _prod(lib, "aq_w4a16_gemm", N=0) == _lib.AQ_OK
     assert _prod(lib, "aq_w4a16_gemv", N=0) == _lib.AQ_OK
     assert _qp(lib, N=0) == _lib.AQ_OK
-    assert lib.aq_fp4_gemm(FAKE, 0, 64, FAKE, FAKE, 1.0, 8, FAKE, None) == _lib.AQ_OK
+    assert _fp4(lib, M=0) == _lib.AQ_OK
 
 
 def test_absmean_einval(lib):
@@ -128,12 +158,12 @@ def test_search_einval(lib):
 
 
 def test_fp4_einval(lib):
-    f = lib.aq_fp4_gemm
-    assert f(FAKE, 1, 48, FAKE, FAKE, 1.0, 8, FAKE, None) == _lib.AQ_EINVAL     # K % 32
-    assert f(FAKE, 1, 64, FAKE, FAKE, float("inf"), 8, FAKE, None) == _lib.AQ_EINVAL
-    assert f(FAKE, 1, 64, FAKE, FAKE, float("nan"), 8, FAKE, None) == _lib.AQ_EINVAL
-    assert f(FAKE, -1, 64, FAKE, FAKE, 1.0, 8, FAKE, None) == _lib.AQ_EINVAL
-    assert f(FAKE, 1, 64, FAKE_ODD, FAKE, 1.0, 8, FAKE, None) == _lib.AQ_EINVAL
+    assert _fp4(lib, K=48) == _lib.AQ_EINVAL     # K % 32
+    assert _fp4(lib, ts=float("inf")) == _lib.AQ_EINVAL
+    assert _fp4(lib, ts=float("nan")) == _lib.AQ_EINVAL
+    assert _fp4(lib, M=-1) == _lib.AQ_EINVAL
+    assert _fp4(lib, C=FAKE_ODD) == _lib.AQ_EINVAL
+    assert _fp4(lib, M=17, K=1 << 22) == _lib.AQ_EINVAL
 
 
 def test_injected_runtime_failure(lib, monkeypatch):
@@ -143,7 +173,7 @@ def test_injected_runtime_failure(lib, monkeypatch):
     assert "injected" in _lib.last_error()
     assert _prod(lib, "aq_w4a16_gemv") == _lib.AQ_ERUNTIME
     assert _prod(lib, "aq_w4a16_gemm", M=128) == _lib.AQ_ERUNTIME
-    assert lib.aq_fp4_gemm(FAKE, 1, 64, FAKE, FAKE, 1.0, 8, FAKE, None) == _lib.AQ_ERUNTIME
+    assert _fp4(lib) == _lib.AQ_ERUNTIME
     ws = lib.aq_act_absmean_workspace(64, 64)
     assert lib.aq_act_absmean(FAKE, 64, 64, FAKE, None, 64, FAKE, ws, None) == _lib.AQ_ERUNTIME
     # validation still wins over the injected fault

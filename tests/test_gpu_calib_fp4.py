@@ -172,6 +172,23 @@ def test_fp4_ragged(m, n, k):
     check_close(y, fp4.forward(synth.bf16_bits_to_f32(xb), c, b, ts), f"fp4 ragged {m}x{n}x{k}")
 
 
+@pytest.mark.parametrize("m,n,k", [(2048, 130, 96), (2048, 257, 512), (2100, 4100, 64)])
+def test_fp4_staged_equals_fused(m, n, k):
+    """FP4 GEMM: staged (exact bf16 weights in the workspace) and fused paths are bit-identical and
+    match the oracle."""
+    rng = np.random.default_rng(m + n + k + 1)
+    c, b, ts = fp4.encode((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+    xb = synth.f32_to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+    assert B.aq_fp4_gemm_workspace(m, n, k) == n * k * 2
+    step(f"aq_fp4_gemm staged M={m} N={n} K={k}")
+    ys = host(B.aq_fp4_gemm(dev_bf16(xb), dev(c), dev(b), ts))
+    step(f"aq_fp4_gemm fused M={m} N={n} K={k}")
+    yf = host(B.aq_fp4_gemm(dev_bf16(xb), dev(c), dev(b), ts, workspace=torch.empty(0, dtype=torch.uint8,
+                                                                                  device="cuda")))
+    assert np.array_equal(ys.view(np.uint32), yf.view(np.uint32))
+    check_close(ys, fp4.forward(synth.bf16_bits_to_f32(xb), c, b, ts), f"fp4 staged {m}x{n}x{k}")
+
+
 @pytest.mark.parametrize("m", [1, 5, 64, 300])
 def test_fp4_exact_case(m):
     """Small-integer X, every E2M1 code, block scales in {1/8 .. 4} and ts = 1: every product and

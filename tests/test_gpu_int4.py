@@ -205,6 +205,26 @@ def test_gemm_exact_integer_case(m, n, k, g):
     assert (y.astype(np.float64) == int4.forward(x, p, s, z, g)).all()
 
 
+@pytest.mark.parametrize("m,n,k,g", [(2048, 130, 96, 32), (2300, 257, 2080, 32), (3072, 384, 640, 128),
+                                     (2049, 257, 2112, 64), (4097, 129, 256, 64), (2100, 200, 32, 32)])
+def test_gemm_staged_equals_fused(m, n, k, g):
+    """The staged path (weights dequantized once into the workspace) and the fused path give
+    bit-identical outputs: the same exact bf16 operands, MFMA order and group rescales.  The
+    staged output is also checked against the oracle (ragged M and N, tail stages, K = 32)."""
+    rng = np.random.default_rng(m + 3 * n + k)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    p, s, z = int4.quantize_pack(w, g)
+    xb = synth.f32_to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+    assert B.aq_w4a16_gemm_workspace(m, n, k, g) == n * k * 2
+    step(f"aq_w4a16_gemm staged M={m} N={n} K={k} g={g}")
+    ys = host(B.aq_w4a16_gemm(dev_bf16(xb), dev(p), dev(s), dev(z), g))
+    step(f"aq_w4a16_gemm fused M={m} N={n} K={k} g={g}")
+    yf = host(B.aq_w4a16_gemm(dev_bf16(xb), dev(p), dev(s), dev(z), g,
+                              workspace=torch.empty(0, dtype=torch.uint8, device="cuda")))
+    assert np.array_equal(ys.view(np.uint32), yf.view(np.uint32))
+    check_close(ys, int4.forward(synth.bf16_bits_to_f32(xb), p, s, z, g), f"gemm staged {m}x{n}x{k}")
+
+
 def test_pack_then_gemv_round_trip():
     """Device pack followed by the device GEMV equals the oracle's pack + forward (the module-swap path)."""
     wb = synth.layer_weight_bf16(4, "o_proj")

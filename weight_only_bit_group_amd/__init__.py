@@ -7,8 +7,9 @@ does not load the library; the first binding call does, and fails loudly if it
 has not been built.
 """
 
-__all__ = ["aq_quantize_pack", "aq_w4a16_gemv", "aq_w4a16_gemm", "aq_act_absmean", "aq_act_absmean_workspace",
-           "aq_awq_search", "aq_awq_search_workspace", "aq_fp4_gemm"]
+__all__ = ["aq_quantize_pack", "aq_w4a16_gemv", "aq_w4a16_gemm", "aq_w4a16_gemm_workspace", "aq_act_absmean",
+           "aq_act_absmean_workspace", "aq_awq_search", "aq_awq_search_workspace", "aq_fp4_gemm",
+           "aq_fp4_gemm_workspace"]
 
 
 def __getattr__(name):

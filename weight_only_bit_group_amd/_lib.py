@@ -21,12 +21,14 @@ _SZ = ctypes.c_size_t
 SIGNATURES = {
     "aq_quantize_pack": (_I32, [_P, _I32, _I64, _I64, _I32, _P, _P, _P, _P, _P]),
     "aq_w4a16_gemv": (_I32, [_P, _I64, _I64, _P, _P, _P, _I64, _I32, _P, _P]),
-    "aq_w4a16_gemm": (_I32, [_P, _I64, _I64, _P, _P, _P, _I64, _I32, _P, _P]),
+    "aq_w4a16_gemm_workspace": (_SZ, [_I64, _I64, _I64, _I32]),
+    "aq_w4a16_gemm": (_I32, [_P, _I64, _I64, _P, _P, _P, _I64, _I32, _P, _P, _SZ, _P]),
     "aq_act_absmean_workspace": (_SZ, [_I64, _I64]),
     "aq_act_absmean": (_I32, [_P, _I64, _I64, _P, _P, _I64, _P, _SZ, _P]),
     "aq_awq_search_workspace": (_SZ, [_I64, _I64, _I64, _I32, _I32]),
     "aq_awq_search": (_I32, [_P, _I64, _P, _P, _I32, _I64, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
-    "aq_fp4_gemm": (_I32, [_P, _I64, _I64, _P, _P, ctypes.c_float, _I64, _P, _P]),
+    "aq_fp4_gemm_workspace": (_SZ, [_I64, _I64, _I64]),
+    "aq_fp4_gemm": (_I32, [_P, _I64, _I64, _P, _P, ctypes.c_float, _I64, _P, _P, _SZ, _P]),
     "aq_last_error": (ctypes.c_char_p, []),
 }
 

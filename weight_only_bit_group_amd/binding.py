@@ -74,7 +74,20 @@ def aq_quantize_pack(W: torch.Tensor, group: int, chan_scale: torch.Tensor | Non
     return packed, scales, zeros
 
 
-def _product(fn_name, X, packed, scales, zeros, group, out):
+def _workspace(ws, need: int, device):
+    """(pointer, bytes) of a workspace: allocated here when `ws` is None and `need` > 0."""
+    if ws is None:
+        if need <= 0:
+            return None, 0
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    if ws.numel() == 0:
+        return None, 0
+    if ws.device.type != "cuda" or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    return ws, ws.numel() * ws.element_size()
+
+
+def _product(fn_name, X, packed, scales, zeros, group, out, workspace=None):
     _need(X, "X", torch.bfloat16, 2)
     _need(packed, "packed", torch.uint8, 2)
     _need(scales, "scales", torch.float32, 2)
@@ -86,8 +99,14 @@ def _product(fn_name, X, packed, scales, zeros, group, out):
     if out is None:
         out = torch.empty((m, n), dtype=torch.float32, device=X.device)
     _need(out, "Y", torch.float32, 2)
-    st = getattr(_lib.load(), fn_name)(X.data_ptr(), m, k, packed.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
-                                       n, group, out.data_ptr(), _stream(X))
+    lib = _lib.load()
+    if fn_name == "aq_w4a16_gemm":
+        ws, nbytes = _workspace(workspace, int(lib.aq_w4a16_gemm_workspace(m, n, k, group)), X.device)
+        st = lib.aq_w4a16_gemm(X.data_ptr(), m, k, packed.data_ptr(), scales.data_ptr(), zeros.data_ptr(), n, group,
+                               out.data_ptr(), _ptr(ws), nbytes, _stream(X))
+    else:
+        st = getattr(lib, fn_name)(X.data_ptr(), m, k, packed.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
+                                   n, group, out.data_ptr(), _stream(X))
     check(st, fn_name)
     return out
 
@@ -97,9 +116,17 @@ def aq_w4a16_gemv(X, packed, scales, zeros, group: int, out=None):
     return _product("aq_w4a16_gemv", X, packed, scales, zeros, group, out)
 
 
-def aq_w4a16_gemm(X, packed, scales, zeros, group: int, out=None):
-    """Y[M, N] fp32 = X[M, K] (bf16, any M) times the dequantized packed weight, transposed (MFMA)."""
-    return _product("aq_w4a16_gemm", X, packed, scales, zeros, group, out)
+def aq_w4a16_gemm_workspace(M: int, N: int, K: int, group: int) -> int:
+    return int(_lib.load().aq_w4a16_gemm_workspace(M, N, K, group))
+
+
+def aq_w4a16_gemm(X, packed, scales, zeros, group: int, out=None, workspace=None):
+    """Y[M, N] fp32 = X[M, K] (bf16, any M) times the dequantized packed weight, transposed (MFMA).
+
+    workspace: None allocates the staging matrix when the size takes the staged path;
+    a uint8 device tensor is used as given (an empty one selects the fused path).
+    """
+    return _product("aq_w4a16_gemm", X, packed, scales, zeros, group, out, workspace)
 
 
 def aq_act_absmean_workspace(T: int, K: int) -> int:
@@ -159,7 +186,11 @@ def aq_awq_search(X_sub, absmean_host, W, group: int, n_grid: int = 20, workspac
     return {"mse": mse, "best": best, "best_scale": best_scale, "packed": packed, "scales": scales, "zeros": zeros}
 
 
-def aq_fp4_gemm(X, codes, block_scales, tensor_scale: float, out=None):
+def aq_fp4_gemm_workspace(M: int, N: int, K: int) -> int:
+    return int(_lib.load().aq_fp4_gemm_workspace(M, N, K))
+
+
+def aq_fp4_gemm(X, codes, block_scales, tensor_scale: float, out=None, workspace=None):
     """Y[M, N] fp32 = tensor_scale * X[M, K] times (e2m1 * e4m3)^T for codes [N, K/2], block_scales [N, K/16]."""
     _need(X, "X", torch.bfloat16, 2)
     _need(codes, "codes", torch.uint8, 2)
@@ -171,7 +202,9 @@ def aq_fp4_gemm(X, codes, block_scales, tensor_scale: float, out=None):
     if out is None:
         out = torch.empty((m, n), dtype=torch.float32, device=X.device)
     _need(out, "Y", torch.float32, 2)
-    st = _lib.load().aq_fp4_gemm(X.data_ptr(), m, k, codes.data_ptr(), block_scales.data_ptr(), float(tensor_scale),
-                                 n, out.data_ptr(), _stream(X))
+    lib = _lib.load()
+    ws, nbytes = _workspace(workspace, int(lib.aq_fp4_gemm_workspace(m, n, k)), X.device)
+    st = lib.aq_fp4_gemm(X.data_ptr(), m, k, codes.data_ptr(), block_scales.data_ptr(), float(tensor_scale),
+                         n, out.data_ptr(), _ptr(ws), nbytes, _stream(X))
     check(st, "aq_fp4_gemm")
     return out

@@ -61,6 +61,11 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
   } while (0)
 
 constexpr int64_t kDimLimit = int64_t(1) << 30;
+// MFMA GEMMs: 32-bit load offsets within a block's rows need K < 2^22.
+constexpr int64_t kGemmKLimit = int64_t(1) << 22;
+// Smallest M for which the staged GEMM path (weights dequantized once into a bf16
+// staging matrix) is used when the caller provides the workspace.
+constexpr int64_t kStagedMinM = 2048;
 
 bool valid_group(int32_t g) { return g == 32 || g == 64 || g == 128; }
 
@@ -134,14 +139,41 @@ aq_status aq_w4a16_gemv(const uint16_t* X, int64_t M, int64_t K, const uint8_t* 
                         "aq_w4a16_gemv");
 }
 
+// Bytes of the bf16 staging matrix the MFMA GEMMs use at this size (0: fused path).
+static size_t staged_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < kStagedMinM || N <= 0 || K <= 0 || N >= kDimLimit || K >= kGemmKLimit) return 0;
+  return (size_t)N * (size_t)K * sizeof(uint16_t);
+}
+
+// The staging matrix when the caller's workspace holds it, else NULL (fused path).
+static aq_status staging(const char* fn, int64_t M, int64_t N, int64_t K, void* workspace, size_t bytes,
+                         uint16_t** out) {
+  *out = nullptr;
+  const size_t need = staged_bytes(M, N, K);
+  if (workspace == nullptr || need == 0 || bytes < need) return AQ_OK;
+  AQ_REQUIRE(aligned(workspace, 256), "%s: workspace must be 256-byte aligned", fn);
+  *out = static_cast<uint16_t*>(workspace);
+  return AQ_OK;
+}
+
+size_t aq_w4a16_gemm_workspace(int64_t M, int64_t N, int64_t K, int32_t group) {
+  if (!valid_group(group) || K % group) return 0;
+  return staged_bytes(M, N, K);
+}
+
 aq_status aq_w4a16_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_t* packed, const float* scales,
-                        const uint8_t* zeros, int64_t N, int32_t group, float* Y, void* stream) {
+                        const uint8_t* zeros, int64_t N, int32_t group, float* Y, void* workspace,
+                        size_t workspace_bytes, void* stream) {
   AQ_REQUIRE(M >= 0 && M < kDimLimit, "aq_w4a16_gemm: M out of range (%lld)", (long long)M);
   aq_status st = check_product("aq_w4a16_gemm", X, M, K, packed, scales, zeros, N, group, Y);
   if (st != AQ_OK) return st;
+  AQ_REQUIRE(K < kGemmKLimit, "aq_w4a16_gemm: K must be below 2^22 (got %lld)", (long long)K);
+  uint16_t* staged = nullptr;
+  st = staging("aq_w4a16_gemm", M, N, K, workspace, workspace_bytes, &staged);
+  if (st != AQ_OK) return st;
   if (fault_injected()) return fail(AQ_ERUNTIME, "aq_w4a16_gemm: injected launch failure");
   if (N == 0 || M == 0) return ok();
-  return runtime_status(aq::launch_w4a16_gemm(X, (int)M, (int)K, packed, scales, zeros, (int)N, group, Y,
+  return runtime_status(aq::launch_w4a16_gemm(X, (int)M, (int)K, packed, scales, zeros, (int)N, group, Y, staged,
                                               (hipStream_t)stream),
                         "aq_w4a16_gemm");
 }
@@ -246,8 +278,14 @@ aq_status aq_awq_search(const uint16_t* X_sub, int64_t T, const float* absmean_h
                         "aq_awq_search: final pack");
 }
 
+size_t aq_fp4_gemm_workspace(int64_t M, int64_t N, int64_t K) {
+  if (M <= 16 || K % 32) return 0;
+  return staged_bytes(M, N, K);
+}
+
 aq_status aq_fp4_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes, const uint8_t* block_scales,
-                      float tensor_scale, int64_t N, float* Y, void* stream) {
+                      float tensor_scale, int64_t N, float* Y, void* workspace, size_t workspace_bytes,
+                      void* stream) {
   AQ_REQUIRE(M >= 0 && M < kDimLimit, "aq_fp4_gemm: M out of range (%lld)", (long long)M);
   AQ_REQUIRE(K > 0 && K < kDimLimit && K % 32 == 0, "aq_fp4_gemm: K must be a positive multiple of 32 (got %lld)",
              (long long)K);
@@ -257,13 +295,20 @@ aq_status aq_fp4_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_t* co
   AQ_PTR(codes, 16, "codes");
   AQ_PTR(block_scales, 2, "block_scales");
   AQ_PTR(Y, 4, "Y");
+  if (M > 16) AQ_REQUIRE(K < kGemmKLimit, "aq_fp4_gemm: K must be below 2^22 for M > 16 (got %lld)", (long long)K);
+  uint16_t* staged = nullptr;
+  if (M > 16) {
+    const aq_status st = staging("aq_fp4_gemm", M, N, K, workspace, workspace_bytes, &staged);
+    if (st != AQ_OK) return st;
+  }
   if (fault_injected()) return fail(AQ_ERUNTIME, "aq_fp4_gemm: injected launch failure");
   if (N == 0 || M == 0) return ok();
   hipError_t e;
   if (M <= 16)
     e = aq::launch_fp4_gemv(X, (int)M, (int)K, codes, block_scales, tensor_scale, (int)N, Y, (hipStream_t)stream);
   else
-    e = aq::launch_fp4_gemm(X, (int)M, (int)K, codes, block_scales, tensor_scale, (int)N, Y, (hipStream_t)stream);
+    e = aq::launch_fp4_gemm(X, (int)M, (int)K, codes, block_scales, tensor_scale, (int)N, Y, staged,
+                            (hipStream_t)stream);
   return runtime_status(e, "aq_fp4_gemm");
 }
 

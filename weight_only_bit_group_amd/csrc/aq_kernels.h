@@ -14,12 +14,14 @@ hipError_t launch_quant_error(const void* W, bool w_bf16, const float* chan_scal
                               int group, hipStream_t stream);
 hipError_t launch_w4a16_gemv(const uint16_t* X, int M, int K, const uint8_t* P, const float* S, const uint8_t* Z,
                              int N, int group, float* Y, hipStream_t stream);
+// `staged`: NULL for the fused kernel, else N * K bf16 of device memory that first
+// receives the dequantized weights (the staged GEMM then loads them like activations)
 hipError_t launch_w4a16_gemm(const uint16_t* X, int M, int K, const uint8_t* P, const float* S, const uint8_t* Z,
-                             int N, int group, float* Y, hipStream_t stream);
+                             int N, int group, float* Y, uint16_t* staged, hipStream_t stream);
 hipError_t launch_fp4_gemv(const uint16_t* X, int M, int K, const uint8_t* codes, const uint8_t* bscale, float ts,
                            int N, float* Y, hipStream_t stream);
 hipError_t launch_fp4_gemm(const uint16_t* X, int M, int K, const uint8_t* codes, const uint8_t* bscale, float ts,
-                           int N, float* Y, hipStream_t stream);
+                           int N, float* Y, uint16_t* staged, hipStream_t stream);
 int sumsq_gemm_blocks(int M, int N);
 hipError_t launch_sumsq_gemm(const uint16_t* X, int M, int K, const uint16_t* E, int N, double* partial,
                              hipStream_t stream);

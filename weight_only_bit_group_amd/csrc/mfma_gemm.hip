@@ -44,8 +44,9 @@
 //     a bf16 LDS tile (two buffers), once per block: each weight row feeds BM
 //     activation rows.
 //   * LDS rows are 128 bytes (64 bf16, 8 units of 16 bytes) with unit u of row r
-//     stored at u ^ (r & 7): the 8 rows read by each 8-lane phase of a
-//     ds_read_b128 hit 8 different bank groups.
+//     stored at u ^ ((r >> 1) & 7): the 16 consecutive rows read by each 16-lane
+//     phase of a ds_read_b128 (the same unit of each) hit all 16 groups of four
+//     banks once (rows r and r + 8 would collide under u ^ (r & 7)).
 //   * Block order is XCD-aware: block b runs on XCD b % 8; each XCD gets a
 //     contiguous range of a grouped tile order (a few row tiles, all column
 //     tiles), so the blocks it runs together share their activation and weight
@@ -66,7 +67,10 @@
 
 namespace aq {
 
-enum BKind { B_INT4 = 0, B_SPLIT = 1, B_FP4 = 2 };
+// B operand kinds: INT4 / FP4 codes dequantized in the kernel; INT4S / FP4S the same
+// weights dequantized beforehand into a bf16 staging matrix (loaded like the SPLIT
+// planes); SPLIT the search's two bf16 planes.
+enum BKind { B_INT4 = 0, B_SPLIT = 1, B_FP4 = 2, B_INT4S = 3, B_FP4S = 4 };
 
 struct GemmArgs {
   const uint16_t* X;
@@ -75,7 +79,7 @@ struct GemmArgs {
   const uint8_t* P;
   const float* S;
   const uint8_t* Z;
-  // SPLIT: the two bf16 planes of E
+  // SPLIT: the two bf16 planes of E; INT4S / FP4S: the staged bf16 weights in B
   const uint16_t* B;
   const uint16_t* B2;
   // FP4
@@ -95,7 +99,7 @@ constexpr int ROW_UNITS = KS / 8;  // 16-byte units per LDS row
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ int swz(int row, int unit) { return row * ROW_UNITS + (unit ^ (row & 7)); }
+__device__ __forceinline__ int swz(int row, int unit) { return row * ROW_UNITS + (unit ^ ((row >> 1) & 7)); }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(const lds_void*)p; }
 
@@ -140,12 +144,18 @@ template <int BK, int G, bool TAIL, int WGM>
 __global__ __launch_bounds__(128 * WGM, 1) void gemm_kernel(GemmArgs a) {
   constexpr int NW = 2 * WGM, NT = 64 * NW;
   constexpr int BM = 64 * WGM;
-  constexpr bool DEQ = BK != B_SPLIT;
-  constexpr int NA = DEQ ? 3 : 2;                   // activation ring
-  constexpr int PD = NA - 1;                        // activation prefetch distance
+  constexpr bool DEQ = BK == B_INT4 || BK == B_FP4;        // codes dequantized here
+  constexpr bool SPLIT = BK == B_SPLIT;
+  constexpr bool STAGED = BK == B_INT4S || BK == B_FP4S;   // bf16 weights from global memory
+  constexpr bool RESCALE = BK == B_INT4 || BK == B_INT4S;  // per-group steps applied to partials
+  constexpr bool TSCALE = BK == B_FP4 || BK == B_FP4S;     // fp32 tensor scale on the output
+  constexpr int PLANES = SPLIT ? 2 : 1;
+  constexpr int NA = SPLIT ? 2 : 3;                 // activation ring
+  constexpr int NB = STAGED ? 3 : 2;                // weight-tile ring
+  constexpr int PD = 2;                             // stage s loads the activations of stage s + 2
   constexpr int CD = 3;                             // code / per-row scalar prefetch distance
   constexpr int A_DMA = BM / 8 / NW;                // activation loads per wave per stage (8 rows each)
-  constexpr int B_DMA = DEQ ? 0 : 2 * (BN / 8) / NW;  // SPLIT plane loads per wave per stage
+  constexpr int B_DMA = PLANES * (BN / 8) / NW * (DEQ ? 0 : 1);  // plane loads per wave per stage
   // code + per-row scalar loads per stage: 4 code loads (1 KB each) and the scalars
   // (INT4: steps and zero points, two 64-row halves per group, one or two groups per
   // stage, the zero-point loads repeated at g = 32 so every wave issues the same
@@ -156,10 +166,10 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_kernel(GemmArgs a) {
   static_assert(!DEQ || JOBS % NW == 0, "scalar loads must split evenly over the waves");
 
   __shared__ __attribute__((aligned(16))) uint16_t As[NA][BM * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][DEQ ? 1 : 2][BN * KS];
-  __shared__ __attribute__((aligned(16))) uint8_t Cs[DEQ ? 3 : 1][BN * KS / 2];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[NB][PLANES][BN * KS];
+  __shared__ __attribute__((aligned(16))) uint8_t Cs[DEQ ? 3 : 1][DEQ ? BN * KS / 2 : 16];
   // per-row scalars: [slot][INT4: 0 = S bits, 1 = zero point | FP4: 0][group in stage or FP4 half][row]
-  __shared__ __attribute__((aligned(16))) uint32_t AX[DEQ ? 4 : 1][2][2][BN];
+  __shared__ __attribute__((aligned(16))) uint32_t AX[(DEQ || RESCALE) ? 4 : 1][DEQ ? 2 : 1][2][BN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -184,135 +194,184 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_kernel(GemmArgs a) {
   const int ngroups = K / G;
 
   // ---- LDS-DMA loads --------------------------------------------------------
-  // Tile rows: load j of wave w covers rows R0 = (j NW + w) 8 .. + 8; lane l lands at
-  // LDS unit (R0 + l / 8, l % 8) and fetches global unit (l % 8) ^ (l / 8), which is
-  // the swizzle since R0 is a multiple of 8.  Offsets are 32-bit (M K, N K < 2^30).
-  // In the 32-wide tail stage the upper four units are folded back onto the lower
-  // four (loaded, never multiplied), so no load runs past a row.
+  // Tile rows: load j of wave w covers the 8 rows from R0 = 8 r8, r8 = j NW + w; lane l
+  // lands at LDS unit (R0 + l / 8, l % 8), which holds logical unit
+  // (l % 8) ^ (((R0 + l / 8) >> 1) & 7) = (l % 8) ^ ((4 r8 + l / 16) & 7): the global
+  // unit it fetches.  Load addresses are a 64-bit base at the block's first row (and
+  // the stage's first column) plus a 32-bit lane offset within the block's rows, which
+  // stays below 2^32 for K < 2^22.  In the 32-wide tail stage
+  // the upper four units are folded back onto the lower four (loaded, never
+  // multiplied), so no load runs past a row.
   const int lrow8 = lane >> 3;
-  const int gunit = (lane & 7) ^ lrow8;
-  const uint32_t tail_fold = (TAIL && gunit >= 4) ? 64u : 0u;
+  auto gunit_of = [&](int r8) { return (lane & 7) ^ ((4 * r8 + (lane >> 4)) & 7); };
+  auto fold_of = [&](int r8) -> uint32_t { return (TAIL && gunit_of(r8) >= 4) ? 64u : 0u; };
   uint32_t aoff[A_DMA];
 #pragma unroll
   for (int j = 0; j < A_DMA; ++j) {
-    const int row = (j * NW + wid) * 8 + lrow8;
-    aoff[j] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)K * 2u + (uint32_t)gunit * 16u;
+    const int r8 = j * NW + wid;
+    aoff[j] = (uint32_t)(min(m0 + 8 * r8 + lrow8, M - 1) - m0) * (uint32_t)K * 2u + (uint32_t)gunit_of(r8) * 16u;
   }
   auto issue_a = [&](int s, int slot) {
-    const char* base = reinterpret_cast<const char*>(a.X) + (size_t)s * (KS * 2);
-    const uint32_t fold = (TAIL && s == nfull) ? tail_fold : 0u;
+    const char* base = reinterpret_cast<const char*>(a.X + (size_t)m0 * K) + (size_t)s * (KS * 2);
+    const bool tail = TAIL && s == nfull;
 #pragma unroll
-    for (int j = 0; j < A_DMA; ++j) dma16(base, aoff[j] - fold, lds_addr(&As[slot][(j * NW + wid) * 8 * KS]));
+    for (int j = 0; j < A_DMA; ++j) {
+      const int r8 = j * NW + wid;
+      dma16(base, aoff[j] - (tail ? fold_of(r8) : 0u), lds_addr(&As[slot][8 * r8 * KS]));
+    }
   };
   auto issue_planes = [&](int s, int slot) {
     if constexpr (!DEQ) {
-      const uint32_t fold = (TAIL && s == nfull) ? tail_fold : 0u;
+      const bool tail = TAIL && s == nfull;
 #pragma unroll
-      for (int pl = 0; pl < 2; ++pl) {
-        const char* base = reinterpret_cast<const char*>(pl ? a.B2 : a.B) + (size_t)s * (KS * 2);
+      for (int pl = 0; pl < PLANES; ++pl) {
+        const char* base = reinterpret_cast<const char*>((pl ? a.B2 : a.B) + (size_t)n0 * K) + (size_t)s * (KS * 2);
 #pragma unroll
         for (int j = 0; j < BN / 8 / NW; ++j) {
-          const int r0 = (j * NW + wid) * 8;
-          const uint32_t off = (uint32_t)min(n0 + r0 + lrow8, N - 1) * (uint32_t)K * 2u + (uint32_t)gunit * 16u;
-          dma16(base, off - fold, lds_addr(&Bs[slot][pl][r0 * KS]));
+          const int r8 = j * NW + wid;
+          const uint32_t off =
+              (uint32_t)(min(n0 + 8 * r8 + lrow8, N - 1) - n0) * (uint32_t)K * 2u + (uint32_t)gunit_of(r8) * 16u;
+          dma16(base, off - (tail ? fold_of(r8) : 0u), lds_addr(&Bs[slot][pl][8 * r8 * KS]));
         }
       }
     }
   };
   // codes (32 bytes per row and stage, two 16-byte halves per lane pair) and the
-  // per-row scalars of stage s
-  auto issue_codes = [&](int s, int cslot, int xslot) {
+  // per-row scalars of stage s: job i (0 <= i < JPW) of this wave
+  auto issue_job = [&](int s, int cslot, int xslot, int i) {
     if constexpr (DEQ) {
       const bool tail = TAIL && s == nfull;
+      const int job = wid * JPW + i;   // wave-uniform
+      if (job < 4) {
+        const int r = 32 * job + (lane >> 1);
+        const uint32_t n = (uint32_t)(min(n0 + r, N - 1) - n0);
+        const uint32_t half = tail ? 0u : (uint32_t)(lane & 1) * 16u;
+        const uint8_t* src = ((BK == B_INT4) ? a.P : a.codes) + (size_t)n0 * (K >> 1) + (size_t)s * (KS / 2);
+        dma16(src, n * (uint32_t)(K >> 1) + half, lds_addr(&Cs[cslot][1024 * job]));
+      } else if constexpr (BK == B_INT4) {
+        int x = job - 4;
+        if (x >= 8) x -= 4;                                  // repeated zero-point loads (g = 32)
+        const int is_z = (G == 32) ? (x >= 4) : (x >= 2);
+        const int gi = (G == 32) ? ((x >> 1) & 1) : 0;
+        const int rh = 64 * (x & 1);
+        const uint32_t n = (uint32_t)(min(n0 + rh + lane, N - 1) - n0);
+        const uint32_t g = (uint32_t)min((s * KS + 32 * gi) / G, ngroups - 1);
+        const uint32_t idx = n * (uint32_t)ngroups + g;
+        if (is_z) dma1(a.Z + (size_t)n0 * ngroups, idx, lds_addr(&AX[xslot][1][gi][rh]));
+        else dma4(a.S + (size_t)n0 * ngroups, idx * 4u, lds_addr(&AX[xslot][0][gi][rh]));
+      } else {
+        const int x = job - 4;
+        const int h = x >> 1, rh = 64 * (x & 1);
+        const uint32_t n = (uint32_t)(min(n0 + rh + lane, N - 1) - n0);
+        const uint32_t byte = (uint32_t)(s * 4 + 2 * (tail ? 0 : h));   // the tail stage has 2 block scales
+        dma2(a.bscale + (size_t)n0 * (K >> 4), n * (uint32_t)(K >> 4) + byte, lds_addr(&AX[xslot][0][h][rh]));
+      }
+    }
+  };
+  auto issue_codes = [&](int s, int cslot, int xslot) {
 #pragma unroll
-      for (int i = 0; i < JPW; ++i) {
-        const int job = wid * JPW + i;   // wave-uniform
-        if (job < 4) {
-          const int r = 32 * job + (lane >> 1);
-          const uint32_t n = (uint32_t)min(n0 + r, N - 1);
-          const uint32_t half = tail ? 0u : (uint32_t)(lane & 1) * 16u;
-          const uint8_t* src = (BK == B_INT4) ? a.P : a.codes;
-          dma16(src + (size_t)s * (KS / 2), n * (uint32_t)(K >> 1) + half, lds_addr(&Cs[cslot][1024 * job]));
-        } else if constexpr (BK == B_INT4) {
-          int x = job - 4;
-          if (x >= 8) x -= 4;                                  // repeated zero-point loads (g = 32)
-          const int is_z = (G == 32) ? (x >= 4) : (x >= 2);
-          const int gi = (G == 32) ? ((x >> 1) & 1) : 0;
-          const int rh = 64 * (x & 1);
-          const uint32_t n = (uint32_t)min(n0 + rh + lane, N - 1);
-          const uint32_t g = (uint32_t)min((s * KS + 32 * gi) / G, ngroups - 1);
-          const uint32_t idx = n * (uint32_t)ngroups + g;
-          if (is_z) dma1(a.Z, idx, lds_addr(&AX[xslot][1][gi][rh]));
-          else dma4(a.S, idx * 4u, lds_addr(&AX[xslot][0][gi][rh]));
-        } else {
-          const int x = job - 4;
-          const int h = x >> 1, rh = 64 * (x & 1);
-          const uint32_t n = (uint32_t)min(n0 + rh + lane, N - 1);
-          const uint32_t byte = (uint32_t)(s * 4 + 2 * (tail ? 0 : h));   // the tail stage has 2 block scales
-          dma2(a.bscale, n * (uint32_t)(K >> 4) + byte, lds_addr(&AX[xslot][0][h][rh]));
-        }
+    for (int i = 0; i < JPW; ++i) issue_job(s, cslot, xslot, i);
+  };
+  // one activation load (j < A_DMA) / one SPLIT plane load (q < B_DMA) of stage s
+  auto issue_a_one = [&](int s, int slot, int j) {
+    const char* base = reinterpret_cast<const char*>(a.X + (size_t)m0 * K) + (size_t)s * (KS * 2);
+    const int r8 = j * NW + wid;
+    dma16(base, aoff[j] - ((TAIL && s == nfull) ? fold_of(r8) : 0u), lds_addr(&As[slot][8 * r8 * KS]));
+  };
+  auto issue_plane_one = [&](int s, int slot, int q) {
+    if constexpr (!DEQ) {
+      constexpr int PER = BN / 8 / NW;   // loads per plane and wave
+      const int pl = q / PER, r8 = (q % PER) * NW + wid;
+      const char* base = reinterpret_cast<const char*>((pl ? a.B2 : a.B) + (size_t)n0 * K) + (size_t)s * (KS * 2);
+      const uint32_t off =
+          (uint32_t)(min(n0 + 8 * r8 + lrow8, N - 1) - n0) * (uint32_t)K * 2u + (uint32_t)gunit_of(r8) * 16u;
+      dma16(base, off - ((TAIL && s == nfull) ? fold_of(r8) : 0u), lds_addr(&Bs[slot][pl][8 * r8 * KS]));
+    }
+  };
+
+  // staged INT4: the group steps of stage s (one dword per row, 64 rows per load, one
+  // or two groups per stage), issued by the first two or four waves
+  auto issue_steps = [&](int s, int slot) {
+    if constexpr (BK == B_INT4S) {
+      constexpr int NL = (G == 32) ? 4 : 2;
+      if (wid < NL) {
+        const int gi = wid >> 1, rh = 64 * (wid & 1);
+        const uint32_t n = (uint32_t)(min(n0 + rh + lane, N - 1) - n0);
+        const uint32_t g = (uint32_t)min((s * KS + 32 * gi) / G, ngroups - 1);
+        dma4(a.S + (size_t)n0 * ngroups, (n * (uint32_t)ngroups + g) * 4u, lds_addr(&AX[slot][0][gi][rh]));
       }
     }
   };
 
   // ---- dequantization: codes of one stage -> bf16 weight tile ----------------
+  // Thread t converts KPT codes of weight row t / TPR (WPT words of 8 codes, each one
+  // 16-byte LDS unit of bf16 values), in four parts so the work can be spread over a
+  // stage.  dq_load reads the codes and per-row scalars; dq_part(p) converts pairs
+  // [p WPT, (p + 1) WPT) and stores each unit once its four pairs are done.
   constexpr int TPR = NT / BN;          // threads per weight row
   constexpr int KPT = KS / TPR;         // k per thread (16 or 32)
   constexpr int WPT = KPT / 8;          // 8-code words (= LDS units) per thread
   const int d_row = tid / TPR, d_part = tid % TPR;
-  // `tail`: stage s is the 32-wide tail (only its first 32 k are dequantized)
-  auto dequant = [&](int cslot, int xslot, int bbuf, bool tail) {
+  uint32_t dq_w[WPT], dq_lo[WPT], dq_hi[WPT], dq_o[WPT][4];
+  float dq_z = 0.0f;
+  uint32_t dq_sc2[2] = {0u, 0u};
+  auto dq_load = [&](int cslot, int xslot) {
     if constexpr (DEQ) {
-      if (tail && d_part * KPT >= 32) return;
-      uint32_t w[WPT];
       const uint8_t* cp = &Cs[cslot][d_row * 32 + d_part * (KPT / 2)];
       if constexpr (WPT == 2) {
         const uint2 v = *reinterpret_cast<const uint2*>(cp);
-        w[0] = v.x; w[1] = v.y;
+        dq_w[0] = v.x; dq_w[1] = v.y;
       } else {
         const u32x4 v = *reinterpret_cast<const u32x4*>(cp);
-        w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+        dq_w[0] = v[0]; dq_w[1] = v[1]; dq_w[2] = v[2]; dq_w[3] = v[3];
       }
-      u32x4* dst = reinterpret_cast<u32x4*>(&Bs[bbuf][0][0]);
       if constexpr (BK == B_INT4) {
         const int gi = (G == 32) ? (d_part * KPT) / 32 : 0;
-        const float zf = (float)AX[xslot][1][gi][d_row];
-#pragma unroll
-        for (int u = 0; u < WPT; ++u) {
-          uint32_t lo = w[u] & 0x0F0F0F0Fu, hi = (w[u] >> 4) & 0x0F0F0F0Fu;
-          // opaque to the optimizer, so each code converts with one v_cvt_f32_ubyteN
-          asm("" : "+v"(lo), "+v"(hi));
-          uint32_t o[4];
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const float ql = (float)((lo >> (8 * b)) & 0xFFu), qh = (float)((hi >> (8 * b)) & 0xFFu);
-            o[b] = pack_bf16_exact(ql - zf, qh - zf);
-          }
-          dst[swz(d_row, d_part * WPT + u)] = u32x4{o[0], o[1], o[2], o[3]};
-        }
+        dq_z = (float)AX[xslot][1][gi][d_row];
       } else {
-#pragma unroll
-        for (int u = 0; u < WPT; ++u) {
-          // 16-element block of word u: (d_part KPT + 8 u) / 16 within the stage
-          const int blk = (d_part * KPT + 8 * u) >> 4;
-          const uint32_t two = AX[xslot][0][blk >> 1][d_row];
-          const float sc = (blk & 1) ? __builtin_amdgcn_cvt_f32_fp8((int)two, 1) : __builtin_amdgcn_cvt_f32_fp8((int)two, 0);
-          uint32_t o[4];
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            uint32_t e2;
-            switch (b) {
-              case 0: e2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[u], 1.0f, 0)); break;
-              case 1: e2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[u], 1.0f, 1)); break;
-              case 2: e2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[u], 1.0f, 2)); break;
-              default: e2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[u], 1.0f, 3)); break;
-            }
-            o[b] = pack_bf16_exact(bf16_lo(e2) * sc, bf16_hi(e2) * sc);
-          }
-          dst[swz(d_row, d_part * WPT + u)] = u32x4{o[0], o[1], o[2], o[3]};
-        }
+        // the 16-element blocks of this thread's codes: (d_part KPT + 8 u) / 16
+        dq_sc2[0] = AX[xslot][0][0][d_row];
+        dq_sc2[1] = AX[xslot][0][1][d_row];
       }
     }
+  };
+  auto dq_part = [&](int p, int bbuf, bool tail) {
+    if constexpr (DEQ) {
+      if (tail && d_part * KPT >= 32) return;   // the tail stage has 32 k
+      u32x4* dst = reinterpret_cast<u32x4*>(&Bs[bbuf][0][0]);
+#pragma unroll
+      for (int q = p * WPT; q < (p + 1) * WPT; ++q) {
+        const int u = q >> 2, b = q & 3;
+        if constexpr (BK == B_INT4) {
+          if (b == 0) {
+            dq_lo[u] = dq_w[u] & 0x0F0F0F0Fu;
+            dq_hi[u] = (dq_w[u] >> 4) & 0x0F0F0F0Fu;
+            // opaque to the optimizer, so each code converts with one v_cvt_f32_ubyteN
+            asm("" : "+v"(dq_lo[u]), "+v"(dq_hi[u]));
+          }
+          const float ql = (float)((dq_lo[u] >> (8 * b)) & 0xFFu), qh = (float)((dq_hi[u] >> (8 * b)) & 0xFFu);
+          dq_o[u][b] = pack_bf16_exact(ql - dq_z, qh - dq_z);
+        } else {
+          const int blk = (d_part * KPT + 8 * u) >> 4;   // block of word u within the stage
+          const uint32_t two = dq_sc2[blk >> 1];
+          const float sc = (blk & 1) ? __builtin_amdgcn_cvt_f32_fp8((int)two, 1) : __builtin_amdgcn_cvt_f32_fp8((int)two, 0);
+          uint32_t e2;
+          switch (b) {
+            case 0: e2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dq_w[u], 1.0f, 0)); break;
+            case 1: e2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dq_w[u], 1.0f, 1)); break;
+            case 2: e2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dq_w[u], 1.0f, 2)); break;
+            default: e2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dq_w[u], 1.0f, 3)); break;
+          }
+          dq_o[u][b] = pack_bf16_exact(bf16_lo(e2) * sc, bf16_hi(e2) * sc);
+        }
+        if (b == 3) dst[swz(d_row, d_part * WPT + u)] = u32x4{dq_o[u][0], dq_o[u][1], dq_o[u][2], dq_o[u][3]};
+      }
+    }
+  };
+  auto dequant = [&](int cslot, int xslot, int bbuf, bool tail) {
+    dq_load(cslot, xslot);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) dq_part(p, bbuf, tail);
   };
 
   // ---- accumulators: 32x32 output blocks (mi, ni) of the 64 x 64 wave tile ----
@@ -328,96 +387,191 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_kernel(GemmArgs a) {
   const int lh = lane >> 5;           // k half of a 16-wide MFMA step
   const u32x4* Av = reinterpret_cast<const u32x4*>(&As[0][0]);
   const u32x4* Bv = reinterpret_cast<const u32x4*>(&Bs[0][0][0]);
-  constexpr int A_BUF = BM * KS / 8, B_BUF = (DEQ ? 1 : 2) * BN * KS / 8, B_PLANE = BN * KS / 8;  // 16-byte units
+  constexpr int A_BUF = BM * KS / 8, B_BUF = PLANES * BN * KS / 8, B_PLANE = BN * KS / 8;  // 16-byte units
+  static_assert(A_DMA == 4 && JPW <= 4 && B_DMA % 2 == 0, "loads are spread over the parts of a stage");
 
-  // NKS: 16-wide MFMA steps of stage s (4, or 2 in the tail); NXT: the same for the
-  // stage whose weights are dequantized here (0 for the last stage)
-  auto run_stage = [&](int s, auto nk_tag, auto nx_tag) {
-    constexpr int NKS = decltype(nk_tag)::value;
-    constexpr int NXT = decltype(nx_tag)::value;
-    const int abuf = s % NA;
-    const int bbuf = s & 1;
-    const int xs = s & 3;
-    // 1. prefetch: codes / scalars of stage s + 3, activations of stage s + 2 (SPLIT:
-    //    activations and planes of stage s + 1)
-    const bool more_c = DEQ && s + CD < nstage;
-    const bool more_a = s + PD < nstage;
-    if (more_c) issue_codes(s + CD, (s + CD) % 3, (s + CD) & 3);
-    if (more_a) {
-      issue_a(s + PD, (s + PD) % NA);
-      issue_planes(s + PD, (s + PD) & 1);
-    }
-    // 2. fragments of this stage
-    bf16x8 af[2][NKS], bf[2][NKS], bf2[2][NKS];
+  // INT4 group partials: the stage's (group, block) items run in four parts of NG
+  // items; each part also rescales the previous part's items, and the last part's
+  // items are carried into the next stage: carried slot c holds the partial of block
+  // 4 - NGMAX + c (zero partial and step when a stage carries fewer).
+  constexpr int NGMAX = (RESCALE && G == 32) ? 2 : 1;
+  f32x16 tcar[NGMAX];
+  float scar[NGMAX];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+  for (int g = 0; g < NGMAX; ++g) {
+    scar[g] = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) tcar[g][v] = 0.0f;
+  }
+
+  // ---- one stage ----------------------------------------------------------------
+  // The workgroup barrier sits in the middle of a stage: stage s reads all its
+  // fragments, runs blocks (0,0) and (0,1), waits for its loads and passes barrier
+  // M_s, then runs blocks (1,0) and (1,1) from registers.  M_s publishes stage s + 1
+  // (its activations landed, its weights dequantized), so the next stage's reads are
+  // issued right behind the MFMAs of blocks (1,*) and there is MFMA work queued on
+  // both sides of every barrier.
+  //   Buffers: stage s's tiles are read only before M_s, so after M_s they take stage
+  //   s + 2's weights (dequantized during parts 2, 3 of stage s and parts 0, 1 of
+  //   stage s + 1) and, for SPLIT (two-deep rings), its planes and activations.
+  //   INT4 / FP4 activations use a three-deep ring: stage s + 2's are loaded during
+  //   all of stage s.  Codes and per-row scalars of stage s + 3 load at its start.
+  //   M_s waits for every load except those issued in stage s before it.
+  // Tags: NKS = 16-wide MFMA steps of stage s (4, or 2 in the tail); NX1 / NX2 = the
+  // same for stages s + 1 / s + 2 (0: none), whose dequantization parts 2, 3 / 0, 1
+  // run here; MA: load activations (INT4, FP4: stage s + 2) or activations and planes
+  // (SPLIT: stage s + 2, after M_s); MC: load codes and scalars of stage s + 3.
+  auto run_stage = [&](int s, auto nk_tag, auto nx1_tag, auto nx2_tag, auto mc_tag, auto ma_tag) {
+    constexpr int NKS = decltype(nk_tag)::value;
+    constexpr int NX1 = decltype(nx1_tag)::value;
+    constexpr int NX2 = decltype(nx2_tag)::value;
+    constexpr bool MC = DEQ && decltype(mc_tag)::value;
+    constexpr bool MA = decltype(ma_tag)::value;
+    constexpr int NG = (RESCALE && G == 32) ? NKS / 2 : 1;   // group partials per block (INT4)
+    constexpr int KPG = NKS / NG;
+    const int abuf = s % NA;
+    const int bbuf = s % NB;
+    const int xs = s & 3;
+    if constexpr (MC) issue_codes(s + CD, (s + CD) % 3, (s + CD) & 3);
+    __builtin_amdgcn_sched_barrier(0);
+    // LDS reads: this stage's fragments (m-block 1's during part 0) and group steps
+    bf16x8 af[2][NKS], bf[2][NKS], bf2[2][NKS];
+    auto read_a = [&](int mi) {
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
         af[mi][ks] = __builtin_bit_cast(bf16x8, Av[abuf * A_BUF + swz(wm * 64 + 32 * mi + l32, 2 * ks + lh)]);
+    };
+    read_a(0);
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const int row = wn * 64 + 32 * ni + l32;
         bf[ni][ks] = __builtin_bit_cast(bf16x8, Bv[bbuf * B_BUF + swz(row, 2 * ks + lh)]);
-        if constexpr (!DEQ) bf2[ni][ks] = __builtin_bit_cast(bf16x8, Bv[bbuf * B_BUF + B_PLANE + swz(row, 2 * ks + lh)]);
+        if constexpr (SPLIT) bf2[ni][ks] = __builtin_bit_cast(bf16x8, Bv[bbuf * B_BUF + B_PLANE + swz(row, 2 * ks + lh)]);
       }
-    // 3. MFMAs
-    if constexpr (BK == B_INT4) {
-      constexpr int NG = (G == 32) ? NKS / 2 : 1;   // group partials per block in this stage
-      constexpr int KPG = NKS / NG;
-      float sc[2][NG];
+    float sc[2][2];
+    if constexpr (RESCALE) {
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) sc[ni][gi] = __builtin_bit_cast(float, AX[xs][0][gi][wn * 64 + 32 * ni + l32]);
-      // (group, block) pairs in order; each block's rescale runs one pair behind its MFMAs
-      f32x16 tprev;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 tprev[NGMAX];   // the previous part's partials and steps
+    float sprev[NGMAX];
 #pragma unroll
-      for (int it = 0; it < 4 * NG; ++it) {
-        const int gi = it >> 2, mi = (it >> 1) & 1, ni = it & 1;
-        f32x16 tp;
+    for (int part = 0; part < 4; ++part) {
+      if constexpr (RESCALE) {
+        // this part: items part NG .. part NG + NG - 1, item it = (group it / 4, block it % 4)
+        f32x16 tp[NGMAX];
+        float st[NGMAX];
 #pragma unroll
-        for (int k = 0; k < KPG; ++k) {
-          const int ks = gi * KPG + k;
-          const f32x16 zero = {};
-          tp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi][ks], bf[ni][ks], k == 0 ? zero : tp, 0, 0, 0);
+        for (int x = 0; x < NG; ++x) {
+          const int it = part * NG + x;
+          const int gi = it >> 2, blk = it & 3, mi = blk >> 1, ni = blk & 1;
+#pragma unroll
+          for (int k = 0; k < KPG; ++k) {
+            const int ks = gi * KPG + k;
+            const f32x16 zero = {};
+            tp[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi][ks], bf[ni][ks], k == 0 ? zero : tp[x], 0, 0, 0);
+          }
+          st[x] = sc[ni][gi];
         }
-        if (it > 0) {
-          const int pg = (it - 1) >> 2, pm = ((it - 1) >> 1) & 1, pn = (it - 1) & 1;
+        // rescale the previous part's items (part 0: the carried slots)
+        if (part == 0) {
 #pragma unroll
-          for (int v = 0; v < 16; ++v) acc[pm][pn][v] = __builtin_fmaf(sc[pn][pg], tprev[v], acc[pm][pn][v]);
+          for (int c = 0; c < NGMAX; ++c) {
+            const int blk = 4 - NGMAX + c, qm = blk >> 1, qn = blk & 1;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[qm][qn][v] = __builtin_fmaf(scar[c], tcar[c][v], acc[qm][qn][v]);
+          }
+        } else {
+#pragma unroll
+          for (int x = 0; x < NG; ++x) {
+            const int blk = ((part - 1) * NG + x) & 3, qm = blk >> 1, qn = blk & 1;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[qm][qn][v] = __builtin_fmaf(sprev[x], tprev[x][v], acc[qm][qn][v]);
+          }
         }
-        tprev = tp;
-      }
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[1][1][v] = __builtin_fmaf(sc[1][NG - 1], tprev[v], acc[1][1][v]);
-    } else {
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int mi = b >> 1, ni = b & 1;
+        for (int x = 0; x < NG; ++x) {
+          tprev[x] = tp[x];
+          sprev[x] = st[x];
+        }
+      } else {
+        const int mi = part >> 1, ni = part & 1;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi][ks], bf[ni][ks], acc[mi][ni], 0, 0, 0);
-          if constexpr (!DEQ)
+          if constexpr (SPLIT)
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi][ks], bf2[ni][ks], acc[mi][ni], 0, 0, 0);
         }
       }
+      // m-block 1 is first used by block 2 (item 2 of group 0): read in the part before
+      if (part == 2 / NG - 1) read_a(1);
+      if constexpr (DEQ) {
+        // dequantization: parts 0, 1 finish stage s + 1 (into the other weight buffer);
+        // parts 2, 3 start stage s + 2 (into this stage's buffer, free after M_s)
+        if (part < 2) {
+          if constexpr (NX1 > 0) dq_part(part + 2, bbuf ^ 1, NX1 == 2);
+        } else {
+          if constexpr (NX2 > 0) {
+            if (part == 2) dq_load((s + 2) % 3, (s + 2) & 3);
+            dq_part(part - 2, bbuf, NX2 == 2);
+          }
+        }
+      }
+      if constexpr (DEQ && MA) {
+        issue_a_one(s + PD, (s + PD) % NA, part);
+      } else if constexpr (STAGED && MA) {
+        // stage s + 2's activations over all four parts, its weights in parts 0, 1,
+        // its group steps in part 2 (after M_s, so they are not counted there)
+        issue_a_one(s + 2, (s + 2) % 3, part);
+        if (part < 2) {
+#pragma unroll
+          for (int q = part * (B_DMA / 2); q < (part + 1) * (B_DMA / 2); ++q) issue_plane_one(s + 2, (s + 2) % 3, q);
+        }
+        if (part == 2) issue_steps(s + 2, (s + 2) & 3);
+      } else if constexpr (MA) {
+        // SPLIT: stage s + 2's activations and planes go into this stage's buffers,
+        // after M_s
+        if (part >= 2) {
+#pragma unroll
+          for (int j = (part - 2) * (A_DMA / 2); j < (part - 1) * (A_DMA / 2); ++j) issue_a_one(s + 2, bbuf, j);
+#pragma unroll
+          for (int q = (part - 2) * (B_DMA / 2); q < (part - 1) * (B_DMA / 2); ++q) issue_plane_one(s + 2, bbuf, q);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (part == 1) {
+        // M_s: only the loads issued in this stage so far may still be in flight (loads
+        // complete in order); this wave's LDS writes are done
+        constexpr int KEEP = DEQ ? (MC ? JPW : 0) + (MA ? 2 : 0) : STAGED ? (MA ? 2 + B_DMA : 0) : 0;
+        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(KEEP));
+        stage_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    // 4. weights of the next stage (its codes were published one barrier ago)
-    if constexpr (DEQ && NXT > 0) dequant((s + 1) % 3, (s + 1) & 3, bbuf ^ 1, NXT == 2);
-    // 5. wait until only this stage's loads are outstanding (loads complete in order),
-    //    and for this wave's LDS writes; then publish
-    //    (SPLIT prefetches one stage ahead: everything issued so far is needed next)
-    if (DEQ && more_c) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(JPW + A_DMA));
-    else if (DEQ && more_a) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(A_DMA));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
-    stage_barrier();
+    if constexpr (RESCALE) {
+      // carry the last part's items (blocks 4 - NG .. 3) into slots NGMAX - NG ..
+#pragma unroll
+      for (int c = 0; c < NGMAX; ++c) {
+        const int x = c - (NGMAX - NG);
+        if (x >= 0) {
+          tcar[c] = tprev[x];
+          scar[c] = sprev[x];
+        } else {
+          scar[c] = 0.0f;
+        }
+      }
+    }
   };
 
-  // ---- prologue --------------------------------------------------------------
+  // ---- prologue ----------------------------------------------------------------
+  // Loads of stages 0 and 1 (and the codes of stage 2), stage 0's weights and the
+  // first half of stage 1's dequantized; SPLIT: stages 0 and 1.
   if constexpr (DEQ) {
-    // P0 = stage 0 (codes, activations), P1 = stage 1 (codes, activations), P2 = codes of stage 2
     issue_codes(0, 0, 0);
     issue_a(0, 0);
     if (nstage > 1) {
@@ -425,34 +579,70 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_kernel(GemmArgs a) {
       issue_a(1, 1);
     }
     if (nstage > 2) issue_codes(2, 2, 2);
-    if (nstage > 2) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(2 * JPW + A_DMA));
-    else if (nstage > 1) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(JPW + A_DMA));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
+    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
     stage_barrier();
     dequant(0, 0, 0, TAIL && nfull == 0);
-    if (nstage > 2) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(JPW));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
-    stage_barrier();
+    if (nstage > 1) {
+      dq_load(1, 1);
+      dq_part(0, 1, TAIL && nfull == 1);
+      dq_part(1, 1, TAIL && nfull == 1);
+    }
   } else {
     issue_a(0, 0);
     issue_planes(0, 0);
-    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
-    stage_barrier();
+    issue_steps(0, 0);
+    if (nstage > 1) {
+      issue_a(1, 1);
+      issue_planes(1, 1);
+      issue_steps(1, 1);
+    }
   }
+  __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
+  stage_barrier();
+
   using IC4 = std::integral_constant<int, 4>;
   using IC2 = std::integral_constant<int, 2>;
   using IC0 = std::integral_constant<int, 0>;
-  for (int s = 0; s + 1 < nfull; ++s) run_stage(s, IC4{}, IC4{});
-  if constexpr (TAIL) {
-    if (nfull > 0) run_stage(nfull - 1, IC4{}, IC2{});
-    run_stage(nfull, IC2{}, IC0{});
-  } else {
-    run_stage(nfull - 1, IC4{}, IC0{});
+  using YES = std::true_type;
+  using NO = std::false_type;
+  // steady state: full stages whose next two stages are full and that load
+  // everything; the last three stages are peeled (their loads and dequantization
+  // depend on the position)
+  const int steady = max(0, nstage - 3);
+  for (int s = 0; s < steady; ++s) run_stage(s, IC4{}, IC4{}, IC4{}, YES{}, YES{});
+  auto kind = [&](int t) { return t >= nstage ? 0 : (TAIL && t == nfull) ? 2 : 4; };
+  for (int s = steady; s < nstage; ++s) {
+    const int k0 = kind(s), k1 = kind(s + 1), k2 = kind(s + 2);
+    const bool ma = s + 2 < nstage;   // codes are never loaded here (s + 3 >= nstage)
+    if (k0 == 2) {
+      run_stage(s, IC2{}, IC0{}, IC0{}, NO{}, NO{});
+    } else if (k1 == 0) {
+      run_stage(s, IC4{}, IC0{}, IC0{}, NO{}, NO{});
+    } else if (k1 == 2) {
+      run_stage(s, IC4{}, IC2{}, IC0{}, NO{}, NO{});
+    } else if (k2 == 0) {
+      run_stage(s, IC4{}, IC4{}, IC0{}, NO{}, NO{});
+    } else if (k2 == 2) {
+      if (ma) run_stage(s, IC4{}, IC4{}, IC2{}, NO{}, YES{});
+      else run_stage(s, IC4{}, IC4{}, IC2{}, NO{}, NO{});
+    } else {
+      if (ma) run_stage(s, IC4{}, IC4{}, IC4{}, NO{}, YES{});
+      else run_stage(s, IC4{}, IC4{}, IC4{}, NO{}, NO{});
+    }
+  }
+  if constexpr (RESCALE) {
+    // the last stage's carried partials
+#pragma unroll
+    for (int c = 0; c < NGMAX; ++c) {
+      const int blk = 4 - NGMAX + c, qm = blk >> 1, qn = blk & 1;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[qm][qn][v] = __builtin_fmaf(scar[c], tcar[c][v], acc[qm][qn][v]);
+    }
   }
 
   // ---- epilogue --------------------------------------------------------------
   // result i of block (mi, ni): row 8 (i / 4) + 4 lh + (i % 4), column l32
-  if constexpr (BK == B_SPLIT) {
+  if constexpr (SPLIT) {
     double ss = 0.0;
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
@@ -486,11 +676,66 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int m = m0 + wm * 64 + 32 * mi + 8 * (v >> 2) + 4 * lh + (v & 3);
-          const float y = (BK == B_FP4) ? acc[mi][ni][v] * a.ts : acc[mi][ni][v];
+          const float y = TSCALE ? acc[mi][ni][v] * a.ts : acc[mi][ni][v];
           if (full || (m < M && n < N)) __builtin_nontemporal_store(y, &a.Y[(int64_t)m * N + n]);
         }
       }
   }
+}
+
+// Staged weights: the codes of one weight matrix dequantized once into a bf16 matrix
+// W16[N, K] (K contiguous) that the INT4S / FP4S GEMMs load like activations.  INT4:
+// the exact integer q - z (group step applied in the GEMM); FP4: the exact product
+// e2m1(code) * e4m3(block scale).  One thread converts 16 codes (8 bytes in, 32 out).
+template <bool FP4>
+__global__ __launch_bounds__(256) void stage_weights_kernel(const uint8_t* __restrict__ codes,
+                                                            const uint8_t* __restrict__ aux, int N, int K, int G,
+                                                            uint16_t* __restrict__ W16) {
+  const int cpr = K >> 4;                                        // 16-code chunks per row
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)N * cpr) return;
+  const int n = (int)(idx / cpr), c = (int)(idx - (int64_t)n * cpr);
+  const uint2 wv = *reinterpret_cast<const uint2*>(codes + (int64_t)n * (K >> 1) + c * 8);
+  const uint32_t w[2] = {wv.x, wv.y};
+  uint32_t o[8];
+  if constexpr (!FP4) {
+    const float z = (float)aux[(int64_t)n * (K / G) + (c * 16) / G];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      uint32_t lo = w[u] & 0x0F0F0F0Fu, hi = (w[u] >> 4) & 0x0F0F0F0Fu;
+      asm("" : "+v"(lo), "+v"(hi));
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        o[4 * u + b] = pack_bf16_exact((float)((lo >> (8 * b)) & 0xFFu) - z, (float)((hi >> (8 * b)) & 0xFFu) - z);
+    }
+  } else {
+    const float sc = __builtin_amdgcn_cvt_f32_fp8((int)aux[(int64_t)n * (K >> 4) + c], 0);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        uint32_t e2;
+        switch (b) {
+          case 0: e2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[u], 1.0f, 0)); break;
+          case 1: e2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[u], 1.0f, 1)); break;
+          case 2: e2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[u], 1.0f, 2)); break;
+          default: e2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[u], 1.0f, 3)); break;
+        }
+        o[4 * u + b] = pack_bf16_exact(bf16_lo(e2) * sc, bf16_hi(e2) * sc);
+      }
+  }
+  u32x4* dst = reinterpret_cast<u32x4*>(W16 + (int64_t)n * K + c * 16);
+  dst[0] = u32x4{o[0], o[1], o[2], o[3]};
+  dst[1] = u32x4{o[4], o[5], o[6], o[7]};
+}
+
+template <bool FP4>
+hipError_t stage_weights(const uint8_t* codes, const uint8_t* aux, int N, int K, int G, uint16_t* W16,
+                         hipStream_t stream) {
+  const int64_t chunks = (int64_t)N * (K >> 4);
+  hipLaunchKernelGGL((stage_weights_kernel<FP4>), dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream, codes,
+                     aux, N, K, G, W16);
+  return hipGetLastError();
 }
 
 int tiles(int M, int N, int bm) { return ((M + bm - 1) / bm) * ((N + BN - 1) / BN); }
@@ -517,9 +762,20 @@ hipError_t launch_tiles(const GemmArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_w4a16_gemm(const uint16_t* X, int M, int K, const uint8_t* P, const float* S,
-                             const uint8_t* Z, int N, int group, float* Y, hipStream_t stream) {
+                             const uint8_t* Z, int N, int group, float* Y, uint16_t* staged, hipStream_t stream) {
   GemmArgs a = {};
   a.X = X; a.M = M; a.N = N; a.K = K; a.P = P; a.S = S; a.Z = Z; a.Y = Y;
+  if (staged) {
+    hipError_t e = stage_weights<false>(P, Z, N, K, group, staged, stream);
+    if (e != hipSuccess) return e;
+    a.B = staged;
+    switch (group) {
+      case 32: return launch_tiles<B_INT4S, 32>(a, stream);
+      case 64: return launch_tiles<B_INT4S, 64>(a, stream);
+      case 128: return launch_tiles<B_INT4S, 128>(a, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (group) {
     case 32: return launch_tiles<B_INT4, 32>(a, stream);
     case 64: return launch_tiles<B_INT4, 64>(a, stream);
@@ -529,9 +785,15 @@ hipError_t launch_w4a16_gemm(const uint16_t* X, int M, int K, const uint8_t* P, 
 }
 
 hipError_t launch_fp4_gemm(const uint16_t* X, int M, int K, const uint8_t* codes, const uint8_t* bscale,
-                           float ts, int N, float* Y, hipStream_t stream) {
+                           float ts, int N, float* Y, uint16_t* staged, hipStream_t stream) {
   GemmArgs a = {};
   a.X = X; a.M = M; a.N = N; a.K = K; a.codes = codes; a.bscale = bscale; a.ts = ts; a.Y = Y;
+  if (staged) {
+    hipError_t e = stage_weights<true>(codes, bscale, N, K, 16, staged, stream);
+    if (e != hipSuccess) return e;
+    a.B = staged;
+    return launch_tiles<B_FP4S, 64>(a, stream);
+  }
   return launch_tiles<B_FP4, 64>(a, stream);
 }
 
