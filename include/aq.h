@@ -100,7 +100,7 @@ aq_status aq_w4a16_gemv(const uint16_t* X, int64_t M, int64_t K, const uint8_t* 
  * faster); otherwise the fused path runs and workspace is not touched.
  * workspace: caller-owned device memory, 256-byte aligned, used only during the
  * call on `stream` (its contents afterwards are unspecified).
- * Errors: EINVAL for M < 0 or M >= 2^30, K >= 2^22, a misaligned workspace, and
+ * Errors: EINVAL for M < 0 or M >= 2^30, K or N >= 2^22, a misaligned workspace, and
  *         as aq_w4a16_gemv otherwise.
  */
 size_t aq_w4a16_gemm_workspace(int64_t M, int64_t N, int64_t K, int32_t group);
@@ -182,7 +182,7 @@ aq_status aq_awq_search(const uint16_t* X_sub, int64_t T, const float* absmean_h
  * (staged: the exact bf16 weights written to `workspace` first), selected the
  * same way with aq_fp4_gemm_workspace(M, N, K).
  * Errors: EINVAL for M < 0, K <= 0 or K % 32, non-finite tensor_scale, N < 0,
- *         NULL / misaligned pointers, K or N >= 2^30, K >= 2^22 when M > 16.
+ *         NULL / misaligned pointers, K or N >= 2^30, K or N >= 2^22 when M > 16.
  */
 size_t aq_fp4_gemm_workspace(int64_t M, int64_t N, int64_t K);
 aq_status aq_fp4_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes, const uint8_t* block_scales,

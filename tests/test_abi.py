@@ -80,7 +80,7 @@ def test_gemv_einval(lib, kw):
 
 
 @pytest.mark.parametrize("kw", [dict(M=-1), dict(g=16), dict(K=100), dict(S=None), dict(Z=None), dict(K=0),
-                                dict(K=1 << 22)])
+                                dict(K=1 << 22), dict(N=1 << 22)])
 def test_gemm_einval(lib, kw):
     assert _prod(lib, "aq_w4a16_gemm", **kw) == _lib.AQ_EINVAL
 
@@ -164,6 +164,7 @@ def test_fp4_einval(lib):
     assert _fp4(lib, M=-1) == _lib.AQ_EINVAL
     assert _fp4(lib, C=FAKE_ODD) == _lib.AQ_EINVAL
     assert _fp4(lib, M=17, K=1 << 22) == _lib.AQ_EINVAL
+    assert _fp4(lib, M=17, N=1 << 22) == _lib.AQ_EINVAL
 
 
 def test_injected_runtime_failure(lib, monkeypatch):

@@ -61,8 +61,9 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
   } while (0)
 
 constexpr int64_t kDimLimit = int64_t(1) << 30;
-// MFMA GEMMs: 32-bit load offsets within a block's rows need K < 2^22.
-constexpr int64_t kGemmKLimit = int64_t(1) << 22;
+// MFMA GEMMs: 32-bit offsets within a block's rows (loads) and within its output
+// tile (stores) need K < 2^22 and N < 2^22.
+constexpr int64_t kGemmDimLimit = int64_t(1) << 22;
 // Smallest M for which the staged GEMM path (weights dequantized once into a bf16
 // staging matrix) is used when the caller provides the workspace.
 constexpr int64_t kStagedMinM = 2048;
@@ -141,7 +142,7 @@ aq_status aq_w4a16_gemv(const uint16_t* X, int64_t M, int64_t K, const uint8_t* 
 
 // Bytes of the bf16 staging matrix the MFMA GEMMs use at this size (0: fused path).
 static size_t staged_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M < kStagedMinM || N <= 0 || K <= 0 || N >= kDimLimit || K >= kGemmKLimit) return 0;
+  if (M < kStagedMinM || N <= 0 || K <= 0 || N >= kGemmDimLimit || K >= kGemmDimLimit) return 0;
   return (size_t)N * (size_t)K * sizeof(uint16_t);
 }
 
@@ -167,7 +168,8 @@ aq_status aq_w4a16_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_t* 
   AQ_REQUIRE(M >= 0 && M < kDimLimit, "aq_w4a16_gemm: M out of range (%lld)", (long long)M);
   aq_status st = check_product("aq_w4a16_gemm", X, M, K, packed, scales, zeros, N, group, Y);
   if (st != AQ_OK) return st;
-  AQ_REQUIRE(K < kGemmKLimit, "aq_w4a16_gemm: K must be below 2^22 (got %lld)", (long long)K);
+  AQ_REQUIRE(K < kGemmDimLimit && N < kGemmDimLimit, "aq_w4a16_gemm: K and N must be below 2^22 (got %lld, %lld)",
+             (long long)K, (long long)N);
   uint16_t* staged = nullptr;
   st = staging("aq_w4a16_gemm", M, N, K, workspace, workspace_bytes, &staged);
   if (st != AQ_OK) return st;
@@ -295,7 +297,9 @@ aq_status aq_fp4_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_t* co
   AQ_PTR(codes, 16, "codes");
   AQ_PTR(block_scales, 2, "block_scales");
   AQ_PTR(Y, 4, "Y");
-  if (M > 16) AQ_REQUIRE(K < kGemmKLimit, "aq_fp4_gemm: K must be below 2^22 for M > 16 (got %lld)", (long long)K);
+  if (M > 16)
+    AQ_REQUIRE(K < kGemmDimLimit && N < kGemmDimLimit,
+               "aq_fp4_gemm: K and N must be below 2^22 for M > 16 (got %lld, %lld)", (long long)K, (long long)N);
   uint16_t* staged = nullptr;
   if (M > 16) {
     const aq_status st = staging("aq_fp4_gemm", M, N, K, workspace, workspace_bytes, &staged);

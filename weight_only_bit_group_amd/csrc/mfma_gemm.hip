@@ -51,11 +51,17 @@
 //     contiguous range of a grouped tile order (a few row tiles, all column
 //     tiles), so the blocks it runs together share their activation and weight
 //     tiles in its L2.
+//   * Persistent grid (K % 64 == 0, at least four stages): one block per compute
+//     unit runs tiles b, b + grid, ...; the last three stages of a tile already
+//     load the next tile's first stages, so the load pipeline never drains.
 //   * INT4: the MFMAs of one group run block by block into a temporary that is
 //     rescaled by S[n, g] straight into the VGPR-resident output (one v_fma per
-//     output element per group), software-pipelined one block behind the MFMAs.
-//     A group wider than a stage (g = 128) is rescaled once per stage with the
-//     same S.
+//     output element per group), software-pipelined one block behind the MFMAs
+//     and interleaved with them (a slice of the rescale after each MFMA, so the
+//     VALU work overlaps the matrix core).  A group wider than a stage (g = 128)
+//     is rescaled once per stage with the same S.
+//   * Output stores address the tile from a uniform base plus one 32-bit lane
+//     offset (N < 2^22), so the epilogue holds no 64-bit address per store.
 // A lane of a 32x32x16 MFMA holds row (lane % 32) and k = 8 (lane / 32) .. +7 of
 // each operand; its 16 results are column (lane % 32), rows
 // 8 (i / 4) + 4 (lane / 32) + (i % 4), so they share one weight row n and need
@@ -178,20 +184,28 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_kernel(GemmArgs a) {
   const int M = a.M, N = a.N, K = a.K;
   const int tiles_n = (N + BN - 1) / BN;
   const int tiles_m = (M + BM - 1) / BM;
-  // XCD-contiguous linear index, then groups of GM row tiles walked column by column:
-  // the blocks an XCD runs at once cover GM row tiles x (blocks / GM) column tiles,
-  // so their activation and weight tiles stay in that XCD's L2.
-  const int t = tile_of_block(blockIdx.x, tiles_m * tiles_n);
-  const int GM = max(1, (tiles_m + 7) / 8);
-  const int group = t / (GM * tiles_n);
-  const int first_m = group * GM;
-  const int gm = min(tiles_m - first_m, GM);
-  const int within = t - group * GM * tiles_n;
-  const int m0 = (first_m + within % gm) * BM;
-  const int n0 = (within / gm) * BN;
+  const int ntiles = tiles_m * tiles_n;
   const int nfull = K / KS;                    // full 64-wide stages; TAIL adds one 32-wide stage
   const int nstage = nfull + (TAIL ? 1 : 0);
   const int ngroups = K / G;
+  // The block runs tiles blockIdx.x, blockIdx.x + gridDim.x, ... (a persistent grid of
+  // one block per CU, or one tile per block).  Virtual block vb maps to a tile by the
+  // XCD-aware order (vb runs on XCD vb % 8 when the grid is a multiple of 8): an
+  // XCD-contiguous linear index, then groups of GM row tiles walked column by column,
+  // so the tiles an XCD runs at once share their activation and weight tiles in its L2.
+  struct TileXY { int m0, n0, t; };
+  auto coords = [&](int i) -> TileXY {
+    const int t = tile_of_block(blockIdx.x + i * (int)gridDim.x, ntiles);
+    const int GM = max(1, (tiles_m + 7) / 8);
+    const int group = t / (GM * tiles_n);
+    const int first_m = group * GM;
+    const int gm = min(tiles_m - first_m, GM);
+    const int within = t - group * GM * tiles_n;
+    // wave-uniform: keep the coordinates in scalar registers
+    return TileXY{__builtin_amdgcn_readfirstlane((first_m + within % gm) * BM),
+                  __builtin_amdgcn_readfirstlane((within / gm) * BN), __builtin_amdgcn_readfirstlane(t)};
+  };
+  const int ntl = (ntiles - 1 - (int)blockIdx.x) / (int)gridDim.x + 1;   // tiles of this block
 
   // ---- LDS-DMA loads --------------------------------------------------------
   // Tile rows: load j of wave w covers the 8 rows from R0 = 8 r8, r8 = j NW + w; lane l
@@ -205,13 +219,17 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_kernel(GemmArgs a) {
   const int lrow8 = lane >> 3;
   auto gunit_of = [&](int r8) { return (lane & 7) ^ ((4 * r8 + (lane >> 4)) & 7); };
   auto fold_of = [&](int r8) -> uint32_t { return (TAIL && gunit_of(r8) >= 4) ? 64u : 0u; };
+  // lane offsets of the activation loads for the tile at row m0 (rows past M clamped)
   uint32_t aoff[A_DMA];
+  auto set_aoff = [&](int m0) {
 #pragma unroll
-  for (int j = 0; j < A_DMA; ++j) {
-    const int r8 = j * NW + wid;
-    aoff[j] = (uint32_t)(min(m0 + 8 * r8 + lrow8, M - 1) - m0) * (uint32_t)K * 2u + (uint32_t)gunit_of(r8) * 16u;
-  }
-  auto issue_a = [&](int s, int slot) {
+    for (int j = 0; j < A_DMA; ++j) {
+      const int r8 = j * NW + wid;
+      aoff[j] = (uint32_t)(min(m0 + 8 * r8 + lrow8, M - 1) - m0) * (uint32_t)K * 2u + (uint32_t)gunit_of(r8) * 16u;
+    }
+  };
+  // activations of stage s of the tile at row m0 (aoff set for that tile)
+  auto issue_a = [&](int m0, int s, int slot) {
     const char* base = reinterpret_cast<const char*>(a.X + (size_t)m0 * K) + (size_t)s * (KS * 2);
     const bool tail = TAIL && s == nfull;
 #pragma unroll
@@ -220,25 +238,22 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_kernel(GemmArgs a) {
       dma16(base, aoff[j] - (tail ? fold_of(r8) : 0u), lds_addr(&As[slot][8 * r8 * KS]));
     }
   };
-  auto issue_planes = [&](int s, int slot) {
+  // lane offsets of the SPLIT plane / staged weight loads for the tile at column n0
+  // (rows past N clamped); plane loads q and q + PER share one
+  constexpr int PER = BN / 8 / NW;   // plane loads per plane and wave
+  uint32_t boff[PER];
+  auto set_boff = [&](int n0) {
     if constexpr (!DEQ) {
-      const bool tail = TAIL && s == nfull;
 #pragma unroll
-      for (int pl = 0; pl < PLANES; ++pl) {
-        const char* base = reinterpret_cast<const char*>((pl ? a.B2 : a.B) + (size_t)n0 * K) + (size_t)s * (KS * 2);
-#pragma unroll
-        for (int j = 0; j < BN / 8 / NW; ++j) {
-          const int r8 = j * NW + wid;
-          const uint32_t off =
-              (uint32_t)(min(n0 + 8 * r8 + lrow8, N - 1) - n0) * (uint32_t)K * 2u + (uint32_t)gunit_of(r8) * 16u;
-          dma16(base, off - (tail ? fold_of(r8) : 0u), lds_addr(&Bs[slot][pl][8 * r8 * KS]));
-        }
+      for (int j = 0; j < PER; ++j) {
+        const int r8 = j * NW + wid;
+        boff[j] = (uint32_t)(min(n0 + 8 * r8 + lrow8, N - 1) - n0) * (uint32_t)K * 2u + (uint32_t)gunit_of(r8) * 16u;
       }
     }
   };
   // codes (32 bytes per row and stage, two 16-byte halves per lane pair) and the
   // per-row scalars of stage s: job i (0 <= i < JPW) of this wave
-  auto issue_job = [&](int s, int cslot, int xslot, int i) {
+  auto issue_job = [&](int n0, int s, int cslot, int xslot, int i) {
     if constexpr (DEQ) {
       const bool tail = TAIL && s == nfull;
       const int job = wid * JPW + i;   // wave-uniform
@@ -268,38 +283,40 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_kernel(GemmArgs a) {
       }
     }
   };
-  auto issue_codes = [&](int s, int cslot, int xslot) {
+  auto issue_codes = [&](int n0, int s, int cslot, int xslot) {
 #pragma unroll
-    for (int i = 0; i < JPW; ++i) issue_job(s, cslot, xslot, i);
+    for (int i = 0; i < JPW; ++i) issue_job(n0, s, cslot, xslot, i);
   };
   // one activation load (j < A_DMA) / one SPLIT plane load (q < B_DMA) of stage s
-  auto issue_a_one = [&](int s, int slot, int j) {
+  auto issue_a_one = [&](int m0, int s, int slot, int j) {
     const char* base = reinterpret_cast<const char*>(a.X + (size_t)m0 * K) + (size_t)s * (KS * 2);
     const int r8 = j * NW + wid;
     dma16(base, aoff[j] - ((TAIL && s == nfull) ? fold_of(r8) : 0u), lds_addr(&As[slot][8 * r8 * KS]));
   };
-  auto issue_plane_one = [&](int s, int slot, int q) {
+  auto issue_plane_one = [&](int n0, int s, int slot, int q) {
     if constexpr (!DEQ) {
-      constexpr int PER = BN / 8 / NW;   // loads per plane and wave
-      const int pl = q / PER, r8 = (q % PER) * NW + wid;
+      const int pl = q / PER, j = q % PER, r8 = j * NW + wid;
       const char* base = reinterpret_cast<const char*>((pl ? a.B2 : a.B) + (size_t)n0 * K) + (size_t)s * (KS * 2);
-      const uint32_t off =
-          (uint32_t)(min(n0 + 8 * r8 + lrow8, N - 1) - n0) * (uint32_t)K * 2u + (uint32_t)gunit_of(r8) * 16u;
-      dma16(base, off - ((TAIL && s == nfull) ? fold_of(r8) : 0u), lds_addr(&Bs[slot][pl][8 * r8 * KS]));
+      dma16(base, boff[j] - ((TAIL && s == nfull) ? fold_of(r8) : 0u), lds_addr(&Bs[slot][pl][8 * r8 * KS]));
     }
+  };
+  auto issue_planes = [&](int n0, int s, int slot) {
+#pragma unroll
+    for (int q = 0; q < B_DMA; ++q) issue_plane_one(n0, s, slot, q);
   };
 
   // staged INT4: the group steps of stage s (one dword per row, 64 rows per load, one
-  // or two groups per stage), issued by the first two or four waves
-  auto issue_steps = [&](int s, int slot) {
+  // or two groups per stage)
+  auto issue_steps = [&](int n0, int s, int slot) {
     if constexpr (BK == B_INT4S) {
+      // every wave issues one (no branch in the stage body): wave w loads part w % NL,
+      // so each part is loaded by several waves with the same bytes
       constexpr int NL = (G == 32) ? 4 : 2;
-      if (wid < NL) {
-        const int gi = wid >> 1, rh = 64 * (wid & 1);
-        const uint32_t n = (uint32_t)(min(n0 + rh + lane, N - 1) - n0);
-        const uint32_t g = (uint32_t)min((s * KS + 32 * gi) / G, ngroups - 1);
-        dma4(a.S + (size_t)n0 * ngroups, (n * (uint32_t)ngroups + g) * 4u, lds_addr(&AX[slot][0][gi][rh]));
-      }
+      const int part = wid % NL;
+      const int gi = part >> 1, rh = 64 * (part & 1);
+      const uint32_t n = (uint32_t)(min(n0 + rh + lane, N - 1) - n0);
+      const uint32_t g = (uint32_t)min((s * KS + 32 * gi) / G, ngroups - 1);
+      dma4(a.S + (size_t)n0 * ngroups, (n * (uint32_t)ngroups + g) * 4u, lds_addr(&AX[slot][0][gi][rh]));
     }
   };
 
@@ -390,19 +407,12 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_kernel(GemmArgs a) {
   constexpr int A_BUF = BM * KS / 8, B_BUF = PLANES * BN * KS / 8, B_PLANE = BN * KS / 8;  // 16-byte units
   static_assert(A_DMA == 4 && JPW <= 4 && B_DMA % 2 == 0, "loads are spread over the parts of a stage");
 
-  // INT4 group partials: the stage's (group, block) items run in four parts of NG
-  // items; each part also rescales the previous part's items, and the last part's
-  // items are carried into the next stage: carried slot c holds the partial of block
-  // 4 - NGMAX + c (zero partial and step when a stage carries fewer).
-  constexpr int NGMAX = (RESCALE && G == 32) ? 2 : 1;
-  f32x16 tcar[NGMAX];
-  float scar[NGMAX];
+  // INT4: the group partial of block (1, 1) from a stage's last part, with its step,
+  // rescaled by the next stage's first part (or the tile epilogue); zero at the start
+  f32x16 tcar;
+  float scar = 0.0f;
 #pragma unroll
-  for (int g = 0; g < NGMAX; ++g) {
-    scar[g] = 0.0f;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) tcar[g][v] = 0.0f;
-  }
+  for (int v = 0; v < 16; ++v) tcar[v] = 0.0f;
 
   // ---- one stage ----------------------------------------------------------------
   // The workgroup barrier sits in the middle of a stage: stage s reads all its
@@ -421,7 +431,10 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_kernel(GemmArgs a) {
   // same for stages s + 1 / s + 2 (0: none), whose dequantization parts 2, 3 / 0, 1
   // run here; MA: load activations (INT4, FP4: stage s + 2) or activations and planes
   // (SPLIT: stage s + 2, after M_s); MC: load codes and scalars of stage s + 3.
-  auto run_stage = [&](int s, auto nk_tag, auto nx1_tag, auto nx2_tag, auto mc_tag, auto ma_tag) {
+  // q: the block's stage index (ring slots); (m2, n2, s2): tile and tile stage of stage
+  // q + 2, (n3, s3): weight rows and tile stage of stage q + 3 (prefetch targets).
+  auto run_stage = [&](int q, int m2, int n2, int s2, int n3, int s3, auto nk_tag, auto nx1_tag, auto nx2_tag,
+                       auto mc_tag, auto ma_tag) {
     constexpr int NKS = decltype(nk_tag)::value;
     constexpr int NX1 = decltype(nx1_tag)::value;
     constexpr int NX2 = decltype(nx2_tag)::value;
@@ -429,10 +442,10 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_kernel(GemmArgs a) {
     constexpr bool MA = decltype(ma_tag)::value;
     constexpr int NG = (RESCALE && G == 32) ? NKS / 2 : 1;   // group partials per block (INT4)
     constexpr int KPG = NKS / NG;
-    const int abuf = s % NA;
-    const int bbuf = s % NB;
-    const int xs = s & 3;
-    if constexpr (MC) issue_codes(s + CD, (s + CD) % 3, (s + CD) & 3);
+    const int abuf = q % NA;
+    const int bbuf = q % NB;
+    const int xs = q & 3;
+    if constexpr (MC) issue_codes(n3, s3, (q + CD) % 3, (q + CD) & 3);
     __builtin_amdgcn_sched_barrier(0);
     // LDS reads: this stage's fragments (m-block 1's during part 0) and group steps
     bf16x8 af[2][NKS], bf[2][NKS], bf2[2][NKS];
@@ -458,47 +471,47 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_kernel(GemmArgs a) {
         for (int gi = 0; gi < NG; ++gi) sc[ni][gi] = __builtin_bit_cast(float, AX[xs][0][gi][wn * 64 + 32 * ni + l32]);
     }
     __builtin_amdgcn_sched_barrier(0);
-    f32x16 tprev[NGMAX];   // the previous part's partials and steps
-    float sprev[NGMAX];
+    // Parts: INT4 runs one (group, block) item per part, item it = (group it / 4,
+    // block it % 4), so NPART = 4 NG; each part rescales the previous part's item (part
+    // 0: the item carried from the previous stage, always block (1, 1)).  The other
+    // kinds run one block per part.  Loads and dequantization are spread over the
+    // parts in four steps (pp = 0 .. 3, one every NPART / 4 parts).
+    constexpr int NPART = RESCALE ? 4 * NG : 4;
+    constexpr int PSTEP = NPART / 4;
+    f32x16 tprev = tcar;
+    float sprev = scar;
 #pragma unroll
-    for (int part = 0; part < 4; ++part) {
+    for (int part = 0; part < NPART; ++part) {
       if constexpr (RESCALE) {
-        // this part: items part NG .. part NG + NG - 1, item it = (group it / 4, block it % 4)
-        f32x16 tp[NGMAX];
-        float st[NGMAX];
+        const int gi = part >> 2, blk = part & 3, mi = blk >> 1, ni = blk & 1;
+        const int pblk = part == 0 ? 3 : ((part - 1) & 3), qm = pblk >> 1, qn = pblk & 1;
+        // The item's MFMAs interleaved with the previous item's rescale: slice k of the
+        // rescale (V of its 16 outputs) runs after MFMA k and before MFMA k + 1, so the
+        // VALU work overlaps the matrix core.  Empty asm statements fix the order (the
+        // compiler would otherwise group the rescale ahead of the MFMAs, or sink it to
+        // the end of the stage): each ties the accumulator elements of slices k - 1 and
+        // k and the A operand of MFMA k.
+        constexpr int V = 16 / KPG;
+        float e[16];
 #pragma unroll
-        for (int x = 0; x < NG; ++x) {
-          const int it = part * NG + x;
-          const int gi = it >> 2, blk = it & 3, mi = blk >> 1, ni = blk & 1;
+        for (int v = 0; v < 16; ++v) e[v] = acc[qm][qn][v];
+        f32x16 tp;
 #pragma unroll
-          for (int k = 0; k < KPG; ++k) {
-            const int ks = gi * KPG + k;
-            const f32x16 zero = {};
-            tp[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi][ks], bf[ni][ks], k == 0 ? zero : tp[x], 0, 0, 0);
-          }
-          st[x] = sc[ni][gi];
-        }
-        // rescale the previous part's items (part 0: the carried slots)
-        if (part == 0) {
+        for (int k = 0; k < KPG; ++k) {
+          const int ks = gi * KPG + k;
 #pragma unroll
-          for (int c = 0; c < NGMAX; ++c) {
-            const int blk = 4 - NGMAX + c, qm = blk >> 1, qn = blk & 1;
+          for (int v = (k > 0 ? (k - 1) * V : 0); v < (k + 1) * V; ++v) asm volatile("" : "+v"(e[v]));
+          asm volatile("" : "+v"(af[mi][ks]));
+          const f32x16 zero = {};
+          tp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi][ks], bf[ni][ks], k == 0 ? zero : tp, 0, 0, 0);
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[qm][qn][v] = __builtin_fmaf(scar[c], tcar[c][v], acc[qm][qn][v]);
-          }
-        } else {
-#pragma unroll
-          for (int x = 0; x < NG; ++x) {
-            const int blk = ((part - 1) * NG + x) & 3, qm = blk >> 1, qn = blk & 1;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[qm][qn][v] = __builtin_fmaf(sprev[x], tprev[x][v], acc[qm][qn][v]);
-          }
+          for (int v = k * V; v < (k + 1) * V; ++v) e[v] = __builtin_fmaf(sprev, tprev[v], e[v]);
         }
 #pragma unroll
-        for (int x = 0; x < NG; ++x) {
-          tprev[x] = tp[x];
-          sprev[x] = st[x];
-        }
+        for (int v = 0; v < 16; ++v) acc[qm][qn][v] = e[v];
+        asm volatile("" : "+v"(acc[qm][qn]));
+        tprev = tp;
+        sprev = sc[ni][gi];
       } else {
         const int mi = part >> 1, ni = part & 1;
 #pragma unroll
@@ -508,43 +521,48 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_kernel(GemmArgs a) {
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi][ks], bf2[ni][ks], acc[mi][ni], 0, 0, 0);
         }
       }
-      // m-block 1 is first used by block 2 (item 2 of group 0): read in the part before
-      if (part == 2 / NG - 1) read_a(1);
-      if constexpr (DEQ) {
-        // dequantization: parts 0, 1 finish stage s + 1 (into the other weight buffer);
-        // parts 2, 3 start stage s + 2 (into this stage's buffer, free after M_s)
-        if (part < 2) {
-          if constexpr (NX1 > 0) dq_part(part + 2, bbuf ^ 1, NX1 == 2);
-        } else {
-          if constexpr (NX2 > 0) {
-            if (part == 2) dq_load((s + 2) % 3, (s + 2) & 3);
-            dq_part(part - 2, bbuf, NX2 == 2);
+      // m-block 1 is first used by block 2 (part 2): read in part 1
+      if (part == 1) read_a(1);
+      if (part % PSTEP == 0) {
+        const int pp = part / PSTEP;
+        if constexpr (DEQ) {
+          // dequantization: steps 0, 1 finish stage q + 1 (into the other weight buffer);
+          // steps 2, 3 start stage q + 2 (into this stage's buffer, free after M_s)
+          if (pp < 2) {
+            if constexpr (NX1 > 0) dq_part(pp + 2, bbuf ^ 1, NX1 == 2);
+          } else {
+            if constexpr (NX2 > 0) {
+              if (pp == 2) dq_load((q + 2) % 3, (q + 2) & 3);
+              dq_part(pp - 2, bbuf, NX2 == 2);
+            }
+          }
+        }
+        if constexpr (DEQ && MA) {
+          issue_a_one(m2, s2, (q + PD) % NA, pp);
+        } else if constexpr (STAGED && MA) {
+          // stage q + 2's activations over all four steps, its weights in steps 0, 1,
+          // its group steps in step 2 (after M_s, so they are not counted there)
+          issue_a_one(m2, s2, (q + 2) % 3, pp);
+          if (pp < 2) {
+#pragma unroll
+            for (int qq = pp * (B_DMA / 2); qq < (pp + 1) * (B_DMA / 2); ++qq)
+              issue_plane_one(n2, s2, (q + 2) % 3, qq);
+          }
+          if (pp == 2) issue_steps(n2, s2, (q + 2) & 3);
+        } else if constexpr (MA) {
+          // SPLIT: stage q + 2's activations and planes go into this stage's buffers,
+          // after M_s
+          if (pp >= 2) {
+#pragma unroll
+            for (int j = (pp - 2) * (A_DMA / 2); j < (pp - 1) * (A_DMA / 2); ++j) issue_a_one(m2, s2, bbuf, j);
+#pragma unroll
+            for (int qq = (pp - 2) * (B_DMA / 2); qq < (pp - 1) * (B_DMA / 2); ++qq)
+              issue_plane_one(n2, s2, bbuf, qq);
           }
         }
       }
-      if constexpr (DEQ && MA) {
-        issue_a_one(s + PD, (s + PD) % NA, part);
-      } else if constexpr (STAGED && MA) {
-        // stage s + 2's activations over all four parts, its weights in parts 0, 1,
-        // its group steps in part 2 (after M_s, so they are not counted there)
-        issue_a_one(s + 2, (s + 2) % 3, part);
-        if (part < 2) {
-#pragma unroll
-          for (int q = part * (B_DMA / 2); q < (part + 1) * (B_DMA / 2); ++q) issue_plane_one(s + 2, (s + 2) % 3, q);
-        }
-        if (part == 2) issue_steps(s + 2, (s + 2) & 3);
-      } else if constexpr (MA) {
-        // SPLIT: stage s + 2's activations and planes go into this stage's buffers,
-        // after M_s
-        if (part >= 2) {
-#pragma unroll
-          for (int j = (part - 2) * (A_DMA / 2); j < (part - 1) * (A_DMA / 2); ++j) issue_a_one(s + 2, bbuf, j);
-#pragma unroll
-          for (int q = (part - 2) * (B_DMA / 2); q < (part - 1) * (B_DMA / 2); ++q) issue_plane_one(s + 2, bbuf, q);
-        }
-      }
       __builtin_amdgcn_sched_barrier(0);
-      if (part == 1) {
+      if (part == NPART / 2 - 1) {
         // M_s: only the loads issued in this stage so far may still be in flight (loads
         // complete in order); this wave's LDS writes are done
         constexpr int KEEP = DEQ ? (MC ? JPW : 0) + (MA ? 2 : 0) : STAGED ? (MA ? 2 + B_DMA : 0) : 0;
@@ -554,31 +572,105 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_kernel(GemmArgs a) {
       }
     }
     if constexpr (RESCALE) {
-      // carry the last part's items (blocks 4 - NG .. 3) into slots NGMAX - NG ..
-#pragma unroll
-      for (int c = 0; c < NGMAX; ++c) {
-        const int x = c - (NGMAX - NG);
-        if (x >= 0) {
-          tcar[c] = tprev[x];
-          scar[c] = sprev[x];
-        } else {
-          scar[c] = 0.0f;
-        }
-      }
+      tcar = tprev;   // the last item (block (1, 1)) is rescaled by the next stage or the epilogue
+      scar = sprev;
     }
   };
 
-  // ---- prologue ----------------------------------------------------------------
-  // Loads of stages 0 and 1 (and the codes of stage 2), stage 0's weights and the
-  // first half of stage 1's dequantized; SPLIT: stages 0 and 1.
-  if constexpr (DEQ) {
-    issue_codes(0, 0, 0);
-    issue_a(0, 0);
-    if (nstage > 1) {
-      issue_codes(1, 1, 1);
-      issue_a(1, 1);
+  // ---- tile epilogue ----------------------------------------------------------------
+  // Applies the last carried group partials, writes the tile's outputs (SPLIT: its fp64
+  // sum of squares) and clears the accumulators for the block's next tile.
+  // Result i of block (mi, ni): row 8 (i / 4) + 4 lh + (i % 4), column l32.
+  __shared__ double wsum[NW];
+  auto finish_tile = [&](const TileXY& tt) {
+    if constexpr (RESCALE) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[1][1][v] = __builtin_fmaf(scar, tcar[v], acc[1][1][v]);
+      scar = 0.0f;
     }
-    if (nstage > 2) issue_codes(2, 2, 2);
+    const int m0 = tt.m0, n0 = tt.n0;
+    // this lane's first output row and column; opaque to the optimizer so no part of the
+    // epilogue's addressing is hoisted out of the tile loop into registers held by the
+    // whole main loop
+    int lrow = wm * 64 + 4 * lh, lcol = wn * 64 + l32;
+    asm volatile("" : "+v"(lrow), "+v"(lcol));
+    if constexpr (SPLIT) {
+      double ss = 0.0;
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+          const int n = n0 + lcol + 32 * ni;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int m = m0 + lrow + 32 * mi + 8 * (v >> 2) + (v & 3);
+            const double d = (double)acc[mi][ni][v];
+            if (m < M && n < N) ss = __builtin_fma(d, d, ss);
+          }
+        }
+      ss = wave_sum(ss);
+      if (lane == 0) wsum[wid] = ss;
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the LDS write is done (loads stay in flight)
+      stage_barrier();
+      if (tid == 0) {
+        double tot = 0.0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) tot += wsum[w];
+        a.partial[tt.t] = tot;
+      }
+    } else {
+      // store addresses: the tile's base (uniform) plus a 32-bit byte offset per lane,
+      // which stays below 2^32 for N < 2^22
+      char* yt = reinterpret_cast<char*>(a.Y + (int64_t)m0 * N + n0);
+      const uint32_t lbase = ((uint32_t)lrow * (uint32_t)N + (uint32_t)lcol) * 4u;
+      const uint32_t rstride = (uint32_t)N * 4u;
+      auto out = [&](int mi, int ni, int v) { return TSCALE ? acc[mi][ni][v] * a.ts : acc[mi][ni][v]; };
+      auto addr = [&](int mi, int ni, int v) {
+        const int dm = 32 * mi + 8 * (v >> 2) + (v & 3);
+        return reinterpret_cast<float*>(yt + (lbase + (uint32_t)dm * rstride + 128u * (uint32_t)ni));
+      };
+      if ((m0 + BM <= M) && (n0 + BN <= N)) {
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) __builtin_nontemporal_store(out(mi, ni, v), addr(mi, ni, v));
+      } else {
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int dm = 32 * mi + 8 * (v >> 2) + (v & 3);
+              if (m0 + lrow + dm < M && n0 + lcol + 32 * ni < N) __builtin_nontemporal_store(out(mi, ni, v), addr(mi, ni, v));
+            }
+      }
+    }
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
+  };
+
+  // ---- prologue ----------------------------------------------------------------
+  // Loads of stages 0 and 1 of the first tile (and the codes of stage 2), stage 0's
+  // weights and the first half of stage 1's dequantized; SPLIT: stages 0 and 1.
+  TileXY tc = coords(0);                       // tile of stage q
+  TileXY tn = ntl > 1 ? coords(1) : tc;        // the block's next tile
+  set_aoff(tc.m0);
+  set_boff(tc.n0);
+  if constexpr (DEQ) {
+    issue_codes(tc.n0, 0, 0, 0);
+    issue_a(tc.m0, 0, 0);
+    if (nstage > 1) {
+      issue_codes(tc.n0, 1, 1, 1);
+      issue_a(tc.m0, 1, 1);
+    }
+    if (nstage > 2) issue_codes(tc.n0, 2, 2, 2);
     __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
     stage_barrier();
     dequant(0, 0, 0, TAIL && nfull == 0);
@@ -588,13 +680,13 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_kernel(GemmArgs a) {
       dq_part(1, 1, TAIL && nfull == 1);
     }
   } else {
-    issue_a(0, 0);
-    issue_planes(0, 0);
-    issue_steps(0, 0);
+    issue_a(tc.m0, 0, 0);
+    issue_planes(tc.n0, 0, 0);
+    issue_steps(tc.n0, 0, 0);
     if (nstage > 1) {
-      issue_a(1, 1);
-      issue_planes(1, 1);
-      issue_steps(1, 1);
+      issue_a(tc.m0, 1, 1);
+      issue_planes(tc.n0, 1, 1);
+      issue_steps(tc.n0, 1, 1);
     }
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
@@ -605,82 +697,56 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_kernel(GemmArgs a) {
   using IC0 = std::integral_constant<int, 0>;
   using YES = std::true_type;
   using NO = std::false_type;
-  // steady state: full stages whose next two stages are full and that load
-  // everything; the last three stages are peeled (their loads and dequantization
-  // depend on the position)
-  const int steady = max(0, nstage - 3);
-  for (int s = 0; s < steady; ++s) run_stage(s, IC4{}, IC4{}, IC4{}, YES{}, YES{});
+  // The block's tiles run back to back; q, the block's stage count, indexes the LDS
+  // rings across tiles.  Within a tile the steady loop runs the full stages whose
+  // prefetch targets (stage s + 2's activations and weights, stage s + 3's codes) lie
+  // in the same tile; a tile's last three stages are peeled: with a next tile they
+  // load its first stages, so the pipeline does not drain between tiles, and on the
+  // block's last tile they run it down (loads and dequantization depend on the
+  // position).  A block with several tiles has full stages only (K % 64 == 0 and at
+  // least four stages per tile).
   auto kind = [&](int t) { return t >= nstage ? 0 : (TAIL && t == nfull) ? 2 : 4; };
-  for (int s = steady; s < nstage; ++s) {
+  const int steady = max(0, nstage - 3);
+  int q = 0;
+  for (int i = 0; i + 1 < ntl; ++i) {
+    for (int s = 0; s < steady; ++s, ++q)
+      run_stage(q, tc.m0, tc.n0, s + 2, tc.n0, s + 3, IC4{}, IC4{}, IC4{}, YES{}, YES{});
+    run_stage(q, tc.m0, tc.n0, nstage - 1, tn.n0, 0, IC4{}, IC4{}, IC4{}, YES{}, YES{});
+    ++q;
+    set_aoff(tn.m0);   // activation and weight loads move to the next tile
+    set_boff(tn.n0);
+    run_stage(q, tn.m0, tn.n0, 0, tn.n0, 1, IC4{}, IC4{}, IC4{}, YES{}, YES{});
+    ++q;
+    run_stage(q, tn.m0, tn.n0, 1, tn.n0, 2, IC4{}, IC4{}, IC4{}, YES{}, YES{});
+    ++q;
+    finish_tile(tc);
+    tc = tn;
+    if (i + 2 < ntl) tn = coords(i + 2);
+  }
+  // the block's last tile
+  const int m0 = tc.m0, n0 = tc.n0;
+  for (int s = 0; s < steady; ++s, ++q)
+    run_stage(q, m0, n0, s + 2, n0, s + 3, IC4{}, IC4{}, IC4{}, YES{}, YES{});
+  for (int s = steady; s < nstage; ++s, ++q) {
     const int k0 = kind(s), k1 = kind(s + 1), k2 = kind(s + 2);
     const bool ma = s + 2 < nstage;   // codes are never loaded here (s + 3 >= nstage)
     if (k0 == 2) {
-      run_stage(s, IC2{}, IC0{}, IC0{}, NO{}, NO{});
+      run_stage(q, m0, n0, s + 2, n0, s + 3, IC2{}, IC0{}, IC0{}, NO{}, NO{});
     } else if (k1 == 0) {
-      run_stage(s, IC4{}, IC0{}, IC0{}, NO{}, NO{});
+      run_stage(q, m0, n0, s + 2, n0, s + 3, IC4{}, IC0{}, IC0{}, NO{}, NO{});
     } else if (k1 == 2) {
-      run_stage(s, IC4{}, IC2{}, IC0{}, NO{}, NO{});
+      run_stage(q, m0, n0, s + 2, n0, s + 3, IC4{}, IC2{}, IC0{}, NO{}, NO{});
     } else if (k2 == 0) {
-      run_stage(s, IC4{}, IC4{}, IC0{}, NO{}, NO{});
+      run_stage(q, m0, n0, s + 2, n0, s + 3, IC4{}, IC4{}, IC0{}, NO{}, NO{});
     } else if (k2 == 2) {
-      if (ma) run_stage(s, IC4{}, IC4{}, IC2{}, NO{}, YES{});
-      else run_stage(s, IC4{}, IC4{}, IC2{}, NO{}, NO{});
+      if (ma) run_stage(q, m0, n0, s + 2, n0, s + 3, IC4{}, IC4{}, IC2{}, NO{}, YES{});
+      else run_stage(q, m0, n0, s + 2, n0, s + 3, IC4{}, IC4{}, IC2{}, NO{}, NO{});
     } else {
-      if (ma) run_stage(s, IC4{}, IC4{}, IC4{}, NO{}, YES{});
-      else run_stage(s, IC4{}, IC4{}, IC4{}, NO{}, NO{});
+      if (ma) run_stage(q, m0, n0, s + 2, n0, s + 3, IC4{}, IC4{}, IC4{}, NO{}, YES{});
+      else run_stage(q, m0, n0, s + 2, n0, s + 3, IC4{}, IC4{}, IC4{}, NO{}, NO{});
     }
   }
-  if constexpr (RESCALE) {
-    // the last stage's carried partials
-#pragma unroll
-    for (int c = 0; c < NGMAX; ++c) {
-      const int blk = 4 - NGMAX + c, qm = blk >> 1, qn = blk & 1;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[qm][qn][v] = __builtin_fmaf(scar[c], tcar[c][v], acc[qm][qn][v]);
-    }
-  }
-
-  // ---- epilogue --------------------------------------------------------------
-  // result i of block (mi, ni): row 8 (i / 4) + 4 lh + (i % 4), column l32
-  if constexpr (SPLIT) {
-    double ss = 0.0;
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
-        const int n = n0 + wn * 64 + 32 * ni + l32;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = m0 + wm * 64 + 32 * mi + 8 * (v >> 2) + 4 * lh + (v & 3);
-          const double d = (double)acc[mi][ni][v];
-          if (m < M && n < N) ss = __builtin_fma(d, d, ss);
-        }
-      }
-    ss = wave_sum(ss);
-    __shared__ double wsum[NW];
-    if (lane == 0) wsum[wid] = ss;
-    __syncthreads();
-    if (tid == 0) {
-      double tot = 0.0;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) tot += wsum[w];
-      a.partial[t] = tot;
-    }
-  } else {
-    const bool full = (m0 + BM <= M) && (n0 + BN <= N);
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
-        const int n = n0 + wn * 64 + 32 * ni + l32;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = m0 + wm * 64 + 32 * mi + 8 * (v >> 2) + 4 * lh + (v & 3);
-          const float y = TSCALE ? acc[mi][ni][v] * a.ts : acc[mi][ni][v];
-          if (full || (m < M && n < N)) __builtin_nontemporal_store(y, &a.Y[(int64_t)m * N + n]);
-        }
-      }
-  }
+  finish_tile(tc);
 }
 
 // Staged weights: the codes of one weight matrix dequantized once into a bf16 matrix
@@ -743,12 +809,30 @@ int tiles(int M, int N, int bm) { return ((M + bm - 1) / bm) * ((N + BN - 1) / B
 // 256-row tiles (8 waves) once M fills them; 128-row tiles (4 waves) for small M.
 constexpr int kWideM = 192;
 
+// Compute units of the current device (queried once per device).
+int cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] <= 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cached[dev] = v;
+  }
+  return cached[dev];
+}
+
+// Grid: one block per CU looping over the tiles (persistent) when every tile has at
+// least four full stages, else one block per tile.
 template <int BK, int G, bool TAIL>
 hipError_t launch_tail(const GemmArgs& a, hipStream_t stream) {
-  if (a.M > kWideM) {
-    hipLaunchKernelGGL((gemm_kernel<BK, G, TAIL, 4>), dim3(tiles(a.M, a.N, 256)), dim3(512), 0, stream, a);
+  const bool wide = a.M > kWideM;
+  const int nt = tiles(a.M, a.N, wide ? 256 : 128);
+  const int grid = (!TAIL && a.K / KS >= 4) ? min(nt, cu_count()) : nt;
+  if (wide) {
+    hipLaunchKernelGGL((gemm_kernel<BK, G, TAIL, 4>), dim3(grid), dim3(512), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((gemm_kernel<BK, G, TAIL, 2>), dim3(tiles(a.M, a.N, 128)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((gemm_kernel<BK, G, TAIL, 2>), dim3(grid), dim3(256), 0, stream, a);
   }
   return hipGetLastError();
 }
