@@ -15,8 +15,10 @@ group 64):
 
 Launches are bracketed by HIP events on the stream they run on (torch's current
 stream, which the binding passes to the library): one event pair per launch,
-except the 40 decode GEMVs of a step, which run back to back between one pair
-(as a decode stream does) and are averaged per launch.  The headline value is
+except the 40 decode GEMVs of a step, which are captured once in a HIP graph and
+replayed back to back between one pair (as a decode loop does; eager Python
+launches would measure the binding's per-call overhead instead of the kernel) and
+are averaged per launch.  The headline value is
 the decode GEMV's HBM throughput (algorithmic bytes / average launch duration);
 the GEMM's TFLOP/s and the other stages are reported beside it.
 
@@ -127,7 +129,7 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
-    print("[bench] setup", flush=True)
+    print("[bench] setup", file=sys.stderr, flush=True)
 
     gen = torch.Generator(device=dev)
     gen.manual_seed(1234)
@@ -189,14 +191,28 @@ def main():
         else:
             fn()
 
+    # The decode GEMVs run back to back over the rotating copies, captured once in a HIP
+    # graph (as a decode loop does): replaying it launches the 40 kernels without the
+    # Python binding's per-call overhead (several microseconds, more than a launch), so the
+    # event pair around the replay measures the GPU, not the interpreter.
+    def gemv_batch():
+        for (p, s, z) in copies:
+            B.aq_w4a16_gemv(x1, p, s, z, G_, out=y1)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        gemv_batch()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    gemv_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gemv_graph):
+        gemv_batch()
+    torch.cuda.synchronize()
+
     def step(record):
         timed("pack", record, lambda: B.aq_quantize_pack(w_gate, G_, packed=pk[0], scales=pk[1], zeros=pk[2]))
-        # the decode GEMVs run back to back over the rotating copies (as a decode stream
-        # does); one event pair brackets the batch and the average is per launch
-        def gemv_batch():
-            for (p, s, z) in copies:
-                B.aq_w4a16_gemv(x1, p, s, z, G_, out=y1)
-        timed("gemv", record, gemv_batch)
+        timed("gemv", record, gemv_graph.replay)
         p, s, z = copies[0]
         timed("gemm", record, lambda: B.aq_w4a16_gemm(xg, p, s, z, G_, out=yg, workspace=ws_gemm))
         sum_abs.zero_()
@@ -205,17 +221,17 @@ def main():
         timed("fp4_gemv", record, lambda: B.aq_fp4_gemm(xf1, codes, bsc, ts, out=yf1))
         timed("fp4_gemm", record, lambda: B.aq_fp4_gemm(xf2, codes, bsc, ts, out=yf2, workspace=ws_fp4))
 
-    print(f"[bench] warmup {args.warmup}", flush=True)
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
-    print(f"[bench] timing {args.steps} steps", flush=True)
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step(True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    print("[bench] timed region done", flush=True)
+    print("[bench] timed region done", file=sys.stderr, flush=True)
 
     ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in events.items()}
     ms["gemv"] /= N_COPIES
@@ -265,7 +281,7 @@ def main():
         "rows": rows,
     }
     if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle)", flush=True)
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
 

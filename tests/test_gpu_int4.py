@@ -234,3 +234,44 @@ def test_pack_then_gemv_round_trip():
     y = host(B.aq_w4a16_gemv(dev_bf16(xb), p, s, z, 64))
     p0, s0, z0 = int4.quantize_pack(synth.bf16_bits_to_f32(wb), 64)
     check_close(y, int4.forward(synth.bf16_bits_to_f32(xb), p0, s0, z0, 64), "pack+gemv o_proj")
+
+
+def test_gemv_batch_in_a_hip_graph():
+    """The decode GEMV allocates nothing and synchronizes nothing, so a batch of launches can
+    be captured in a HIP graph (the bench times its decode batch that way).  Every replay,
+    with eager work and synchronizations between replays, equals the eager result bit for bit."""
+    ws = [synth.layer_weight_bf16(20 + i, "o_proj") for i in range(3)]
+    xb = synth.layer_activations_bf16(7, 1, 2048)
+    step("aq_w4a16_gemv x3 captured in a HIP graph")
+    x = dev_bf16(xb)
+    packs = [B.aq_quantize_pack(dev_bf16(w), 64) for w in ws]
+    outs = [torch.empty((1, 2048), dtype=torch.float32, device=x.device) for _ in packs]
+
+    def batch():
+        for (p, s, z), y in zip(packs, outs):
+            B.aq_w4a16_gemv(x, p, s, z, 64, out=y)
+
+    batch()
+    eager = [host(y).copy() for y in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        batch()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        batch()
+    torch.cuda.synchronize()
+    other = B.aq_w4a16_gemv(dev_bf16(synth.layer_activations_bf16(8, 1, 2048)), *packs[0], 64)
+    for rep in range(3):
+        for y in outs:
+            y.fill_(float("nan"))
+        graph.replay()
+        got = [host(y) for y in outs]
+        for i, (a, b) in enumerate(zip(got, eager)):
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"replay {rep}, launch {i}"
+        B.aq_w4a16_gemv(x, *packs[1], 64, out=other)   # eager work between replays
+        torch.cuda.synchronize()
+    check_close(eager[0], int4.forward(synth.bf16_bits_to_f32(xb), *int4.quantize_pack(
+        synth.bf16_bits_to_f32(ws[0]), 64), 64), "graph gemv o_proj")
