@@ -12,6 +12,11 @@ group 64):
   absmean  aq_act_absmean over 65536 x 2048 calibration tokens   (AWQ statistic)
   search   aq_awq_search, 4096 tokens, 20 alphas, final pack     (AWQ search)
   fp4      aq_fp4_gemm at M = 1 and M = 2048 on W[14336, 4096]   (FP4 decode)
+  layer    a whole Qwen2.5-3B decoder layer: norm-group AWQ of    (module-level path)
+           q|k|v and gate|up (joint search, 65536-token abs-mean,
+           4096-token search) plus plain packing of o and down;
+           and the layer's seven decode GEMVs at M = 1, averaged
+           over a graph-replayed stack of 12 layers (536 MB)
 
 Launches are bracketed by HIP events on the stream they run on (torch's current
 stream, which the binding passes to the library): one event pair per launch,
@@ -46,6 +51,7 @@ M_GEMM = 4096
 N_COPIES = 40
 FP4_N, FP4_K, FP4_M = 14336, 4096, 2048
 CAL_T, CAL_SUB = 65536, 4096
+LAYER_STACK = 12
 
 
 def gemv_bytes(m, n, k, g):
@@ -122,6 +128,7 @@ def main():
 
     import torch
     from weight_only_bit_group_amd import binding as B
+    from weight_only_bit_group_amd import layer as L
     from weight_only_bit_group_amd import synth
 
     if not torch.cuda.is_available():
@@ -176,9 +183,56 @@ def main():
     yf2 = torch.empty((FP4_M, FP4_N), dtype=torch.float32, device=dev)
     ws_gemm = torch.empty(B.aq_w4a16_gemm_workspace(M_GEMM, N_, K_, G_), dtype=torch.uint8, device=dev)
     ws_fp4 = torch.empty(B.aq_fp4_gemm_workspace(FP4_M, FP4_N, FP4_K), dtype=torch.uint8, device=dev)
+    # a whole decoder layer: the seven linears as bf16 nn.Linear, RMSNorm weights, and its
+    # quantized form (norm-group AWQ for q|k|v and gate|up, plain packing of o and down)
+    layer_lin = {}
+    for name, n, k in synth.LAYER_LINEARS:
+        m = torch.nn.Linear(k, n, bias=False, device=dev, dtype=torch.bfloat16)
+        with torch.no_grad():
+            m.weight.copy_(weight_bf16(n, k))
+        layer_lin[name] = m
+    ln_w = torch.ones(K_, dtype=torch.float32, device=dev)
+
+    def layer_awq():
+        out = {}
+        _, mods, _ = L.norm_group_awq(ln_w, [layer_lin[n] for n in ("q_proj", "k_proj", "v_proj")], xcal, G_, 20,
+                                      CAL_SUB)
+        out.update(zip(("q_proj", "k_proj", "v_proj"), mods))
+        _, mods, _ = L.norm_group_awq(ln_w, [layer_lin[n] for n in ("gate_proj", "up_proj")], xcal, G_, 20,
+                                      CAL_SUB)
+        out.update(zip(("gate_proj", "up_proj"), mods))
+        out["o_proj"] = L.quantize_linear(layer_lin["o_proj"], G_)
+        out["down_proj"] = L.quantize_linear(layer_lin["down_proj"], G_)
+        return out
+
+    qlayer = layer_awq()
+    # decode through a stack of LAYER_STACK layers x 7 linears (the AWQ-quantized layer first,
+    # then plainly packed ones): 536 MB of packed weights, so every launch reads HBM
+    stack = [{name: (m.packed, m.scales, m.zeros) for name, m in qlayer.items()}]
+    for _ in range(LAYER_STACK - 1):
+        stack.append({name: B.aq_quantize_pack(weight_bf16(n, k), G_) for name, n, k in synth.LAYER_LINEARS})
+    x_in = {name: acts_bf16(1, k, round(0.01 * k)) for name, n, k in synth.LAYER_LINEARS}
+    y_out = {name: torch.empty((1, n), dtype=torch.float32, device=dev) for name, n, k in synth.LAYER_LINEARS}
+
+    def layer_decode():
+        for lay in stack:
+            for name, _, _ in synth.LAYER_LINEARS:
+                B.aq_w4a16_gemv(x_in[name], *lay[name], G_, out=y_out[name])
+
+    side2 = torch.cuda.Stream()
+    side2.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side2):
+        layer_decode()
+    torch.cuda.current_stream().wait_stream(side2)
+    torch.cuda.synchronize()
+    layer_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(layer_graph):
+        layer_decode()
+    torch.cuda.synchronize()
     torch.cuda.synchronize()
 
-    events = {k: [] for k in ("pack", "gemv", "gemm", "absmean", "search", "fp4_gemv", "fp4_gemm")}
+    events = {k: [] for k in ("pack", "gemv", "gemm", "absmean", "search", "fp4_gemv", "fp4_gemm", "layer_awq",
+                              "layer_gemv")}
 
     def timed(name, record, fn):
         if record:
@@ -220,6 +274,8 @@ def main():
         timed("search", record, lambda: B.aq_awq_search(xsub, absmean_host, w_gate, G_, 20, ws_search))
         timed("fp4_gemv", record, lambda: B.aq_fp4_gemm(xf1, codes, bsc, ts, out=yf1))
         timed("fp4_gemm", record, lambda: B.aq_fp4_gemm(xf2, codes, bsc, ts, out=yf2, workspace=ws_fp4))
+        timed("layer_awq", record, layer_awq)
+        timed("layer_gemv", record, layer_graph.replay)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -235,6 +291,7 @@ def main():
 
     ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in events.items()}
     ms["gemv"] /= N_COPIES
+    ms["layer_gemv"] /= LAYER_STACK
     gemv_b = gemv_bytes(1, N_, K_, G_)
     gemv_gbs = gemv_b / (ms["gemv"] * 1e-3) / 1e9
     gemm_flop = 2.0 * M_GEMM * N_ * K_
@@ -248,6 +305,10 @@ def main():
         "awq_search": {"ms": ms["search"], "TFLOP/s": search_flop / (ms["search"] * 1e-3) / 1e12},
         "fp4_gemv_m1": {"us": ms["fp4_gemv"] * 1e3,
                         "GB/s": fp4_bytes(1, FP4_N, FP4_K) / (ms["fp4_gemv"] * 1e-3) / 1e9},
+        "layer_awq": {"ms": ms["layer_awq"]},
+        "layer_gemv_m1": {"us": ms["layer_gemv"] * 1e3,
+                          "GB/s": sum(gemv_bytes(1, n, k, G_) for _, n, k in synth.LAYER_LINEARS)
+                          / (ms["layer_gemv"] * 1e-3) / 1e9},
         "fp4_gemm_m2048": {"us": ms["fp4_gemm"] * 1e3,
                            "TFLOP/s": 2.0 * FP4_M * FP4_N * FP4_K / (ms["fp4_gemm"] * 1e-3) / 1e12},
     }

@@ -2,7 +2,8 @@
 
 The compute lives in libaq.so (hand-written HIP kernels for gfx950 behind the C
 ABI of include/aq.h).  ``binding`` exposes the entry points to torch under the
-same names; ``synth`` holds the seeded synthetic inputs.  Importing this package
+same names; ``layer`` builds on it the quantized linear module and the
+norm-group AWQ apply step; ``synth`` holds the seeded synthetic inputs.  Importing this package
 does not load the library; the first binding call does, and fails loudly if it
 has not been built.
 """

@@ -115,11 +115,23 @@ __global__ __launch_bounds__(256) void w4a16_gemv_kernel(const uint16_t* X, cons
   issue(0);
   asm volatile("" ::: "memory");  // keep the first weight batch ahead of the X staging
   if constexpr (LDS_X) {
+    // up to XU 16-byte units per thread requested together, then converted (one
+    // activation round trip per XU units instead of one per unit); XU follows the
+    // units a thread has (M * K / 8 over 256 threads), so short single rows keep the
+    // plain one-unit loop
+    constexpr int XU = M * CPL < 6 ? M * CPL : 6;
     const int n8 = M * (K >> 3);
-    for (int i = threadIdx.x; i < n8; i += 256) {
-      const u32x4 t = reinterpret_cast<const u32x4*>(X)[i];
-      reinterpret_cast<u32x4*>(xpl)[i] = permute_pairs(t);
-      xsl[i] = sum8(t);
+    for (int i0 = threadIdx.x; i0 < n8; i0 += 256 * XU) {
+      u32x4 t[XU];
+#pragma unroll
+      for (int u = 0; u < XU; ++u)
+        if (i0 + 256 * u < n8) t[u] = reinterpret_cast<const u32x4*>(X)[i0 + 256 * u];
+#pragma unroll
+      for (int u = 0; u < XU; ++u)
+        if (i0 + 256 * u < n8) {
+          reinterpret_cast<u32x4*>(xpl)[i0 + 256 * u] = permute_pairs(t[u]);
+          xsl[i0 + 256 * u] = sum8(t[u]);
+        }
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are complete
     __builtin_amdgcn_s_barrier();
@@ -205,6 +217,10 @@ hipError_t launch_m(const uint16_t* X, const uint8_t* P, const float* S, const u
   const int nchunk = K >> 5;
   if (lds_x) {
     if (nchunk <= 64) return launch_cfg<M, R, 1, true>(X, P, S, Z, Y, N, K, gshift, stream);
+    // long rows (K > 4096, e.g. a down projection): one row per wave and up to six
+    // chunks per lane in flight, so the whole row is requested at once and twice as
+    // many waves share the HBM latency
+    if (M <= 4 && nchunk > 128) return launch_cfg<M, 1, 6, true>(X, P, S, Z, Y, N, K, gshift, stream);
     return launch_cfg<M, R, 2, true>(X, P, S, Z, Y, N, K, gshift, stream);
   }
   if (nchunk <= 64) return launch_cfg<M, R, 1, false>(X, P, S, Z, Y, N, K, gshift, stream);

@@ -1,0 +1,128 @@
+"""Quantized linear module and the norm-group AWQ apply step, on top of the binding.
+
+Every computation is a libaq call (pack, abs-mean, alpha search, GEMV / GEMM);
+this module only arranges tensors and swaps modules.
+
+  * ``W4A16Linear``: the drop-in replacement of an ``nn.Linear`` holding the
+    packed INT4 triple; its forward is the W4A16 GEMV (M <= 16 rows) or GEMM
+    ("Lance-Quant", zingnex.cn, "运行时替换与内存优化": linears replaced by
+    quantized linear modules; "模型量化指南", blog.yoooo.fun, "共同约定": the
+    quantized layer dequantizes in memory and equals the original layer with W
+    replaced by its dequantized value, and quantizing an already quantized
+    layer is refused).
+  * ``norm_group_awq``: AWQ for one normalisation and the linears consuming its
+    output ("Lance-Quant", "量化应用：网格搜索与分组策略": grid search of the
+    scale per norm and its consumers, the scale folded into the preceding
+    RMSNorm, group-wise INT4 packing).  The consumers are searched jointly:
+    their weights concatenated along N share one channel scale s, the norm
+    weight becomes w / s and each linear holds Q(W diag(s)).
+  * ``quantize_linear``: plain group-wise min-max packing for linears with no
+    norm in front of them (o_proj and down_proj follow a non-linearity, so no
+    scale can be folded; same page, after the fourth case).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import binding as B
+
+
+class W4A16Linear(torch.nn.Module):
+    """y = x W^T (+ bias) with W stored as group-wise INT4 (packed [N, K/2], S, z).
+
+    The input is cast to bf16 (the kernels' activation type); the output is fp32.
+    """
+
+    def __init__(self, packed: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor, group: int,
+                 bias: torch.Tensor | None = None):
+        super().__init__()
+        if packed.dim() != 2 or scales.shape != zeros.shape or scales.shape[0] != packed.shape[0]:
+            raise ValueError("packed [N, K/2], scales and zeros [N, K/group] expected")
+        self.group = int(group)
+        self.in_features = packed.shape[1] * 2
+        self.out_features = packed.shape[0]
+        if scales.shape[1] * self.group != self.in_features:
+            raise ValueError("scales must be [N, K/group]")
+        self.register_buffer("packed", packed.contiguous())
+        self.register_buffer("scales", scales.contiguous())
+        self.register_buffer("zeros", zeros.contiguous())
+        self.register_buffer("bias", None if bias is None else bias.detach().float().contiguous())
+        self._ws = None
+
+    @classmethod
+    def from_weight(cls, weight: torch.Tensor, group: int, chan_scale: torch.Tensor | None = None,
+                    bias: torch.Tensor | None = None) -> "W4A16Linear":
+        """Pack W [N, K] (fp32 or bf16, on the GPU), optionally scaled by chan_scale [K]."""
+        p, s, z = B.aq_quantize_pack(weight.detach().contiguous(), group, chan_scale)
+        return cls(p, s, z, group, bias)
+
+    def _workspace(self, m: int):
+        need = B.aq_w4a16_gemm_workspace(m, self.out_features, self.in_features, self.group)
+        if need == 0:
+            return torch.empty(0, dtype=torch.uint8, device=self.packed.device)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.packed.device)
+        return self._ws
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        if x.shape[-1] != self.in_features:
+            raise ValueError(f"expected {self.in_features} input features, got {x.shape[-1]}")
+        x2 = x.reshape(-1, self.in_features).to(torch.bfloat16).contiguous()
+        m = x2.shape[0]
+        if m <= 16:
+            y = B.aq_w4a16_gemv(x2, self.packed, self.scales, self.zeros, self.group)
+        else:
+            y = B.aq_w4a16_gemm(x2, self.packed, self.scales, self.zeros, self.group, workspace=self._workspace(m))
+        if self.bias is not None:
+            y = y + self.bias
+        return y.reshape(*x.shape[:-1], self.out_features)
+
+    def extra_repr(self) -> str:
+        return f"in_features={self.in_features}, out_features={self.out_features}, group={self.group}"
+
+
+def _weight_of(linear) -> torch.Tensor:
+    if isinstance(linear, W4A16Linear):
+        raise ValueError("layer is already quantized")
+    if not isinstance(linear, torch.nn.Linear):
+        raise TypeError(f"expected torch.nn.Linear, got {type(linear).__name__}")
+    return linear.weight.detach()
+
+
+def quantize_linear(linear: torch.nn.Linear, group: int) -> W4A16Linear:
+    """Plain group-wise min-max INT4 of one linear (no channel scale)."""
+    w = _weight_of(linear)
+    return W4A16Linear.from_weight(w.contiguous(), group, None, linear.bias)
+
+
+def norm_group_awq(norm_weight: torch.Tensor, linears, x_norm: torch.Tensor, group: int, n_grid: int = 20,
+                   search_tokens: int = 4096):
+    """AWQ of the linears consuming one RMSNorm's output.
+
+    x_norm: that norm's output over the calibration tokens [T, K] bf16 (all T
+    tokens give the abs-mean statistic; the first ``search_tokens`` score the
+    search).  Returns (folded fp32 norm weight [K], [W4A16Linear per linear],
+    search dict of aq_awq_search).
+    """
+    ws = [_weight_of(l) for l in linears]
+    if not ws:
+        raise ValueError("no linear to quantize")
+    k = ws[0].shape[1]
+    if any(w.shape[1] != k for w in ws) or any(w.dtype != ws[0].dtype for w in ws):
+        raise ValueError("the consumers of one norm must share K and the weight dtype")
+    if x_norm.dim() != 2 or x_norm.shape[1] != k:
+        raise ValueError(f"x_norm must be [T, {k}]")
+    t = x_norm.shape[0]
+    x = x_norm.to(torch.bfloat16).contiguous()
+    sum_abs = torch.zeros(k, dtype=torch.float64, device=x.device)
+    mean = torch.empty(k, dtype=torch.float32, device=x.device)
+    B.aq_act_absmean(x, sum_abs, t, mean)          # EINVAL (ValueError) for T == 0
+    w_cat = torch.cat(ws, dim=0).contiguous()
+    res = B.aq_awq_search(x[:search_tokens].contiguous(), mean.cpu(), w_cat, group, n_grid)
+    folded = norm_weight.detach().float() / res["best_scale"]
+    out, n0 = [], 0
+    for lin, w in zip(linears, ws):
+        n1 = n0 + w.shape[0]
+        out.append(W4A16Linear(res["packed"][n0:n1], res["scales"][n0:n1], res["zeros"][n0:n1], group, lin.bias))
+        n0 = n1
+    return folded, out, res
