@@ -12,6 +12,7 @@ group 64):
   absmean  aq_act_absmean over 65536 x 2048 calibration tokens   (AWQ statistic)
   search   aq_awq_search, 4096 tokens, 20 alphas, final pack     (AWQ search)
   fp4      aq_fp4_gemm at M = 1 and M = 2048 on W[14336, 4096]   (FP4 decode)
+           and aq_fp4_quantize of an fp32 W[14336, 4096]          (FP4 encode)
   layer    a whole Qwen2.5-3B decoder layer: norm-group AWQ of    (module-level path)
            q|k|v and gate|up (joint search, 65536-token abs-mean,
            4096-token search) plus plain packing of o and down;
@@ -183,6 +184,12 @@ def main():
     yf2 = torch.empty((FP4_M, FP4_N), dtype=torch.float32, device=dev)
     ws_gemm = torch.empty(B.aq_w4a16_gemm_workspace(M_GEMM, N_, K_, G_), dtype=torch.uint8, device=dev)
     ws_fp4 = torch.empty(B.aq_fp4_gemm_workspace(FP4_M, FP4_N, FP4_K), dtype=torch.uint8, device=dev)
+    # FP4 encoder input: an fp32 weight of the FP4 shape, and its preallocated outputs
+    w_fp4 = torch.randn((FP4_N, FP4_K), generator=gen, device=dev, dtype=torch.float32) * 0.02
+    enc_out = dict(codes=torch.empty((FP4_N, FP4_K // 2), dtype=torch.uint8, device=dev),
+                   block_scales=torch.empty((FP4_N, FP4_K // 16), dtype=torch.uint8, device=dev),
+                   tensor_scale=torch.empty(1, dtype=torch.float32, device=dev),
+                   workspace=torch.empty(B.aq_fp4_quantize_workspace(FP4_N, FP4_K), dtype=torch.uint8, device=dev))
     # a whole decoder layer: the seven linears as bf16 nn.Linear, RMSNorm weights, and its
     # quantized form (norm-group AWQ for q|k|v and gate|up, plain packing of o and down)
     layer_lin = {}
@@ -231,8 +238,8 @@ def main():
     torch.cuda.synchronize()
     torch.cuda.synchronize()
 
-    events = {k: [] for k in ("pack", "gemv", "gemm", "absmean", "search", "fp4_gemv", "fp4_gemm", "layer_awq",
-                              "layer_gemv")}
+    events = {k: [] for k in ("pack", "gemv", "gemm", "absmean", "search", "fp4_gemv", "fp4_gemm", "fp4_encode",
+                              "layer_awq", "layer_gemv")}
 
     def timed(name, record, fn):
         if record:
@@ -274,6 +281,7 @@ def main():
         timed("search", record, lambda: B.aq_awq_search(xsub, absmean_host, w_gate, G_, 20, ws_search))
         timed("fp4_gemv", record, lambda: B.aq_fp4_gemm(xf1, codes, bsc, ts, out=yf1))
         timed("fp4_gemm", record, lambda: B.aq_fp4_gemm(xf2, codes, bsc, ts, out=yf2, workspace=ws_fp4))
+        timed("fp4_encode", record, lambda: B.aq_fp4_quantize(w_fp4, **enc_out))
         timed("layer_awq", record, layer_awq)
         timed("layer_gemv", record, layer_graph.replay)
 
@@ -305,6 +313,9 @@ def main():
         "awq_search": {"ms": ms["search"], "TFLOP/s": search_flop / (ms["search"] * 1e-3) / 1e12},
         "fp4_gemv_m1": {"us": ms["fp4_gemv"] * 1e3,
                         "GB/s": fp4_bytes(1, FP4_N, FP4_K) / (ms["fp4_gemv"] * 1e-3) / 1e9},
+        "fp4_encode": {"us": ms["fp4_encode"] * 1e3,
+                       "GB/s": (4 * FP4_N * FP4_K + FP4_N * FP4_K // 2 + FP4_N * FP4_K // 16)
+                       / (ms["fp4_encode"] * 1e-3) / 1e9},
         "layer_awq": {"ms": ms["layer_awq"]},
         "layer_gemv_m1": {"us": ms["layer_gemv"] * 1e3,
                           "GB/s": sum(gemv_bytes(1, n, k, G_) for _, n, k in synth.LAYER_LINEARS)

@@ -189,6 +189,33 @@ aq_status aq_fp4_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_t* co
                       float tensor_scale, int64_t N, float* Y, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/*
+ * FP4 encoder: W [N, K] (fp32 or bf16) -> the codes, block scales and tensor
+ * scale that aq_fp4_gemm decodes.
+ * Source: "Lance-Quant" (zingnex.cn), grid-search / grouping section (nvfp4_apply
+ * packs E2M1 codes with an FP8 E4M3 scale per 16-element block);
+ * "Quantization：模型量化" (xingyuwang.me), section 12 (E4M3 = 1 + 4 + 3 bits).
+ *
+ *   ts   = fl32(max |W| / 2688)              (2688 = 6 * 448); 1 if W is all zero
+ *   b    = E4M3(fl32(max_block |w| / fl32(6 ts)))   nearest, ties to the even
+ *          code, saturating at 448; one byte per 16 consecutive k of a row
+ *   code = nearest E2M1 magnitude of fl32(|w| / fl32(e4m3(b) ts)), ties to the
+ *          even code, saturating at 6 (0 when the block scale is 0); bit 3 set
+ *          for negative w with a non-zero magnitude
+ * Outputs: codes [N, K/2] uint8 (k even in the low nibble), block_scales
+ * [N, K/16] uint8, tensor_scale: one fp32 on the device.  Every fp32 operation
+ * is an IEEE operation in the order above (deterministic, bit-reproducible).
+ * workspace: device memory of at least aq_fp4_quantize_workspace(N, K) bytes
+ * (the partial maxima), 4-byte aligned, used only during the call.
+ * Errors: EINVAL for w_dtype not AQ_F32 / AQ_BF16, N < 0, K <= 0 or K % 16,
+ *         K or N >= 2^30, a small workspace, NULL / misaligned pointers (W 16,
+ *         codes 8, tensor_scale and workspace 4 bytes).  Inputs must be finite.
+ */
+size_t aq_fp4_quantize_workspace(int64_t N, int64_t K);
+aq_status aq_fp4_quantize(const void* W, int32_t w_dtype, int64_t N, int64_t K, uint8_t* codes,
+                          uint8_t* block_scales, float* tensor_scale, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* Thread-local text for the last non-OK status of this thread ("" if none). */
 const char* aq_last_error(void);
 

@@ -31,7 +31,7 @@ def _declared():
 def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("aq_quantize_pack", "aq_w4a16_gemv", "aq_w4a16_gemm", "aq_act_absmean", "aq_awq_search",
-              "aq_fp4_gemm", "aq_last_error"):
+              "aq_fp4_gemm", "aq_fp4_quantize", "aq_last_error"):
         assert n in names
     assert set(names) == set(_lib.SIGNATURES), "binding prototypes must mirror the header"
 
@@ -167,6 +167,25 @@ def test_fp4_einval(lib):
     assert _fp4(lib, M=17, N=1 << 22) == _lib.AQ_EINVAL
 
 
+def _fp4q(lib, W=FAKE, dt=0, N=8, K=64, C=FAKE, B=FAKE, T=FAKE, ws=FAKE, wsb=None):
+    wsb = lib.aq_fp4_quantize_workspace(N, K) if wsb is None else wsb
+    return lib.aq_fp4_quantize(W, dt, N, K, C, B, T, ws, wsb, None)
+
+
+def test_fp4_quantize_einval(lib):
+    assert lib.aq_fp4_quantize_workspace(8, 64) >= 4
+    assert lib.aq_fp4_quantize_workspace(8, 24) == 0
+    assert _fp4q(lib, K=24) == _lib.AQ_EINVAL        # K % 16
+    assert _fp4q(lib, K=0) == _lib.AQ_EINVAL
+    assert _fp4q(lib, dt=7) == _lib.AQ_EINVAL
+    assert _fp4q(lib, N=-1) == _lib.AQ_EINVAL
+    assert _fp4q(lib, W=FAKE + 8) == _lib.AQ_EINVAL  # W must be 16-byte aligned
+    assert _fp4q(lib, C=FAKE + 4) == _lib.AQ_EINVAL  # codes 8-byte aligned
+    assert _fp4q(lib, T=None) == _lib.AQ_EINVAL
+    assert _fp4q(lib, wsb=0) == _lib.AQ_EINVAL       # workspace too small
+    assert "workspace" in _lib.last_error()
+
+
 def test_injected_runtime_failure(lib, monkeypatch):
     """AQ_FAULT_INJECT=launch: valid arguments, no GPU touched, status 2 (runtime failure)."""
     monkeypatch.setenv("AQ_FAULT_INJECT", "launch")
@@ -175,6 +194,7 @@ def test_injected_runtime_failure(lib, monkeypatch):
     assert _prod(lib, "aq_w4a16_gemv") == _lib.AQ_ERUNTIME
     assert _prod(lib, "aq_w4a16_gemm", M=128) == _lib.AQ_ERUNTIME
     assert _fp4(lib) == _lib.AQ_ERUNTIME
+    assert _fp4q(lib) == _lib.AQ_ERUNTIME
     ws = lib.aq_act_absmean_workspace(64, 64)
     assert lib.aq_act_absmean(FAKE, 64, 64, FAKE, None, 64, FAKE, ws, None) == _lib.AQ_ERUNTIME
     # validation still wins over the injected fault

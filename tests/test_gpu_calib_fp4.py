@@ -201,3 +201,84 @@ def test_fp4_exact_case(m):
     step(f"aq_fp4_gemm exact M={m}")
     y = host(B.aq_fp4_gemm(dev_bf16(synth.f32_to_bf16_bits(x)), dev(c), dev(b), 1.0))
     assert (y.astype(np.float64) == fp4.forward(x, c, b, np.float32(1.0))).all()
+
+
+# ---------------------------------------------------------------- FP4 encoder
+
+def _encode_gpu(w_dev):
+    c, b, ts = B.aq_fp4_quantize(w_dev)
+    return host(c), host(b), host(ts)[0]
+
+
+def _assert_encoding_equal(got, want, what):
+    (c, b, ts), (c0, b0, ts0) = got, want
+    bad_c = int(np.count_nonzero(c != c0))
+    bad_b = int(np.count_nonzero(b != b0))
+    print(f"[gpu] {what}: ts {ts!r} vs {np.float32(ts0)!r}, mismatching code bytes {bad_c}, scale bytes {bad_b}",
+          flush=True)
+    assert np.float32(ts).view(np.uint32) == np.float32(ts0).view(np.uint32)
+    assert bad_c == 0 and bad_b == 0
+
+
+@pytest.mark.parametrize("n,k", [(14336, 4096), (4096, 14336)])
+def test_fp4_quantize_mlp_shapes_bit_exact(n, k):
+    """aq_fp4_quantize reproduces the oracle encoder byte for byte on the 7B-like MLP shapes."""
+    w = synth.fp4_weight_f32(5, n, k)
+    step(f"aq_fp4_quantize fp32 [{n},{k}]")
+    _assert_encoding_equal(_encode_gpu(dev(w)), fp4.encode(w), f"fp4 encode [{n},{k}]")
+
+
+def _edge_weight():
+    """ts = 1 exactly (max |w| = 2688) and blocks built to land on every rounding decision:
+    E4M3 ties (block amax / 6 halfway between two codes, normal and subnormal), E4M3
+    saturation, E2M1 midpoints of both parities, a value past 6, signed zeros, a zero block."""
+    rows = []
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25, -0.75, -1.25, -5.0, 6.0, -6.0, -0.0, 0.0]
+    # block amax 6.375: target 1.0625, halfway between E4M3 1.0 (even code) and 1.125 -> scale
+    # 1, and 6.375 itself saturates to the largest E2M1 code
+    rows.append([6.375] + mids)
+    # block amax 6 * 2.5 / 512: target 2.5 * 2^-9 (subnormal tie) -> code 2, scale 2^-8
+    sub = 6 * 2.5 / 512
+    rows.append([sub] + [v * 2.0 ** -8 for v in mids])
+    # block amax 2688: target 448 -> 0x7E, scale 448 (midpoints up to 5: nothing above 2688)
+    small = [v for v in mids if abs(v) <= 5.0]
+    rows.append([2688.0] + [v * 448 for v in small] + [0.0] * (15 - len(small)))
+    # block amax 6 * 432: target 432, halfway between 416 and 448 -> 448 (even code)
+    rows.append([6 * 432.0] + [v * 448 for v in small] + [0.0] * (15 - len(small)))
+    # all-zero block and a block of tiny values
+    rows.append([0.0] * 16)
+    rows.append([1e-30 * (i + 1) * (-1) ** i for i in range(16)])
+    rng = np.random.default_rng(9)
+    w = np.array(rows, dtype=np.float32).reshape(-1)
+    w = np.concatenate([w, (rng.standard_normal(16 * 58) * 3).astype(np.float32)])
+    return w.reshape(4, -1)
+
+
+def test_fp4_quantize_rounding_edges_bit_exact():
+    w = _edge_weight()
+    step(f"aq_fp4_quantize edge cases {w.shape}")
+    want = fp4.encode(w)
+    assert np.float32(want[2]) == np.float32(1.0)
+    _assert_encoding_equal(_encode_gpu(dev(w)), want, "fp4 encode edges")
+
+
+def test_fp4_quantize_bf16_input_and_all_zero():
+    wb = synth.f32_to_bf16_bits(synth.fp4_weight_f32(6, 256, 512))
+    step("aq_fp4_quantize bf16 [256,512]")
+    _assert_encoding_equal(_encode_gpu(dev_bf16(wb)), fp4.encode(synth.bf16_bits_to_f32(wb)), "fp4 encode bf16")
+    z = np.zeros((8, 64), np.float32)
+    step("aq_fp4_quantize all-zero [8,64]")
+    c, b, ts = _encode_gpu(dev(z))
+    assert ts == np.float32(1.0) and not c.any() and not b.any()
+
+
+def test_fp4_quantize_then_decode_product():
+    """Encode on the GPU, then run the FP4 GEMV / GEMM on its output: equal to the oracle's
+    decode of the oracle's encoding (the same bytes), within the product tolerance."""
+    w = synth.fp4_weight_f32(7, 1024, 2048)
+    xb = synth.layer_activations_bf16(7, 64, 2048)
+    step("aq_fp4_quantize + aq_fp4_gemm [1024,2048] M=64")
+    c, b, ts = B.aq_fp4_quantize(dev(w))
+    y = host(B.aq_fp4_gemm(dev_bf16(xb), c, b, float(host(ts)[0])))
+    c0, b0, ts0 = fp4.encode(w)
+    check_close(y, fp4.forward(synth.bf16_bits_to_f32(xb), c0, b0, ts0), "fp4 encode + gemm")

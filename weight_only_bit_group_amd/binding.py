@@ -208,3 +208,31 @@ def aq_fp4_gemm(X, codes, block_scales, tensor_scale: float, out=None, workspace
                          n, out.data_ptr(), _ptr(ws), nbytes, _stream(X))
     check(st, "aq_fp4_gemm")
     return out
+
+
+def aq_fp4_quantize_workspace(N: int, K: int) -> int:
+    return int(_lib.load().aq_fp4_quantize_workspace(N, K))
+
+
+def aq_fp4_quantize(W, *, codes=None, block_scales=None, tensor_scale=None, workspace=None):
+    """(codes [N, K/2] u8, block_scales [N, K/16] u8, tensor_scale [1] f32) of W[N, K] (f32 or bf16), on the device."""
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D [N, K]")
+    _need(W, "W", W.dtype)
+    n, k = W.shape
+    if k % 16:
+        raise ValueError("K must be a multiple of 16")
+    dev = W.device
+    if codes is None:
+        codes = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
+    if block_scales is None:
+        block_scales = torch.empty((n, k // 16), dtype=torch.uint8, device=dev)
+    if tensor_scale is None:
+        tensor_scale = torch.empty(1, dtype=torch.float32, device=dev)
+    need = aq_fp4_quantize_workspace(n, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
+    st = _lib.load().aq_fp4_quantize(W.data_ptr(), _wdtype(W), n, k, codes.data_ptr(), block_scales.data_ptr(),
+                                     tensor_scale.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(W))
+    check(st, "aq_fp4_quantize")
+    return codes, block_scales, tensor_scale

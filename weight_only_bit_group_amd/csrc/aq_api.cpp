@@ -113,6 +113,33 @@ aq_status aq_quantize_pack(const void* W, int32_t w_dtype, int64_t N, int64_t K,
                         "aq_quantize_pack");
 }
 
+size_t aq_fp4_quantize_workspace(int64_t N, int64_t K) {
+  if (N < 0 || K <= 0 || K % 16 || N >= kDimLimit || K >= kDimLimit) return 0;
+  return aq::fp4_quantize_workspace_bytes(N, K);
+}
+
+aq_status aq_fp4_quantize(const void* W, int32_t w_dtype, int64_t N, int64_t K, uint8_t* codes,
+                          uint8_t* block_scales, float* tensor_scale, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  AQ_REQUIRE(w_dtype == AQ_F32 || w_dtype == AQ_BF16, "aq_fp4_quantize: w_dtype must be AQ_F32 or AQ_BF16 (got %d)",
+             w_dtype);
+  AQ_REQUIRE(N >= 0 && N < kDimLimit, "aq_fp4_quantize: N out of range (%lld)", (long long)N);
+  AQ_REQUIRE(K > 0 && K < kDimLimit && K % 16 == 0, "aq_fp4_quantize: K must be a positive multiple of 16 (got %lld)",
+             (long long)K);
+  AQ_PTR(W, 16, "W");
+  AQ_PTR(codes, 8, "codes");
+  AQ_PTR(block_scales, 1, "block_scales");
+  AQ_PTR(tensor_scale, 4, "tensor_scale");
+  AQ_PTR(workspace, 4, "workspace");
+  AQ_REQUIRE(workspace_bytes >= aq_fp4_quantize_workspace(N, K),
+             "aq_fp4_quantize: workspace too small (%zu < %zu bytes)", workspace_bytes,
+             aq_fp4_quantize_workspace(N, K));
+  if (fault_injected()) return fail(AQ_ERUNTIME, "aq_fp4_quantize: injected launch failure");
+  return runtime_status(aq::launch_fp4_quantize(W, w_dtype == AQ_BF16, N, K, codes, block_scales, tensor_scale,
+                                                static_cast<float*>(workspace), (hipStream_t)stream),
+                        "aq_fp4_quantize");
+}
+
 static aq_status check_product(const char* fn, const uint16_t* X, int64_t M, int64_t K, const uint8_t* packed,
                                const float* scales, const uint8_t* zeros, int64_t N, int32_t group, float* Y) {
   AQ_REQUIRE(valid_group(group), "%s: group must be 32, 64 or 128 (got %d)", fn, group);

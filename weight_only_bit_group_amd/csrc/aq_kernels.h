@@ -22,6 +22,10 @@ hipError_t launch_fp4_gemv(const uint16_t* X, int M, int K, const uint8_t* codes
                            int N, float* Y, hipStream_t stream);
 hipError_t launch_fp4_gemm(const uint16_t* X, int M, int K, const uint8_t* codes, const uint8_t* bscale, float ts,
                            int N, float* Y, uint16_t* staged, hipStream_t stream);
+size_t fp4_quantize_workspace_bytes(int64_t N, int64_t K);
+// ts: one fp32 on the device (written); partial: fp4_quantize_workspace_bytes of device memory
+hipError_t launch_fp4_quantize(const void* W, bool w_bf16, int64_t N, int64_t K, uint8_t* codes, uint8_t* bscale,
+                               float* ts, float* partial, hipStream_t stream);
 int sumsq_gemm_blocks(int M, int N);
 hipError_t launch_sumsq_gemm(const uint16_t* X, int M, int K, const uint16_t* E, int N, double* partial,
                              hipStream_t stream);
