@@ -5,6 +5,7 @@ like the gate projection of a Qwen2.5-3B decoder layer (K = 2048, N = 11008,
 group 64):
 
   pack     aq_quantize_pack of the bf16 weight                   (quantize + pack)
+           and its symmetric variant aq_quantize_pack_sym
   gemv     aq_w4a16_gemv at M = 1, once on each of 40 distinct   (decode; 40 copies =
            packed weight copies, so every launch reads HBM         520 MB > the 256 MB MALL)
   gemm     aq_w4a16_gemm at M = 4096                             (prefill, bf16 MFMA; staged
@@ -238,7 +239,7 @@ def main():
     torch.cuda.synchronize()
     torch.cuda.synchronize()
 
-    events = {k: [] for k in ("pack", "gemv", "gemm", "absmean", "search", "fp4_gemv", "fp4_gemm", "fp4_encode",
+    events = {k: [] for k in ("pack", "pack_sym", "gemv", "gemm", "absmean", "search", "fp4_gemv", "fp4_gemm", "fp4_encode",
                               "layer_awq", "layer_gemv")}
 
     def timed(name, record, fn):
@@ -273,6 +274,8 @@ def main():
 
     def step(record):
         timed("pack", record, lambda: B.aq_quantize_pack(w_gate, G_, packed=pk[0], scales=pk[1], zeros=pk[2]))
+        timed("pack_sym", record, lambda: B.aq_quantize_pack(w_gate, G_, packed=pk[0], scales=pk[1], zeros=pk[2],
+                                                             sym=True))
         timed("gemv", record, gemv_graph.replay)
         p, s, z = copies[0]
         timed("gemm", record, lambda: B.aq_w4a16_gemm(xg, p, s, z, G_, out=yg, workspace=ws_gemm))
@@ -307,6 +310,7 @@ def main():
     search_flop = 20 * 2.0 * CAL_SUB * N_ * K_
     rows = {
         "pack": {"us": ms["pack"] * 1e3, "GB/s": pack_bytes(N_, K_, G_) / (ms["pack"] * 1e-3) / 1e9},
+        "pack_sym": {"us": ms["pack_sym"] * 1e3, "GB/s": pack_bytes(N_, K_, G_) / (ms["pack_sym"] * 1e-3) / 1e9},
         "gemv_m1": {"us": ms["gemv"] * 1e3, "GB/s": gemv_gbs},
         "gemm_m4096": {"us": ms["gemm"] * 1e3, "TFLOP/s": gemm_tf},
         "absmean": {"us": ms["absmean"] * 1e3, "GB/s": 2.0 * CAL_T * K_ / (ms["absmean"] * 1e-3) / 1e9},

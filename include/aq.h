@@ -71,6 +71,23 @@ aq_status aq_quantize_pack(const void* W, int32_t w_dtype, int64_t N, int64_t K,
                            void* stream);
 
 /*
+ * Group-wise symmetric INT4 quantization and packing (the same packed format).
+ * Source: "Quantization：模型量化" (xingyuwang.me), section 2 (symmetric
+ * quantization: a symmetric integer range with zero mapped to integer zero,
+ * q = round(x/s), dequantization q s, clipping to the range) and section 3.
+ *
+ * For every row n and group j of g consecutive k (v as above):
+ *   S = fl32(max |v| / 7),  q_k = clamp(rne(fl32(v_k / S)), -7, 7),
+ *   stored code q_k + 8 and zero point 8, so (code - z) S = q S and
+ *   aq_w4a16_gemv / aq_w4a16_gemm decode it unchanged; an all-zero group stores
+ *   S = 0 and codes 8.
+ * Arguments, layout and errors as aq_quantize_pack.
+ */
+aq_status aq_quantize_pack_sym(const void* W, int32_t w_dtype, int64_t N, int64_t K, int32_t group,
+                               const float* chan_scale, uint8_t* packed, float* scales, uint8_t* zeros,
+                               void* stream);
+
+/*
  * W4A16 decode GEMV, 1 <= M <= 16 activation rows.  VALU kernel, HBM-bound.
  * Source: "模型量化指南" (blog.yoooo.fun), common conventions (the packed linear
  * dequantizes in memory and equals the original layer with W replaced by its

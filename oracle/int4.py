@@ -106,6 +106,42 @@ def quantize_pack(w, group: int, chan_scale=None):
     return pack_nibbles(q), s, z
 
 
+# ---- symmetric variant --------------------------------------------------------
+# "Quantization：模型量化" (xingyuwang.me), section 2, symmetric quantization: a
+# symmetric integer range with zero mapped to integer zero, q = round(x / s),
+# x_hat = q s (the page's INT8 example uses -127 .. 127), then clipping to the
+# integer range.  Readings (listed in the design notes): the 4-bit range is
+# -7 .. 7 with s = fl32(max |v| / 7) per group; the code is stored offset by 8
+# (1 .. 15) with a zero point of 8 for every group, so (code - z) S = q s and the
+# asymmetric decode applies unchanged; an all-zero group stores S = 0, codes 8.
+SYM_QMAX = 7
+SYM_ZERO = 8
+
+
+def quantize_codes_sym(w, group: int, chan_scale=None):
+    """Stored codes [N, K] (uint8, q + 8 with q in -7..7), S [N, K/g] fp32, z [N, K/g] (all 8)."""
+    w = _as_f32(w)
+    n, k = w.shape
+    if k % group:
+        raise ValueError("K must be a multiple of the group size")
+    v = (w * _as_f32(chan_scale)[None, :]).astype(np.float32) if chan_scale is not None else w
+    vg = v.reshape(n, k // group, group)
+    amax = np.abs(vg).max(axis=-1)                                   # exact
+    s = (amax / np.float32(SYM_QMAX)).astype(np.float32)             # fl32(max|v| / 7)
+    degenerate = (s == 0)[..., None]
+    safe = np.where(degenerate, np.float32(1), s[..., None]).astype(np.float32)
+    q = np.clip(np.rint(vg / safe), -SYM_QMAX, SYM_QMAX)               # rne(fl32(v / S)), clipped
+    q = np.where(degenerate, 0, q) + SYM_ZERO
+    z = np.full(s.shape, SYM_ZERO, dtype=np.uint8)
+    return q.astype(np.uint8).reshape(n, k), s, z
+
+
+def quantize_pack_sym(w, group: int, chan_scale=None):
+    """(packed [N, K/2] uint8, S [N, K/g] fp32, z [N, K/g] uint8 = 8) of the symmetric variant."""
+    q, s, z = quantize_codes_sym(w, group, chan_scale)
+    return pack_nibbles(q), s, z
+
+
 def dequantize(packed, scales, zeros, group: int) -> np.ndarray:
     """W_hat[N, K] = (q - z) * S in fp64 (exact: a 5-bit integer times an fp32 value)."""
     q = unpack_nibbles(packed).astype(np.float64)

@@ -44,10 +44,10 @@ def test_library_exports_every_declared_symbol(lib):
         assert re.search(rf"\bT {name}\b", out), name
 
 
-def _qp(lib, **kw):
+def _qp(lib, fn="aq_quantize_pack", **kw):
     a = dict(W=FAKE, dt=1, N=16, K=128, g=64, s=None, p=FAKE, sc=FAKE, z=FAKE)
     a.update(kw)
-    return lib.aq_quantize_pack(a["W"], a["dt"], a["N"], a["K"], a["g"], a["s"], a["p"], a["sc"], a["z"], None)
+    return getattr(lib, fn)(a["W"], a["dt"], a["N"], a["K"], a["g"], a["s"], a["p"], a["sc"], a["z"], None)
 
 
 @pytest.mark.parametrize("kw,frag", [
@@ -56,8 +56,9 @@ def _qp(lib, **kw):
     (dict(p=None), "packed"), (dict(s=FAKE_ODD), "chan_scale"), (dict(K=1 << 31), "K"),
 ])
 def test_quantize_pack_einval(lib, kw, frag):
-    assert _qp(lib, **kw) == _lib.AQ_EINVAL
-    assert frag in _lib.last_error()
+    for fn in ("aq_quantize_pack", "aq_quantize_pack_sym"):
+        assert _qp(lib, fn, **kw) == _lib.AQ_EINVAL
+        assert frag in _lib.last_error()
 
 
 def _prod(lib, fn, **kw):
@@ -195,6 +196,7 @@ def test_injected_runtime_failure(lib, monkeypatch):
     assert _prod(lib, "aq_w4a16_gemm", M=128) == _lib.AQ_ERUNTIME
     assert _fp4(lib) == _lib.AQ_ERUNTIME
     assert _fp4q(lib) == _lib.AQ_ERUNTIME
+    assert _qp(lib, "aq_quantize_pack_sym") == _lib.AQ_ERUNTIME
     ws = lib.aq_act_absmean_workspace(64, 64)
     assert lib.aq_act_absmean(FAKE, 64, 64, FAKE, None, 64, FAKE, ws, None) == _lib.AQ_ERUNTIME
     # validation still wins over the injected fault

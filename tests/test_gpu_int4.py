@@ -275,3 +275,36 @@ def test_gemv_batch_in_a_hip_graph():
         torch.cuda.synchronize()
     check_close(eager[0], int4.forward(synth.bf16_bits_to_f32(xb), *int4.quantize_pack(
         synth.bf16_bits_to_f32(ws[0]), 64), 64), "graph gemv o_proj")
+
+
+# ---------------------------------------------------------------- symmetric variant
+
+@pytest.mark.parametrize("g", [32, 64, 128])
+def test_pack_sym_decoder_layer_bit_exact(g):
+    """aq_quantize_pack_sym: codes, S and z bit-exact against the oracle on the layer's linears
+    (bf16) and on fp32 weights with an AWQ channel scale and all-zero groups."""
+    for name in ("q_proj", "down_proj"):
+        wb = synth.layer_weight_bf16(3, name)
+        step(f"aq_quantize_pack_sym {name} bf16 g={g}")
+        got = tuple(host(t) for t in B.aq_quantize_pack(dev_bf16(wb), g, sym=True))
+        _assert_pack_equal(got, int4.quantize_pack_sym(synth.bf16_bits_to_f32(wb), g), f"sym pack {name} g={g}")
+    rng = np.random.default_rng(g)
+    w = (rng.standard_normal((96, 512)) * 0.02).astype(np.float32)
+    w[5, :g] = 0.0
+    s = rng.uniform(0.25, 4.0, 512).astype(np.float32)
+    step(f"aq_quantize_pack_sym fp32 + channel scale g={g}")
+    got = tuple(host(t) for t in B.aq_quantize_pack(dev(w), g, dev(s), sym=True))
+    _assert_pack_equal(got, int4.quantize_pack_sym(w, g, s), f"sym pack fp32 scaled g={g}")
+
+
+@pytest.mark.parametrize("m", [1, 16, 300])
+def test_sym_packs_through_gemv_and_gemm(m):
+    """The symmetric packs decode with the unchanged GEMV (M <= 16) / GEMM: within tolerance of
+    the oracle's forward on the same triple."""
+    wb = synth.layer_weight_bf16(4, "gate_proj")
+    p, s, z = int4.quantize_pack_sym(synth.bf16_bits_to_f32(wb), 64)
+    xb = synth.layer_activations_bf16(4, m, 2048)
+    step(f"sym gate_proj forward M={m}")
+    fn = B.aq_w4a16_gemv if m <= 16 else B.aq_w4a16_gemm
+    y = host(fn(dev_bf16(xb), dev(p), dev(s), dev(z), 64))
+    check_close(y, int4.forward(synth.bf16_bits_to_f32(xb), p, s, z, 64), f"sym forward M={m}")

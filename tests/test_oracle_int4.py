@@ -242,3 +242,54 @@ def test_golden_regression():
     assert packed.tobytes().hex() == gold["packed_hex"]
     assert s.view(np.uint32).tolist() == gold["scales_bits"]
     assert z.tolist() == gold["zeros"]
+
+
+# ---------------------------------------------------------------- symmetric variant
+
+@pytest.mark.parametrize("g", [32, 64, 128])
+def test_symmetric_nearest_grid_point_brute_force(g):
+    """Symmetric INT4: S is the fp32 value nearest to max|v| / 7; every stored code is q + 8
+    with q the nearest integer (ties even) to fl32(v / S) among -7 .. 7 (brute force over all
+    15 levels); z = 8 everywhere; an all-zero group stores S = 0 and codes 8."""
+    rng = np.random.default_rng(31 + g)
+    w = _adversarial_groups(rng, g, 24)
+    w[4] = 0.0                                                     # an all-zero group
+    q, s, z = int4.quantize_codes_sym(w, g)
+    assert (z == 8).all()
+    for r in range(w.shape[0]):
+        vals = w[r]
+        amax = max(abs(float(x)) for x in vals)
+        S = float(s[r, 0])
+        if amax == 0:
+            assert S == 0 and (q[r] == 8).all()
+            continue
+        exact = Fraction(amax) / 7
+        cand = [np.float32(S), np.nextafter(np.float32(S), np.float32(np.inf)),
+                np.nextafter(np.float32(S), np.float32(-np.inf))]
+        assert abs(Fraction(float(cand[0])) - exact) <= min(abs(Fraction(float(c)) - exact) for c in cand[1:])
+        for kk in range(g):
+            t = Fraction(float(np.float32(vals[kk] / np.float32(S))))
+            target = _rne_fraction(t)
+            best = min(range(-7, 8), key=lambda c: (abs(c - target), c))
+            assert int(q[r, kk]) == best + 8
+
+
+def test_symmetric_zero_is_exact_and_codes_are_odd():
+    """Zero maps to integer zero (code 8, dequantized exactly 0); negating the weights negates
+    every q (stored code 16 - code) with the same S; the element of largest magnitude gets
+    +-7; the reconstruction error is at most S/2 (plus the fp32 rounding of v / S)."""
+    rng = np.random.default_rng(7)
+    w = (rng.standard_normal((16, 256)) * 0.02).astype(np.float32)
+    w[:, ::17] = 0.0
+    q, s, z = int4.quantize_codes_sym(w, 64)
+    qn, sn, _ = int4.quantize_codes_sym(-w, 64)
+    assert (q[w == 0] == 8).all()
+    assert np.array_equal(sn.view(np.uint32), s.view(np.uint32))
+    assert np.array_equal(qn.astype(int), 16 - q.astype(int))
+    wg = np.abs(w).reshape(16, 4, 64)
+    qg = q.reshape(16, 4, 64).astype(int) - 8
+    arg = wg.argmax(axis=-1)
+    assert (np.abs(np.take_along_axis(qg, arg[..., None], -1)) == 7).all()
+    what = int4.dequantize(*int4.quantize_pack_sym(w, 64), 64)
+    bound = np.repeat(s.astype(np.float64), 64, axis=1) * (0.5 + 2.0 ** -20)
+    assert (np.abs(what - w) <= bound).all()

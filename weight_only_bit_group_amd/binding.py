@@ -57,8 +57,11 @@ def _packed_outputs(w_like: torch.Tensor, n: int, k: int, group: int, packed, sc
 
 
 def aq_quantize_pack(W: torch.Tensor, group: int, chan_scale: torch.Tensor | None = None, *,
-                     packed=None, scales=None, zeros=None):
-    """(packed [N, K/2] u8, scales [N, K/g] f32, zeros [N, K/g] u8) of W[N, K] (f32 or bf16)."""
+                     packed=None, scales=None, zeros=None, sym: bool = False):
+    """(packed [N, K/2] u8, scales [N, K/g] f32, zeros [N, K/g] u8) of W[N, K] (f32 or bf16).
+
+    sym=True calls aq_quantize_pack_sym (symmetric codes, zero point 8).
+    """
     if W.dim() != 2:
         raise ValueError("W must be 2-D [N, K]")
     _need(W, "W", W.dtype)
@@ -68,9 +71,10 @@ def aq_quantize_pack(W: torch.Tensor, group: int, chan_scale: torch.Tensor | Non
     if chan_scale is not None:
         _need(chan_scale, "chan_scale", torch.float32, 1)
     packed, scales, zeros = _packed_outputs(W, n, k, group, packed, scales, zeros)
-    st = _lib.load().aq_quantize_pack(W.data_ptr(), _wdtype(W), n, k, group, _ptr(chan_scale), packed.data_ptr(),
-                                      scales.data_ptr(), zeros.data_ptr(), _stream(W))
-    check(st, "aq_quantize_pack")
+    fn = "aq_quantize_pack_sym" if sym else "aq_quantize_pack"
+    st = getattr(_lib.load(), fn)(W.data_ptr(), _wdtype(W), n, k, group, _ptr(chan_scale), packed.data_ptr(),
+                                  scales.data_ptr(), zeros.data_ptr(), _stream(W))
+    check(st, fn)
     return packed, scales, zeros
 
 

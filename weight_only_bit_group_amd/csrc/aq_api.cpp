@@ -93,24 +93,38 @@ extern "C" {
 
 const char* aq_last_error(void) { return g_last_error.c_str(); }
 
-aq_status aq_quantize_pack(const void* W, int32_t w_dtype, int64_t N, int64_t K, int32_t group,
-                           const float* chan_scale, uint8_t* packed, float* scales, uint8_t* zeros,
-                           void* stream) {
-  AQ_REQUIRE(w_dtype == AQ_F32 || w_dtype == AQ_BF16, "w_dtype must be AQ_F32 or AQ_BF16 (got %d)", w_dtype);
-  AQ_REQUIRE(valid_group(group), "group must be 32, 64 or 128 (got %d)", group);
-  AQ_REQUIRE(N >= 0 && N < kDimLimit, "N out of range (%lld)", (long long)N);
-  AQ_REQUIRE(K > 0 && K < kDimLimit, "K out of range (%lld)", (long long)K);
-  AQ_REQUIRE(K % group == 0, "K (%lld) must be a multiple of group (%d)", (long long)K, group);
+static aq_status quantize_pack_common(const char* fn, bool sym, const void* W, int32_t w_dtype, int64_t N,
+                                      int64_t K, int32_t group, const float* chan_scale, uint8_t* packed,
+                                      float* scales, uint8_t* zeros, void* stream) {
+  AQ_REQUIRE(w_dtype == AQ_F32 || w_dtype == AQ_BF16, "%s: w_dtype must be AQ_F32 or AQ_BF16 (got %d)", fn, w_dtype);
+  AQ_REQUIRE(valid_group(group), "%s: group must be 32, 64 or 128 (got %d)", fn, group);
+  AQ_REQUIRE(N >= 0 && N < kDimLimit, "%s: N out of range (%lld)", fn, (long long)N);
+  AQ_REQUIRE(K > 0 && K < kDimLimit, "%s: K out of range (%lld)", fn, (long long)K);
+  AQ_REQUIRE(K % group == 0, "%s: K (%lld) must be a multiple of group (%d)", fn, (long long)K, group);
   AQ_PTR(W, 16, "W");
-  if (chan_scale) AQ_REQUIRE(aligned(chan_scale, 16), "chan_scale must be 16-byte aligned");
+  if (chan_scale) AQ_REQUIRE(aligned(chan_scale, 16), "%s: chan_scale must be 16-byte aligned", fn);
   AQ_PTR(packed, 16, "packed");
   AQ_PTR(scales, 4, "scales");
   AQ_PTR(zeros, 1, "zeros");
-  if (fault_injected()) return fail(AQ_ERUNTIME, "aq_quantize_pack: injected launch failure");
+  if (fault_injected()) return fail(AQ_ERUNTIME, "%s: injected launch failure", fn);
   if (N == 0) return ok();
   return runtime_status(aq::launch_quant_pack(W, w_dtype == AQ_BF16, chan_scale, packed, scales, zeros, N, K, group,
-                                              (hipStream_t)stream),
-                        "aq_quantize_pack");
+                                              sym, (hipStream_t)stream),
+                        fn);
+}
+
+aq_status aq_quantize_pack(const void* W, int32_t w_dtype, int64_t N, int64_t K, int32_t group,
+                           const float* chan_scale, uint8_t* packed, float* scales, uint8_t* zeros,
+                           void* stream) {
+  return quantize_pack_common("aq_quantize_pack", false, W, w_dtype, N, K, group, chan_scale, packed, scales, zeros,
+                              stream);
+}
+
+aq_status aq_quantize_pack_sym(const void* W, int32_t w_dtype, int64_t N, int64_t K, int32_t group,
+                               const float* chan_scale, uint8_t* packed, float* scales, uint8_t* zeros,
+                               void* stream) {
+  return quantize_pack_common("aq_quantize_pack_sym", true, W, w_dtype, N, K, group, chan_scale, packed, scales,
+                              zeros, stream);
 }
 
 size_t aq_fp4_quantize_workspace(int64_t N, int64_t K) {
@@ -303,7 +317,7 @@ aq_status aq_awq_search(const uint16_t* X_sub, int64_t T, const float* absmean_h
   e = aq::launch_search_select(d_partial, L.nblocks, n_grid, (double)T * (double)N, d_sgrid, (int)K, mse, best,
                                best_scale, s);
   if (e != hipSuccess) return runtime_status(e, "aq_awq_search: select kernel");
-  return runtime_status(aq::launch_quant_pack(W, bf16, best_scale, packed, scales, zeros, N, K, group, s),
+  return runtime_status(aq::launch_quant_pack(W, bf16, best_scale, packed, scales, zeros, N, K, group, false, s),
                         "aq_awq_search: final pack");
 }
 

@@ -9,6 +9,12 @@
 //   q = clamp(rne(fl32(v / S)) + z, 0, 15)
 // with two codes per byte (even k in the low nibble).
 //
+// Symmetric variant (same page, section 2: a symmetric integer range with zero at
+// integer zero, q = round(x / s), x_hat = q s, clipped to the range): per group
+//   S = fl32(max |v| / 7),  q = clamp(rne(fl32(v / S)), -7, 7)
+// stored as the code q + 8 with a zero point of 8, so the decode (code - z) S of
+// the asymmetric format applies unchanged; an all-zero group stores S = 0, codes 8.
+//
 // Mapping: W[N, K] row-major is a flat run of N*K/g groups of g contiguous
 // elements.  Each lane owns 8 consecutive elements (one 16-byte bf16 load or two
 // 16-byte fp32 loads), so a group spans g/8 lanes and its min/max is a
@@ -19,7 +25,7 @@
 
 namespace aq {
 
-template <int G, bool BF16, bool SCALED>
+template <int G, bool BF16, bool SCALED, bool SYM>
 __global__ __launch_bounds__(256) void quant_pack_kernel(const void* __restrict__ W,
                                                          const float* __restrict__ chan_scale,
                                                          uint8_t* __restrict__ packed,
@@ -61,11 +67,23 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(const void* __restrict_
   }
   mn = segment_min<LPG>(mn);
   mx = segment_max<LPG>(mx);
-  const GroupQ g = group_params(mn, mx);
+  GroupQ g;
+  if constexpr (SYM) {
+    g.S = fmaxf(-mn, mx) / 7.0f;   // max |v| / 7 (fmaxf(-min, max) is max |v| exactly)
+    g.zf = 8.0f;
+    g.inv = g.S == 0.0f ? 0.0f : 1.0f / g.S;
+  } else {
+    g = group_params(mn, mx);
+  }
 
   uint32_t word = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) word |= group_code(v[i], g) << (4 * i);
+  for (int i = 0; i < 8; ++i) {
+    // |v / S| <= 7 (1 + 2^-23), so rne(v / S) + 8 stays in 1 .. 15 and the 0 .. 15
+    // clamp of group_code is the -7 .. 7 clamp of the symmetric code
+    const uint32_t c = (SYM && g.S == 0.0f) ? 8u : group_code(v[i], g);
+    word |= c << (4 * i);
+  }
   if (!live) return;
   *reinterpret_cast<uint32_t*>(packed + e / 2) = word;
   if ((threadIdx.x % LPG) == 0) {
@@ -152,7 +170,7 @@ hipError_t launch_quant_error(const void* W, bool w_bf16, const float* chan_scal
   return hipGetLastError();
 }
 
-template <int G>
+template <int G, bool SYM>
 static hipError_t launch_g(const void* W, bool bf16, const float* s, uint8_t* packed, float* scales,
                            uint8_t* zeros, int64_t N, int64_t K, hipStream_t stream) {
   const int64_t total = N * K;
@@ -160,24 +178,31 @@ static hipError_t launch_g(const void* W, bool bf16, const float* s, uint8_t* pa
   const dim3 block(256);
   const dim3 grid((unsigned)((lanes + 255) / 256));
   if (bf16) {
-    if (s) hipLaunchKernelGGL((quant_pack_kernel<G, true, true>), grid, block, 0, stream, W, s, packed, scales, zeros, total, K);
-    else hipLaunchKernelGGL((quant_pack_kernel<G, true, false>), grid, block, 0, stream, W, s, packed, scales, zeros, total, K);
+    if (s) hipLaunchKernelGGL((quant_pack_kernel<G, true, true, SYM>), grid, block, 0, stream, W, s, packed, scales, zeros, total, K);
+    else hipLaunchKernelGGL((quant_pack_kernel<G, true, false, SYM>), grid, block, 0, stream, W, s, packed, scales, zeros, total, K);
   } else {
-    if (s) hipLaunchKernelGGL((quant_pack_kernel<G, false, true>), grid, block, 0, stream, W, s, packed, scales, zeros, total, K);
-    else hipLaunchKernelGGL((quant_pack_kernel<G, false, false>), grid, block, 0, stream, W, s, packed, scales, zeros, total, K);
+    if (s) hipLaunchKernelGGL((quant_pack_kernel<G, false, true, SYM>), grid, block, 0, stream, W, s, packed, scales, zeros, total, K);
+    else hipLaunchKernelGGL((quant_pack_kernel<G, false, false, SYM>), grid, block, 0, stream, W, s, packed, scales, zeros, total, K);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_quant_pack(const void* W, bool w_bf16, const float* chan_scale, uint8_t* packed,
-                             float* scales, uint8_t* zeros, int64_t N, int64_t K, int group,
-                             hipStream_t stream) {
+template <bool SYM>
+static hipError_t launch_sym(const void* W, bool w_bf16, const float* chan_scale, uint8_t* packed, float* scales,
+                             uint8_t* zeros, int64_t N, int64_t K, int group, hipStream_t stream) {
   switch (group) {
-    case 32: return launch_g<32>(W, w_bf16, chan_scale, packed, scales, zeros, N, K, stream);
-    case 64: return launch_g<64>(W, w_bf16, chan_scale, packed, scales, zeros, N, K, stream);
-    case 128: return launch_g<128>(W, w_bf16, chan_scale, packed, scales, zeros, N, K, stream);
+    case 32: return launch_g<32, SYM>(W, w_bf16, chan_scale, packed, scales, zeros, N, K, stream);
+    case 64: return launch_g<64, SYM>(W, w_bf16, chan_scale, packed, scales, zeros, N, K, stream);
+    case 128: return launch_g<128, SYM>(W, w_bf16, chan_scale, packed, scales, zeros, N, K, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_quant_pack(const void* W, bool w_bf16, const float* chan_scale, uint8_t* packed,
+                             float* scales, uint8_t* zeros, int64_t N, int64_t K, int group, bool sym,
+                             hipStream_t stream) {
+  if (sym) return launch_sym<true>(W, w_bf16, chan_scale, packed, scales, zeros, N, K, group, stream);
+  return launch_sym<false>(W, w_bf16, chan_scale, packed, scales, zeros, N, K, group, stream);
 }
 
 }  // namespace aq

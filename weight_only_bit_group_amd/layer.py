@@ -51,9 +51,10 @@ class W4A16Linear(torch.nn.Module):
 
     @classmethod
     def from_weight(cls, weight: torch.Tensor, group: int, chan_scale: torch.Tensor | None = None,
-                    bias: torch.Tensor | None = None) -> "W4A16Linear":
-        """Pack W [N, K] (fp32 or bf16, on the GPU), optionally scaled by chan_scale [K]."""
-        p, s, z = B.aq_quantize_pack(weight.detach().contiguous(), group, chan_scale)
+                    bias: torch.Tensor | None = None, sym: bool = False) -> "W4A16Linear":
+        """Pack W [N, K] (fp32 or bf16, on the GPU), optionally scaled by chan_scale [K];
+        sym=True packs the symmetric variant (same format, zero point 8)."""
+        p, s, z = B.aq_quantize_pack(weight.detach().contiguous(), group, chan_scale, sym=sym)
         return cls(p, s, z, group, bias)
 
     def _workspace(self, m: int):
@@ -89,10 +90,11 @@ def _weight_of(linear) -> torch.Tensor:
     return linear.weight.detach()
 
 
-def quantize_linear(linear: torch.nn.Linear, group: int) -> W4A16Linear:
-    """Plain group-wise min-max INT4 of one linear (no channel scale)."""
+def quantize_linear(linear: torch.nn.Linear, group: int, sym: bool = False) -> W4A16Linear:
+    """Plain group-wise INT4 of one linear (no channel scale): min-max asymmetric, or
+    symmetric (max |w| / 7, zero point 8) with sym=True."""
     w = _weight_of(linear)
-    return W4A16Linear.from_weight(w.contiguous(), group, None, linear.bias)
+    return W4A16Linear.from_weight(w.contiguous(), group, None, linear.bias, sym)
 
 
 def norm_group_awq(norm_weight: torch.Tensor, linears, x_norm: torch.Tensor, group: int, n_grid: int = 20,
