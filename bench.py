@@ -14,6 +14,9 @@ group 64):
   search   aq_awq_search, 4096 tokens, 20 alphas, final pack     (AWQ search)
   fp4      aq_fp4_gemm at M = 1 and M = 2048 on W[14336, 4096]   (FP4 decode)
            and aq_fp4_quantize of an fp32 W[14336, 4096]          (FP4 encode)
+  int8     aq_quantize_pack8, aq_w8a16_gemv at M = 1 (24          (8-bit variant)
+           rotating copies, graph-replayed), aq_w8a16_gemm at
+           M = 4096 (staged)
   layer    a whole Qwen2.5-3B decoder layer: norm-group AWQ of    (module-level path)
            q|k|v and gate|up (joint search, 65536-token abs-mean,
            4096-token search) plus plain packing of o and down;
@@ -54,6 +57,7 @@ N_COPIES = 40
 FP4_N, FP4_K, FP4_M = 14336, 4096, 2048
 CAL_T, CAL_SUB = 65536, 4096
 LAYER_STACK = 12
+N8_COPIES = 24
 
 
 def gemv_bytes(m, n, k, g):
@@ -239,7 +243,7 @@ def main():
     torch.cuda.synchronize()
     torch.cuda.synchronize()
 
-    events = {k: [] for k in ("pack", "pack_sym", "gemv", "gemm", "absmean", "search", "fp4_gemv", "fp4_gemm", "fp4_encode",
+    events = {k: [] for k in ("pack", "pack_sym", "pack8", "gemv8", "gemm8", "gemv", "gemm", "absmean", "search", "fp4_gemv", "fp4_gemm", "fp4_encode",
                               "layer_awq", "layer_gemv")}
 
     def timed(name, record, fn):
@@ -272,11 +276,35 @@ def main():
         gemv_batch()
     torch.cuda.synchronize()
 
+    # INT8: the gate weight's 8-bit codes, 24 distinct copies for the rotating decode GEMV
+    # (24 x 22.9 MB = 549 MB > 2 x the MALL), captured in a graph like the INT4 batch
+    pk8 = B.aq_quantize_pack8(w_gate, G_)
+    copies8 = [pk8] + [B.aq_quantize_pack8(weight_bf16(N_, K_), G_) for _ in range(N8_COPIES - 1)]
+    ws8 = torch.empty(B.aq_w8a16_gemm_workspace(M_GEMM, N_, K_, G_), dtype=torch.uint8, device=dev)
+
+    def gemv8_batch():
+        for (c, s8, z8) in copies8:
+            B.aq_w8a16_gemv(x1, c, s8, z8, G_, out=y1)
+
+    side3 = torch.cuda.Stream()
+    side3.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side3):
+        gemv8_batch()
+    torch.cuda.current_stream().wait_stream(side3)
+    torch.cuda.synchronize()
+    gemv8_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gemv8_graph):
+        gemv8_batch()
+    torch.cuda.synchronize()
+
     def step(record):
         timed("pack", record, lambda: B.aq_quantize_pack(w_gate, G_, packed=pk[0], scales=pk[1], zeros=pk[2]))
         timed("pack_sym", record, lambda: B.aq_quantize_pack(w_gate, G_, packed=pk[0], scales=pk[1], zeros=pk[2],
                                                              sym=True))
         timed("gemv", record, gemv_graph.replay)
+        timed("pack8", record, lambda: B.aq_quantize_pack8(w_gate, G_, codes=pk8[0], scales=pk8[1], zeros=pk8[2]))
+        timed("gemv8", record, gemv8_graph.replay)
+        timed("gemm8", record, lambda: B.aq_w8a16_gemm(xg, *pk8, G_, out=yg, workspace=ws8))
         p, s, z = copies[0]
         timed("gemm", record, lambda: B.aq_w4a16_gemm(xg, p, s, z, G_, out=yg, workspace=ws_gemm))
         sum_abs.zero_()
@@ -302,6 +330,7 @@ def main():
 
     ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in events.items()}
     ms["gemv"] /= N_COPIES
+    ms["gemv8"] /= N8_COPIES
     ms["layer_gemv"] /= LAYER_STACK
     gemv_b = gemv_bytes(1, N_, K_, G_)
     gemv_gbs = gemv_b / (ms["gemv"] * 1e-3) / 1e9
@@ -313,6 +342,11 @@ def main():
         "pack_sym": {"us": ms["pack_sym"] * 1e3, "GB/s": pack_bytes(N_, K_, G_) / (ms["pack_sym"] * 1e-3) / 1e9},
         "gemv_m1": {"us": ms["gemv"] * 1e3, "GB/s": gemv_gbs},
         "gemm_m4096": {"us": ms["gemm"] * 1e3, "TFLOP/s": gemm_tf},
+        "pack8": {"us": ms["pack8"] * 1e3,
+                  "GB/s": (2 * N_ * K_ + N_ * K_ + (N_ * K_ // G_) * 5) / (ms["pack8"] * 1e-3) / 1e9},
+        "gemv8_m1": {"us": ms["gemv8"] * 1e3,
+                     "GB/s": (N_ * K_ + (N_ * K_ // G_) * 5 + 2 * K_ + 4 * N_) / (ms["gemv8"] * 1e-3) / 1e9},
+        "gemm8_m4096": {"us": ms["gemm8"] * 1e3, "TFLOP/s": gemm_flop / (ms["gemm8"] * 1e-3) / 1e12},
         "absmean": {"us": ms["absmean"] * 1e3, "GB/s": 2.0 * CAL_T * K_ / (ms["absmean"] * 1e-3) / 1e9},
         "awq_search": {"ms": ms["search"], "TFLOP/s": search_flop / (ms["search"] * 1e-3) / 1e12},
         "fp4_gemv_m1": {"us": ms["fp4_gemv"] * 1e3,

@@ -182,6 +182,41 @@ aq_status aq_awq_search(const uint16_t* X_sub, int64_t T, const float* absmean_h
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Group-wise asymmetric INT8 quantization (one code byte per weight).
+ * Source: "Quantization：模型量化" (xingyuwang.me), sections 2 and 3 (the
+ * asymmetric formulas with the integer range setting the clip; per-group
+ * scales); "模型量化指南" (blog.yoooo.fun), "混合精度（按层 4/8-bit）" (a per-layer
+ * policy keeps key layers at 8 bits, the rest at 4).
+ *
+ *   S = fl32(fl32(max v - min v) / 255), z = clamp(rne(fl32(-min v / S)), 0, 255),
+ *   q_k = clamp(rne(fl32(v_k / S)) + z, 0, 255); a constant group stores S = 0,
+ *   z = 0, q = 0 (v as in aq_quantize_pack, with the optional chan_scale).
+ * codes [N, K] uint8 (one byte per weight), scales [N, K/g] fp32, zeros
+ * [N, K/g] uint8.  Arguments and errors as aq_quantize_pack.
+ */
+aq_status aq_quantize_pack8(const void* W, int32_t w_dtype, int64_t N, int64_t K, int32_t group,
+                            const float* chan_scale, uint8_t* codes, float* scales, uint8_t* zeros, void* stream);
+
+/*
+ * W8A16 products of the INT8 format: Y[m, n] = sum_g S[n, g] sum_{k in g}
+ * X[m, k] (q[n, k] - z[n, g]), fp32 Y [M, N], X [M, K] bf16.
+ * aq_w8a16_gemv: 1 <= M <= 16, VALU kernel (HBM-bound at M = 1).
+ * aq_w8a16_gemm: any M; the codes are first dequantized exactly into the bf16
+ * matrix (q - z) in `workspace` (N * K * 2 bytes, aq_w8a16_gemm_workspace,
+ * 256-byte aligned, caller-owned, contents unspecified afterwards), then a
+ * bf16-MFMA GEMM applies the fp32 group steps to per-group partials.
+ * Source: as aq_quantize_pack8; the products as aq_w4a16_gemv / aq_w4a16_gemm.
+ * Errors: as aq_w4a16_gemv / aq_w4a16_gemm; aq_w8a16_gemm also for a NULL,
+ *         misaligned or small workspace.
+ */
+aq_status aq_w8a16_gemv(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes, const float* scales,
+                        const uint8_t* zeros, int64_t N, int32_t group, float* Y, void* stream);
+size_t aq_w8a16_gemm_workspace(int64_t M, int64_t N, int64_t K, int32_t group);
+aq_status aq_w8a16_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes, const float* scales,
+                        const uint8_t* zeros, int64_t N, int32_t group, float* Y, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
  * FP4 decode product: E2M1 codes with an FP8-E4M3 scale per 16-element block
  * and an fp32 tensor scale.  M <= 16 runs a VALU GEMV, larger M a bf16-MFMA
  * GEMM; both use the exact bf16 value e2m1 * e4m3.

@@ -106,6 +106,54 @@ def quantize_pack(w, group: int, chan_scale=None):
     return pack_nibbles(q), s, z
 
 
+# ---- 8-bit variant ---------------------------------------------------------------
+# The same asymmetric min-max formulas with the 8-bit unsigned range 0 .. 255
+# ("Quantization：模型量化", xingyuwang.me, section 2: the integer range sets the
+# clip; "BNB/GPTQ/AWQ量化全面支持", maplevalley.com.cn: weight-only 8-bit next to
+# 4-bit; the mixed 4/8-bit policy keeps key layers at 8 bits, "模型量化指南",
+# blog.yoooo.fun, "混合精度（按层 4/8-bit）").  Readings: S = fl32(fl32(max - min)
+# / 255), z = clamp(rne(fl32(-min / S)), 0, 255), q = clamp(rne(fl32(v / S)) + z,
+# 0, 255); one code byte per weight, codes [N, K] uint8; S fp32 and z uint8
+# [N, K / g]; a constant group stores S = 0, z = 0, q = 0.
+QMAX8 = 255
+
+
+def quantize_codes8(w, group: int, chan_scale=None):
+    """Codes q [N, K] (uint8 0..255), S [N, K/g] fp32, z [N, K/g] uint8."""
+    w = _as_f32(w)
+    n, k = w.shape
+    if k % group:
+        raise ValueError("K must be a multiple of the group size")
+    v = (w * _as_f32(chan_scale)[None, :]).astype(np.float32) if chan_scale is not None else w
+    vg = v.reshape(n, k // group, group)
+    mn = vg.min(axis=-1)
+    mx = vg.max(axis=-1)
+    s = ((mx - mn).astype(np.float32) / np.float32(QMAX8)).astype(np.float32)   # fl32(fl32(max-min) / 255)
+    degenerate = s == 0
+    safe = np.where(degenerate, np.float32(1), s).astype(np.float32)
+    z = np.clip(np.rint((-mn) / safe), 0, QMAX8)                             # rne(fl32(-min / S))
+    z = np.where(degenerate, 0, z)
+    r = np.rint(vg / safe[..., None])                                         # rne(fl32(v / S))
+    q = np.clip(r + z[..., None], 0, QMAX8)
+    q = np.where(degenerate[..., None], 0, q)
+    s = np.where(degenerate, np.float32(0), s).astype(np.float32)
+    return q.astype(np.uint8).reshape(n, k), s, z.astype(np.uint8)
+
+
+def dequantize8(codes, scales, zeros, group: int) -> np.ndarray:
+    """W_hat[N, K] = (q - z) * S in fp64 from one code byte per weight."""
+    q = np.asarray(codes, dtype=np.float64)
+    n, k = q.shape
+    s = np.asarray(scales, dtype=np.float64).reshape(n, k // group, 1)
+    z = np.asarray(zeros, dtype=np.float64).reshape(n, k // group, 1)
+    return ((q.reshape(n, k // group, group) - z) * s).reshape(n, k)
+
+
+def forward8(x_f32, codes, scales, zeros, group: int) -> np.ndarray:
+    """Y[M, N] = X @ W_hat^T for 8-bit codes, fp64."""
+    return np.asarray(x_f32, dtype=np.float64) @ dequantize8(codes, scales, zeros, group).T
+
+
 # ---- symmetric variant --------------------------------------------------------
 # "Quantization：模型量化" (xingyuwang.me), section 2, symmetric quantization: a
 # symmetric integer range with zero mapped to integer zero, q = round(x / s),

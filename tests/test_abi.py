@@ -56,7 +56,7 @@ def _qp(lib, fn="aq_quantize_pack", **kw):
     (dict(p=None), "packed"), (dict(s=FAKE_ODD), "chan_scale"), (dict(K=1 << 31), "K"),
 ])
 def test_quantize_pack_einval(lib, kw, frag):
-    for fn in ("aq_quantize_pack", "aq_quantize_pack_sym"):
+    for fn in ("aq_quantize_pack", "aq_quantize_pack_sym", "aq_quantize_pack8"):
         assert _qp(lib, fn, **kw) == _lib.AQ_EINVAL
         assert frag in _lib.last_error()
 
@@ -68,6 +68,25 @@ def _prod(lib, fn, **kw):
     if fn == "aq_w4a16_gemm":
         args += [a["ws"], a["wsb"]]
     return getattr(lib, fn)(*args, None)
+
+
+def _prod8(lib, fn, **kw):
+    a = dict(X=FAKE, M=1, K=256, C=FAKE, S=FAKE, Z=FAKE, N=64, g=64, Y=FAKE, ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    args = [a["X"], a["M"], a["K"], a["C"], a["S"], a["Z"], a["N"], a["g"], a["Y"]]
+    if fn == "aq_w8a16_gemm":
+        args += [a["ws"], a["wsb"]]
+    return getattr(lib, fn)(*args, None)
+
+
+def test_int8_products_einval(lib):
+    assert lib.aq_w8a16_gemm_workspace(4096, 64, 256, 64) == 64 * 256 * 2
+    assert lib.aq_w8a16_gemm_workspace(4096, 64, 250, 64) == 0
+    for kw in (dict(M=0), dict(M=17), dict(g=16), dict(K=100), dict(X=None), dict(C=FAKE + 8), dict(Y=FAKE + 2)):
+        assert _prod8(lib, "aq_w8a16_gemv", **kw) == _lib.AQ_EINVAL, kw
+    for kw in (dict(M=-1), dict(g=16), dict(ws=None), dict(ws=FAKE + 16), dict(wsb=64 * 256 * 2 - 1),
+               dict(K=1 << 22), dict(N=1 << 22)):
+        assert _prod8(lib, "aq_w8a16_gemm", **kw) == _lib.AQ_EINVAL, kw
 
 
 def _fp4(lib, X=FAKE, M=1, K=64, C=FAKE, B=FAKE, ts=1.0, N=8, Y=FAKE, ws=None, wsb=0):
@@ -197,6 +216,9 @@ def test_injected_runtime_failure(lib, monkeypatch):
     assert _fp4(lib) == _lib.AQ_ERUNTIME
     assert _fp4q(lib) == _lib.AQ_ERUNTIME
     assert _qp(lib, "aq_quantize_pack_sym") == _lib.AQ_ERUNTIME
+    assert _qp(lib, "aq_quantize_pack8") == _lib.AQ_ERUNTIME
+    assert _prod8(lib, "aq_w8a16_gemv") == _lib.AQ_ERUNTIME
+    assert _prod8(lib, "aq_w8a16_gemm", M=128) == _lib.AQ_ERUNTIME
     ws = lib.aq_act_absmean_workspace(64, 64)
     assert lib.aq_act_absmean(FAKE, 64, 64, FAKE, None, 64, FAKE, ws, None) == _lib.AQ_ERUNTIME
     # validation still wins over the injected fault

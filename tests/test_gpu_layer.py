@@ -126,3 +126,45 @@ def test_decoder_layer_norm_group_awq_and_module_swap():
         hx = host(h_test[:rows]).astype(np.float64)
         check_close(y - hx, ref - hx, f"decoder layer branch sum, {rows} token(s)")
         check_close(y, ref, f"decoder layer output, {rows} token(s)")
+
+
+def test_quantize_modules_mixed_4_8_bit_policy():
+    """quantize_modules swaps the selected linears following the policies (lm_head at 8 bits, one
+    block's MLP at g=128 symmetric, the rest 4-bit g=64); each swapped module's output equals the
+    oracle's packing + fp64 forward of the same weight within the tolerance."""
+    torch.manual_seed(0)
+    dev_ = torch.device("cuda")
+    model = torch.nn.Module()
+    model.layers = torch.nn.ModuleList()
+    for _ in range(2):
+        blk = torch.nn.Module()
+        blk.q_proj = torch.nn.Linear(512, 512, bias=True)
+        blk.mlp = torch.nn.Module()
+        blk.mlp.down_proj = torch.nn.Linear(1408, 512, bias=False)
+        model.layers.append(blk)
+    model.lm_head = torch.nn.Linear(512, 1024, bias=False)
+    model = model.to(dev_)
+    weights = {n: m.weight.detach().float().cpu().numpy() for n, m in model.named_modules()
+               if isinstance(m, torch.nn.Linear)}
+    biases = {n: (m.bias.detach().float().cpu().numpy() if m.bias is not None else 0.0)
+              for n, m in model.named_modules() if isinstance(m, torch.nn.Linear)}
+    step("quantize_modules with a 4/8-bit policy")
+    plan = L.quantize_modules(model, ("q_proj", "mlp", "lm_head"), bits=4, group_size=64,
+                              layer_policies=(L.LayerQuantPolicy(("lm_head",), bits=8),
+                                              L.LayerQuantPolicy(("layers.1.mlp",), group_size=128, sym=True)))
+    assert plan["lm_head"] == (8, 64, False) and plan["layers.1.mlp.down_proj"] == (4, 128, True)
+    named = dict(model.named_modules())
+    assert isinstance(named["lm_head"], L.W8A16Linear) and isinstance(named["layers.0.q_proj"], L.W4A16Linear)
+    for name, (bits, g, sym) in plan.items():
+        k = weights[name].shape[1]
+        for m in (1, 40):
+            xb = synth.layer_activations_bf16(9, m, k)
+            x = synth.bf16_bits_to_f32(xb)
+            step(f"{name} bits={bits} g={g} sym={sym} M={m}")
+            y = host(named[name](torch.from_numpy(x).to(dev_)))
+            if bits == 8:
+                ref = int4.forward8(x, *int4.quantize_codes8(weights[name], g), g)
+            else:
+                trip = int4.quantize_pack_sym(weights[name], g) if sym else int4.quantize_pack(weights[name], g)
+                ref = int4.forward(x, *trip, g)
+            check_close(y, ref + biases[name], f"policy {name} M={m}")

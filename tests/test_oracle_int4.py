@@ -293,3 +293,54 @@ def test_symmetric_zero_is_exact_and_codes_are_odd():
     what = int4.dequantize(*int4.quantize_pack_sym(w, 64), 64)
     bound = np.repeat(s.astype(np.float64), 64, axis=1) * (0.5 + 2.0 ** -20)
     assert (np.abs(what - w) <= bound).all()
+
+
+# ---------------------------------------------------------------- 8-bit variant
+
+@pytest.mark.parametrize("g", [32, 128])
+def test_int8_nearest_grid_point_brute_force(g):
+    """8-bit codes: S nearest fp32 to (max - min) / 255, z the nearest integer to -min/S clamped
+    to 0..255, each code the clamped rne(v/S) + z, and (q - z) S a nearest grid point of v."""
+    rng = np.random.default_rng(41 + g)
+    w = _adversarial_groups(rng, g, 16)
+    q, s, z = int4.quantize_codes8(w, g)
+    for r in range(w.shape[0]):
+        vals = w[r]
+        mn, mx = min(vals.tolist()), max(vals.tolist())
+        S = float(s[r, 0])
+        R = Fraction(float(np.float32(np.float32(mx) - np.float32(mn))))
+        if R == 0:
+            assert S == 0 and z[r, 0] == 0 and not q[r].any()
+            continue
+        exact = R / 255
+        cand = [np.float32(S), np.nextafter(np.float32(S), np.float32(np.inf)),
+                np.nextafter(np.float32(S), np.float32(-np.inf))]
+        assert abs(Fraction(float(cand[0])) - exact) <= min(abs(Fraction(float(c)) - exact) for c in cand[1:])
+        zq = Fraction(float(np.float32(np.float32(-mn) / np.float32(S))))
+        assert int(z[r, 0]) == min(max(_rne_fraction(zq), 0), 255)
+        for kk in range(g):
+            t = Fraction(float(np.float32(vals[kk] / np.float32(S))))
+            assert int(q[r, kk]) == min(max(_rne_fraction(t) + int(z[r, 0]), 0), 255)
+            v = Fraction(float(vals[kk]))
+            dq = abs(v - (int(q[r, kk]) - int(z[r, 0])) * Fraction(S))
+            # (up to the fp32 rounding of v / S: |t| <= 255 leaves an error below S 2^-15)
+            lo, hi = max(int(q[r, kk]) - 2, 0), min(int(q[r, kk]) + 2, 255)
+            for c in range(lo, hi + 1):
+                assert dq <= abs(v - (c - int(z[r, 0])) * Fraction(S)) + Fraction(S) * Fraction(1, 2 ** 14)
+
+
+def test_int8_min_to_zero_and_dequant_bound():
+    """Zero-straddling groups: the minimum gets code 0; every element is reconstructed within
+    S/2 (plus the fp32 rounding of v / S); the 8-bit error is about 17x (255 / 15) below the
+    4-bit one."""
+    rng = np.random.default_rng(8)
+    w = (rng.standard_normal((32, 512)) * 0.02).astype(np.float32)
+    q, s, z = int4.quantize_codes8(w, 64)
+    wg = w.reshape(32, 8, 64)
+    qg = q.reshape(32, 8, 64)
+    assert (np.take_along_axis(qg, wg.argmin(axis=-1)[..., None], -1) == 0).all()
+    what = int4.dequantize8(q, s, z, 64)
+    assert (np.abs(what - w) <= np.repeat(s.astype(np.float64), 64, axis=1) * (0.5 + 2.0 ** -14)).all()
+    e8 = np.abs(what - w).mean()
+    e4 = np.abs(int4.dequantize(*int4.quantize_pack(w, 64), 64) - w).mean()
+    assert 12 < e4 / e8 < 22

@@ -10,7 +10,8 @@ has not been built.
 
 __all__ = ["aq_quantize_pack", "aq_w4a16_gemv", "aq_w4a16_gemm", "aq_w4a16_gemm_workspace", "aq_act_absmean",
            "aq_act_absmean_workspace", "aq_awq_search", "aq_awq_search_workspace", "aq_fp4_gemm",
-           "aq_fp4_gemm_workspace", "aq_fp4_quantize", "aq_fp4_quantize_workspace"]
+           "aq_fp4_gemm_workspace", "aq_fp4_quantize", "aq_fp4_quantize_workspace", "aq_quantize_pack8",
+           "aq_w8a16_gemv", "aq_w8a16_gemm", "aq_w8a16_gemm_workspace"]
 
 
 def __getattr__(name):

@@ -21,6 +21,10 @@ _SZ = ctypes.c_size_t
 SIGNATURES = {
     "aq_quantize_pack": (_I32, [_P, _I32, _I64, _I64, _I32, _P, _P, _P, _P, _P]),
     "aq_quantize_pack_sym": (_I32, [_P, _I32, _I64, _I64, _I32, _P, _P, _P, _P, _P]),
+    "aq_quantize_pack8": (_I32, [_P, _I32, _I64, _I64, _I32, _P, _P, _P, _P, _P]),
+    "aq_w8a16_gemv": (_I32, [_P, _I64, _I64, _P, _P, _P, _I64, _I32, _P, _P]),
+    "aq_w8a16_gemm_workspace": (_SZ, [_I64, _I64, _I64, _I32]),
+    "aq_w8a16_gemm": (_I32, [_P, _I64, _I64, _P, _P, _P, _I64, _I32, _P, _P, _SZ, _P]),
     "aq_w4a16_gemv": (_I32, [_P, _I64, _I64, _P, _P, _P, _I64, _I32, _P, _P]),
     "aq_w4a16_gemm_workspace": (_SZ, [_I64, _I64, _I64, _I32]),
     "aq_w4a16_gemm": (_I32, [_P, _I64, _I64, _P, _P, _P, _I64, _I32, _P, _P, _SZ, _P]),

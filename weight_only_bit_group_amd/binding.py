@@ -240,3 +240,63 @@ def aq_fp4_quantize(W, *, codes=None, block_scales=None, tensor_scale=None, work
                                      tensor_scale.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(W))
     check(st, "aq_fp4_quantize")
     return codes, block_scales, tensor_scale
+
+
+def aq_quantize_pack8(W: torch.Tensor, group: int, chan_scale: torch.Tensor | None = None, *,
+                      codes=None, scales=None, zeros=None):
+    """(codes [N, K] u8, scales [N, K/g] f32, zeros [N, K/g] u8) of W[N, K] (f32 or bf16), 8-bit codes."""
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D [N, K]")
+    _need(W, "W", W.dtype)
+    n, k = W.shape
+    if k % group:
+        raise ValueError("K must be a multiple of group")
+    if chan_scale is not None:
+        _need(chan_scale, "chan_scale", torch.float32, 1)
+    if codes is None:
+        codes = torch.empty((n, k), dtype=torch.uint8, device=W.device)
+    _, scales, zeros = _packed_outputs(W, n, k, group, codes, scales, zeros)
+    st = _lib.load().aq_quantize_pack8(W.data_ptr(), _wdtype(W), n, k, group, _ptr(chan_scale), codes.data_ptr(),
+                                       scales.data_ptr(), zeros.data_ptr(), _stream(W))
+    check(st, "aq_quantize_pack8")
+    return codes, scales, zeros
+
+
+def aq_w8a16_gemm_workspace(M: int, N: int, K: int, group: int) -> int:
+    return int(_lib.load().aq_w8a16_gemm_workspace(M, N, K, group))
+
+
+def _product8(fn_name, X, codes, scales, zeros, group, out, workspace=None):
+    _need(X, "X", torch.bfloat16, 2)
+    _need(codes, "codes", torch.uint8, 2)
+    _need(scales, "scales", torch.float32, 2)
+    _need(zeros, "zeros", torch.uint8, 2)
+    m, k = X.shape
+    n = codes.shape[0]
+    if codes.shape[1] != k:
+        raise ValueError("codes must be [N, K] for X [M, K]")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=X.device)
+    _need(out, "Y", torch.float32, 2)
+    lib = _lib.load()
+    if fn_name == "aq_w8a16_gemm":
+        need = int(lib.aq_w8a16_gemm_workspace(m, n, k, group))
+        if workspace is None:
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=X.device)
+        st = lib.aq_w8a16_gemm(X.data_ptr(), m, k, codes.data_ptr(), scales.data_ptr(), zeros.data_ptr(), n, group,
+                               out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(X))
+    else:
+        st = lib.aq_w8a16_gemv(X.data_ptr(), m, k, codes.data_ptr(), scales.data_ptr(), zeros.data_ptr(), n, group,
+                               out.data_ptr(), _stream(X))
+    check(st, fn_name)
+    return out
+
+
+def aq_w8a16_gemv(X, codes, scales, zeros, group: int, out=None):
+    """Y[M, N] fp32 = X[M, K] (bf16, 1 <= M <= 16) times the dequantized 8-bit weight, transposed."""
+    return _product8("aq_w8a16_gemv", X, codes, scales, zeros, group, out)
+
+
+def aq_w8a16_gemm(X, codes, scales, zeros, group: int, out=None, workspace=None):
+    """Y[M, N] fp32 = X[M, K] (bf16, any M) times the dequantized 8-bit weight (staged bf16 + MFMA)."""
+    return _product8("aq_w8a16_gemm", X, codes, scales, zeros, group, out, workspace)

@@ -93,7 +93,7 @@ extern "C" {
 
 const char* aq_last_error(void) { return g_last_error.c_str(); }
 
-static aq_status quantize_pack_common(const char* fn, bool sym, const void* W, int32_t w_dtype, int64_t N,
+static aq_status quantize_pack_common(const char* fn, int mode, const void* W, int32_t w_dtype, int64_t N,
                                       int64_t K, int32_t group, const float* chan_scale, uint8_t* packed,
                                       float* scales, uint8_t* zeros, void* stream) {
   AQ_REQUIRE(w_dtype == AQ_F32 || w_dtype == AQ_BF16, "%s: w_dtype must be AQ_F32 or AQ_BF16 (got %d)", fn, w_dtype);
@@ -108,23 +108,32 @@ static aq_status quantize_pack_common(const char* fn, bool sym, const void* W, i
   AQ_PTR(zeros, 1, "zeros");
   if (fault_injected()) return fail(AQ_ERUNTIME, "%s: injected launch failure", fn);
   if (N == 0) return ok();
-  return runtime_status(aq::launch_quant_pack(W, w_dtype == AQ_BF16, chan_scale, packed, scales, zeros, N, K, group,
-                                              sym, (hipStream_t)stream),
-                        fn);
+  const bool bf16 = w_dtype == AQ_BF16;
+  const hipError_t e =
+      mode == 2 ? aq::launch_quant_pack8(W, bf16, chan_scale, packed, scales, zeros, N, K, group, (hipStream_t)stream)
+                : aq::launch_quant_pack(W, bf16, chan_scale, packed, scales, zeros, N, K, group, mode == 1,
+                                        (hipStream_t)stream);
+  return runtime_status(e, fn);
 }
 
 aq_status aq_quantize_pack(const void* W, int32_t w_dtype, int64_t N, int64_t K, int32_t group,
                            const float* chan_scale, uint8_t* packed, float* scales, uint8_t* zeros,
                            void* stream) {
-  return quantize_pack_common("aq_quantize_pack", false, W, w_dtype, N, K, group, chan_scale, packed, scales, zeros,
+  return quantize_pack_common("aq_quantize_pack", 0, W, w_dtype, N, K, group, chan_scale, packed, scales, zeros,
                               stream);
 }
 
 aq_status aq_quantize_pack_sym(const void* W, int32_t w_dtype, int64_t N, int64_t K, int32_t group,
                                const float* chan_scale, uint8_t* packed, float* scales, uint8_t* zeros,
                                void* stream) {
-  return quantize_pack_common("aq_quantize_pack_sym", true, W, w_dtype, N, K, group, chan_scale, packed, scales,
+  return quantize_pack_common("aq_quantize_pack_sym", 1, W, w_dtype, N, K, group, chan_scale, packed, scales,
                               zeros, stream);
+}
+
+aq_status aq_quantize_pack8(const void* W, int32_t w_dtype, int64_t N, int64_t K, int32_t group,
+                            const float* chan_scale, uint8_t* codes, float* scales, uint8_t* zeros, void* stream) {
+  return quantize_pack_common("aq_quantize_pack8", 2, W, w_dtype, N, K, group, chan_scale, codes, scales, zeros,
+                              stream);
 }
 
 size_t aq_fp4_quantize_workspace(int64_t N, int64_t K) {
@@ -196,6 +205,43 @@ static aq_status staging(const char* fn, int64_t M, int64_t N, int64_t K, void* 
   AQ_REQUIRE(aligned(workspace, 256), "%s: workspace must be 256-byte aligned", fn);
   *out = static_cast<uint16_t*>(workspace);
   return AQ_OK;
+}
+
+aq_status aq_w8a16_gemv(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes, const float* scales,
+                        const uint8_t* zeros, int64_t N, int32_t group, float* Y, void* stream) {
+  AQ_REQUIRE(M >= 1 && M <= 16, "aq_w8a16_gemv: M must be in 1..16 (got %lld)", (long long)M);
+  aq_status st = check_product("aq_w8a16_gemv", X, M, K, codes, scales, zeros, N, group, Y);
+  if (st != AQ_OK) return st;
+  if (fault_injected()) return fail(AQ_ERUNTIME, "aq_w8a16_gemv: injected launch failure");
+  if (N == 0) return ok();
+  return runtime_status(aq::launch_w8a16_gemv(X, (int)M, (int)K, codes, scales, zeros, (int)N, group, Y,
+                                              (hipStream_t)stream),
+                        "aq_w8a16_gemv");
+}
+
+size_t aq_w8a16_gemm_workspace(int64_t M, int64_t N, int64_t K, int32_t group) {
+  if (!valid_group(group) || M < 0 || N <= 0 || K <= 0 || K % group || N >= kGemmDimLimit || K >= kGemmDimLimit)
+    return 0;
+  return (size_t)N * (size_t)K * sizeof(uint16_t);
+}
+
+aq_status aq_w8a16_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes, const float* scales,
+                        const uint8_t* zeros, int64_t N, int32_t group, float* Y, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  AQ_REQUIRE(M >= 0 && M < kDimLimit, "aq_w8a16_gemm: M out of range (%lld)", (long long)M);
+  aq_status st = check_product("aq_w8a16_gemm", X, M, K, codes, scales, zeros, N, group, Y);
+  if (st != AQ_OK) return st;
+  AQ_REQUIRE(K < kGemmDimLimit && N < kGemmDimLimit, "aq_w8a16_gemm: K and N must be below 2^22 (got %lld, %lld)",
+             (long long)K, (long long)N);
+  AQ_PTR(workspace, 256, "workspace");
+  AQ_REQUIRE(workspace_bytes >= (size_t)N * (size_t)K * sizeof(uint16_t),
+             "aq_w8a16_gemm: workspace too small (%zu < %zu bytes)", workspace_bytes,
+             (size_t)N * (size_t)K * sizeof(uint16_t));
+  if (fault_injected()) return fail(AQ_ERUNTIME, "aq_w8a16_gemm: injected launch failure");
+  if (N == 0 || M == 0) return ok();
+  return runtime_status(aq::launch_w8a16_gemm(X, (int)M, (int)K, codes, scales, zeros, (int)N, group, Y,
+                                              static_cast<uint16_t*>(workspace), (hipStream_t)stream),
+                        "aq_w8a16_gemm");
 }
 
 size_t aq_w4a16_gemm_workspace(int64_t M, int64_t N, int64_t K, int32_t group) {

@@ -19,6 +19,14 @@ hipError_t launch_w4a16_gemv(const uint16_t* X, int M, int K, const uint8_t* P, 
 // receives the dequantized weights (the staged GEMM then loads them like activations)
 hipError_t launch_w4a16_gemm(const uint16_t* X, int M, int K, const uint8_t* P, const float* S, const uint8_t* Z,
                              int N, int group, float* Y, uint16_t* staged, hipStream_t stream);
+// 8-bit codes [N, K] (one byte per weight), S / z as the INT4 format
+hipError_t launch_quant_pack8(const void* W, bool w_bf16, const float* chan_scale, uint8_t* codes, float* scales,
+                              uint8_t* zeros, int64_t N, int64_t K, int group, hipStream_t stream);
+hipError_t launch_w8a16_gemv(const uint16_t* X, int M, int K, const uint8_t* C, const float* S, const uint8_t* Z,
+                             int N, int group, float* Y, hipStream_t stream);
+// `staged`: N * K bf16 of device memory (always used)
+hipError_t launch_w8a16_gemm(const uint16_t* X, int M, int K, const uint8_t* C, const float* S, const uint8_t* Z,
+                             int N, int group, float* Y, uint16_t* staged, hipStream_t stream);
 hipError_t launch_fp4_gemv(const uint16_t* X, int M, int K, const uint8_t* codes, const uint8_t* bscale, float ts,
                            int N, float* Y, hipStream_t stream);
 hipError_t launch_fp4_gemm(const uint16_t* X, int M, int K, const uint8_t* codes, const uint8_t* bscale, float ts,

@@ -795,6 +795,29 @@ __global__ __launch_bounds__(256) void stage_weights_kernel(const uint8_t* __res
   dst[1] = u32x4{o[4], o[5], o[6], o[7]};
 }
 
+// 8-bit codes: the exact integer q - z (|q - z| <= 255 has at most 8 significant
+// bits, exact in bf16); one thread converts 16 code bytes (16 in, 32 out).
+__global__ __launch_bounds__(256) void stage_weights8_kernel(const uint8_t* __restrict__ codes,
+                                                             const uint8_t* __restrict__ zeros, int N, int K, int G,
+                                                             uint16_t* __restrict__ W16) {
+  const int cpr = K >> 4;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)N * cpr) return;
+  const int n = (int)(idx / cpr), c = (int)(idx - (int64_t)n * cpr);
+  const u32x4 w = *reinterpret_cast<const u32x4*>(codes + (int64_t)n * K + c * 16);
+  const float z = (float)zeros[(int64_t)n * (K / G) + (c * 16) / G];
+  uint32_t o[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = pack_bf16_exact(ubyte_f32<0>(w[i]) - z, ubyte_f32<1>(w[i]) - z);
+    o[2 * i + 1] =
+        pack_bf16_exact(ubyte_f32<2>(w[i]) - z, ubyte_f32<3>(w[i]) - z);
+  }
+  u32x4* dst = reinterpret_cast<u32x4*>(W16 + (int64_t)n * K + c * 16);
+  dst[0] = u32x4{o[0], o[1], o[2], o[3]};
+  dst[1] = u32x4{o[4], o[5], o[6], o[7]};
+}
+
 template <bool FP4>
 hipError_t stage_weights(const uint8_t* codes, const uint8_t* aux, int N, int K, int G, uint16_t* W16,
                          hipStream_t stream) {
@@ -864,6 +887,25 @@ hipError_t launch_w4a16_gemm(const uint16_t* X, int M, int K, const uint8_t* P, 
     case 32: return launch_tiles<B_INT4, 32>(a, stream);
     case 64: return launch_tiles<B_INT4, 64>(a, stream);
     case 128: return launch_tiles<B_INT4, 128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_w8a16_gemm(const uint16_t* X, int M, int K, const uint8_t* C, const float* S, const uint8_t* Z,
+                             int N, int group, float* Y, uint16_t* staged, hipStream_t stream) {
+  // always staged: the 8-bit codes are dequantized once into the bf16 matrix, then
+  // the staged INT4 GEMM (same per-group step rescale) runs on it
+  const int64_t chunks = (int64_t)N * (K >> 4);
+  hipLaunchKernelGGL(stage_weights8_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream, C, Z, N, K,
+                     group, staged);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  GemmArgs a = {};
+  a.X = X; a.M = M; a.N = N; a.K = K; a.S = S; a.Y = Y; a.B = staged;
+  switch (group) {
+    case 32: return launch_tiles<B_INT4S, 32>(a, stream);
+    case 64: return launch_tiles<B_INT4S, 64>(a, stream);
+    case 128: return launch_tiles<B_INT4S, 128>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

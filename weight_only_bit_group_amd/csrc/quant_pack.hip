@@ -15,6 +15,9 @@
 // stored as the code q + 8 with a zero point of 8, so the decode (code - z) S of
 // the asymmetric format applies unchanged; an all-zero group stores S = 0, codes 8.
 //
+// 8-bit variant: the asymmetric formulas with the range 0 .. 255 and one code byte
+// per weight (codes [N, K]).
+//
 // Mapping: W[N, K] row-major is a flat run of N*K/g groups of g contiguous
 // elements.  Each lane owns 8 consecutive elements (one 16-byte bf16 load or two
 // 16-byte fp32 loads), so a group spans g/8 lanes and its min/max is a
@@ -25,7 +28,8 @@
 
 namespace aq {
 
-template <int G, bool BF16, bool SCALED, bool SYM>
+// MODE: 0 asymmetric INT4, 1 symmetric INT4, 2 asymmetric INT8.
+template <int G, bool BF16, bool SCALED, int MODE>
 __global__ __launch_bounds__(256) void quant_pack_kernel(const void* __restrict__ W,
                                                          const float* __restrict__ chan_scale,
                                                          uint8_t* __restrict__ packed,
@@ -67,25 +71,35 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(const void* __restrict_
   }
   mn = segment_min<LPG>(mn);
   mx = segment_max<LPG>(mx);
+  constexpr bool SYM = MODE == 1;
+  constexpr int QM = MODE == 2 ? 255 : 15;
   GroupQ g;
   if constexpr (SYM) {
     g.S = fmaxf(-mn, mx) / 7.0f;   // max |v| / 7 (fmaxf(-min, max) is max |v| exactly)
     g.zf = 8.0f;
     g.inv = g.S == 0.0f ? 0.0f : 1.0f / g.S;
   } else {
-    g = group_params(mn, mx);
+    g = group_params_q<QM>(mn, mx);
   }
 
-  uint32_t word = 0;
+  if constexpr (MODE == 2) {
+    uint32_t b[2] = {0u, 0u};
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    // |v / S| <= 7 (1 + 2^-23), so rne(v / S) + 8 stays in 1 .. 15 and the 0 .. 15
-    // clamp of group_code is the -7 .. 7 clamp of the symmetric code
-    const uint32_t c = (SYM && g.S == 0.0f) ? 8u : group_code(v[i], g);
-    word |= c << (4 * i);
+    for (int i = 0; i < 8; ++i) b[i >> 2] |= group_code_q<255>(v[i], g) << (8 * (i & 3));
+    if (!live) return;
+    *reinterpret_cast<uint2*>(packed + e) = uint2{b[0], b[1]};
+  } else {
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      // |v / S| <= 7 (1 + 2^-23), so rne(v / S) + 8 stays in 1 .. 15 and the 0 .. 15
+      // clamp of group_code is the -7 .. 7 clamp of the symmetric code
+      const uint32_t c = (SYM && g.S == 0.0f) ? 8u : group_code(v[i], g);
+      word |= c << (4 * i);
+    }
+    if (!live) return;
+    *reinterpret_cast<uint32_t*>(packed + e / 2) = word;
   }
-  if (!live) return;
-  *reinterpret_cast<uint32_t*>(packed + e / 2) = word;
   if ((threadIdx.x % LPG) == 0) {
     const int64_t grp = e / G;
     scales[grp] = g.S;
@@ -170,7 +184,7 @@ hipError_t launch_quant_error(const void* W, bool w_bf16, const float* chan_scal
   return hipGetLastError();
 }
 
-template <int G, bool SYM>
+template <int G, int MODE>
 static hipError_t launch_g(const void* W, bool bf16, const float* s, uint8_t* packed, float* scales,
                            uint8_t* zeros, int64_t N, int64_t K, hipStream_t stream) {
   const int64_t total = N * K;
@@ -178,22 +192,22 @@ static hipError_t launch_g(const void* W, bool bf16, const float* s, uint8_t* pa
   const dim3 block(256);
   const dim3 grid((unsigned)((lanes + 255) / 256));
   if (bf16) {
-    if (s) hipLaunchKernelGGL((quant_pack_kernel<G, true, true, SYM>), grid, block, 0, stream, W, s, packed, scales, zeros, total, K);
-    else hipLaunchKernelGGL((quant_pack_kernel<G, true, false, SYM>), grid, block, 0, stream, W, s, packed, scales, zeros, total, K);
+    if (s) hipLaunchKernelGGL((quant_pack_kernel<G, true, true, MODE>), grid, block, 0, stream, W, s, packed, scales, zeros, total, K);
+    else hipLaunchKernelGGL((quant_pack_kernel<G, true, false, MODE>), grid, block, 0, stream, W, s, packed, scales, zeros, total, K);
   } else {
-    if (s) hipLaunchKernelGGL((quant_pack_kernel<G, false, true, SYM>), grid, block, 0, stream, W, s, packed, scales, zeros, total, K);
-    else hipLaunchKernelGGL((quant_pack_kernel<G, false, false, SYM>), grid, block, 0, stream, W, s, packed, scales, zeros, total, K);
+    if (s) hipLaunchKernelGGL((quant_pack_kernel<G, false, true, MODE>), grid, block, 0, stream, W, s, packed, scales, zeros, total, K);
+    else hipLaunchKernelGGL((quant_pack_kernel<G, false, false, MODE>), grid, block, 0, stream, W, s, packed, scales, zeros, total, K);
   }
   return hipGetLastError();
 }
 
-template <bool SYM>
-static hipError_t launch_sym(const void* W, bool w_bf16, const float* chan_scale, uint8_t* packed, float* scales,
-                             uint8_t* zeros, int64_t N, int64_t K, int group, hipStream_t stream) {
+template <int MODE>
+static hipError_t launch_mode(const void* W, bool w_bf16, const float* chan_scale, uint8_t* packed, float* scales,
+                              uint8_t* zeros, int64_t N, int64_t K, int group, hipStream_t stream) {
   switch (group) {
-    case 32: return launch_g<32, SYM>(W, w_bf16, chan_scale, packed, scales, zeros, N, K, stream);
-    case 64: return launch_g<64, SYM>(W, w_bf16, chan_scale, packed, scales, zeros, N, K, stream);
-    case 128: return launch_g<128, SYM>(W, w_bf16, chan_scale, packed, scales, zeros, N, K, stream);
+    case 32: return launch_g<32, MODE>(W, w_bf16, chan_scale, packed, scales, zeros, N, K, stream);
+    case 64: return launch_g<64, MODE>(W, w_bf16, chan_scale, packed, scales, zeros, N, K, stream);
+    case 128: return launch_g<128, MODE>(W, w_bf16, chan_scale, packed, scales, zeros, N, K, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -201,8 +215,13 @@ static hipError_t launch_sym(const void* W, bool w_bf16, const float* chan_scale
 hipError_t launch_quant_pack(const void* W, bool w_bf16, const float* chan_scale, uint8_t* packed,
                              float* scales, uint8_t* zeros, int64_t N, int64_t K, int group, bool sym,
                              hipStream_t stream) {
-  if (sym) return launch_sym<true>(W, w_bf16, chan_scale, packed, scales, zeros, N, K, group, stream);
-  return launch_sym<false>(W, w_bf16, chan_scale, packed, scales, zeros, N, K, group, stream);
+  if (sym) return launch_mode<1>(W, w_bf16, chan_scale, packed, scales, zeros, N, K, group, stream);
+  return launch_mode<0>(W, w_bf16, chan_scale, packed, scales, zeros, N, K, group, stream);
+}
+
+hipError_t launch_quant_pack8(const void* W, bool w_bf16, const float* chan_scale, uint8_t* codes, float* scales,
+                              uint8_t* zeros, int64_t N, int64_t K, int group, hipStream_t stream) {
+  return launch_mode<2>(W, w_bf16, chan_scale, codes, scales, zeros, N, K, group, stream);
 }
 
 }  // namespace aq

@@ -36,16 +36,6 @@ namespace {
 
 constexpr int kLdsBytes = 48 * 1024;
 
-__device__ __forceinline__ float dpp_sum_to_lane63(float v) {
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xC, 0xF, false));
-  return v;  // lane 63 holds the wave total
-}
-
 // (k, k+4) pairing of one 8-activation dword quad: xw = 4 dwords of natural bf16 pairs.
 __device__ __forceinline__ u32x4 permute_pairs(const u32x4 t) {
   u32x4 p;

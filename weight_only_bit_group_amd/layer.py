@@ -19,8 +19,16 @@ this module only arranges tensors and swaps modules.
   * ``quantize_linear``: plain group-wise min-max packing for linears with no
     norm in front of them (o_proj and down_proj follow a non-linearity, so no
     scale can be folded; same page, after the fourth case).
+  * ``W8A16Linear`` and ``quantize_modules`` with ``LayerQuantPolicy``: the mixed
+    4/8-bit policy ("模型量化指南", "混合精度（按层 4/8-bit）": a policy binds bits /
+    group size / symmetry to named layers, unspecified fields inherit the base
+    configuration, and a policy target outside the layers selected by
+    target_modules is an error at parse time; "共同约定": explicit errors for a
+    model without linears, targets that match nothing, and re-quantization).
 """
 from __future__ import annotations
+
+from dataclasses import dataclass
 
 import torch
 
@@ -128,3 +136,117 @@ def norm_group_awq(norm_weight: torch.Tensor, linears, x_norm: torch.Tensor, gro
         out.append(W4A16Linear(res["packed"][n0:n1], res["scales"][n0:n1], res["zeros"][n0:n1], group, lin.bias))
         n0 = n1
     return folded, out, res
+
+
+class W8A16Linear(torch.nn.Module):
+    """y = x W^T (+ bias) with W stored as group-wise INT8 (codes [N, K], S, z); bf16 in, fp32 out."""
+
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor, group: int,
+                 bias: torch.Tensor | None = None):
+        super().__init__()
+        if codes.dim() != 2 or scales.shape != zeros.shape or scales.shape[0] != codes.shape[0]:
+            raise ValueError("codes [N, K], scales and zeros [N, K/group] expected")
+        self.group = int(group)
+        self.in_features = codes.shape[1]
+        self.out_features = codes.shape[0]
+        if scales.shape[1] * self.group != self.in_features:
+            raise ValueError("scales must be [N, K/group]")
+        self.register_buffer("codes", codes.contiguous())
+        self.register_buffer("scales", scales.contiguous())
+        self.register_buffer("zeros", zeros.contiguous())
+        self.register_buffer("bias", None if bias is None else bias.detach().float().contiguous())
+        self._ws = None
+
+    @classmethod
+    def from_weight(cls, weight: torch.Tensor, group: int, chan_scale: torch.Tensor | None = None,
+                    bias: torch.Tensor | None = None) -> "W8A16Linear":
+        c, s, z = B.aq_quantize_pack8(weight.detach().contiguous(), group, chan_scale)
+        return cls(c, s, z, group, bias)
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        if x.shape[-1] != self.in_features:
+            raise ValueError(f"expected {self.in_features} input features, got {x.shape[-1]}")
+        x2 = x.reshape(-1, self.in_features).to(torch.bfloat16).contiguous()
+        m = x2.shape[0]
+        if m <= 16:
+            y = B.aq_w8a16_gemv(x2, self.codes, self.scales, self.zeros, self.group)
+        else:
+            need = B.aq_w8a16_gemm_workspace(m, self.out_features, self.in_features, self.group)
+            if self._ws is None or self._ws.numel() < need:
+                self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.codes.device)
+            y = B.aq_w8a16_gemm(x2, self.codes, self.scales, self.zeros, self.group, workspace=self._ws)
+        if self.bias is not None:
+            y = y + self.bias
+        return y.reshape(*x.shape[:-1], self.out_features)
+
+    def extra_repr(self) -> str:
+        return f"in_features={self.in_features}, out_features={self.out_features}, group={self.group}, bits=8"
+
+
+@dataclass(frozen=True)
+class LayerQuantPolicy:
+    """Per-layer override of the base configuration; None fields inherit it."""
+    target_modules: tuple
+    bits: int | None = None
+    group_size: int | None = None
+    sym: bool | None = None
+
+
+def _matches(name: str, target: str) -> bool:
+    """target names whole dotted components of name (a linear or one of its parents)."""
+    return ("." + target + ".") in ("." + name + ".")
+
+
+def plan_quantization(model: torch.nn.Module, target_modules, bits: int = 4, group_size: int = 64,
+                      sym: bool = False, layer_policies=()):
+    """{linear name: (bits, group_size, sym)} for the linears the call would quantize.
+
+    Checks everything before anything is quantized: the model has linears, the
+    targets match some, no target is already quantized, every policy target matches
+    a selected linear, and every (bits, sym) pair is supported (4-bit asymmetric or
+    symmetric, 8-bit asymmetric).
+    """
+    named = dict(model.named_modules())
+    quantized = [n for n, m in named.items() if isinstance(m, (W4A16Linear, W8A16Linear))]
+    linears = [n for n, m in named.items() if isinstance(m, torch.nn.Linear)]
+    if not linears and not quantized:
+        raise ValueError("the model contains no torch.nn.Linear")
+    targets = tuple(target_modules)
+    hit = [n for n in linears if any(_matches(n, t) for t in targets)]
+    again = [n for n in quantized if any(_matches(n, t) for t in targets)]
+    if again:
+        raise ValueError(f"already quantized: {again[0]}")
+    if not hit:
+        raise ValueError(f"target_modules {targets} match no linear")
+    plan = {n: (bits, group_size, sym) for n in hit}
+    for pol in layer_policies:
+        sel = [n for n in hit if any(_matches(n, t) for t in pol.target_modules)]
+        if not sel:
+            raise ValueError(f"policy targets {tuple(pol.target_modules)} match no selected linear")
+        for n in sel:
+            b, g, s = plan[n]
+            plan[n] = (pol.bits if pol.bits is not None else b, pol.group_size if pol.group_size is not None else g,
+                       pol.sym if pol.sym is not None else s)
+    for n, (b, g, s) in plan.items():
+        if b not in (4, 8) or (b == 8 and s) or g not in (32, 64, 128):
+            raise ValueError(f"{n}: unsupported configuration bits={b} group_size={g} sym={s}")
+        k = named[n].in_features
+        if k % g:
+            raise ValueError(f"{n}: in_features {k} is not a multiple of group_size {g}")
+    return plan
+
+
+def quantize_modules(model: torch.nn.Module, target_modules, bits: int = 4, group_size: int = 64, sym: bool = False,
+                     layer_policies=()):
+    """Replace the selected nn.Linear modules of ``model`` by W4A16Linear / W8A16Linear
+    (plain group-wise packing) following the base configuration and the policies (the
+    last matching policy wins).  Returns the plan of ``plan_quantization``."""
+    plan = plan_quantization(model, target_modules, bits, group_size, sym, layer_policies)
+    named = dict(model.named_modules())
+    for name, (b, g, s) in plan.items():
+        lin = named[name]
+        new = (W8A16Linear.from_weight(_weight_of(lin).contiguous(), g, None, lin.bias) if b == 8
+               else W4A16Linear.from_weight(_weight_of(lin).contiguous(), g, None, lin.bias, s))
+        parent_name, _, attr = name.rpartition(".")
+        setattr(named[parent_name] if parent_name else model, attr, new)
+    return plan
