@@ -30,7 +30,9 @@ replayed back to back between one pair (as a decode loop does; eager Python
 launches would measure the binding's per-call overhead instead of the kernel) and
 are averaged per launch.  The headline value is
 the decode GEMV's HBM throughput (algorithmic bytes / average launch duration);
-the GEMM's TFLOP/s and the other stages are reported beside it.
+the GEMM's TFLOP/s and the other stages are reported beside it, and, as context
+only, torch's dense bf16 matmul (the vendor BLAS) on the unquantized prefill
+weight (`context_torch_bf16_mm_m4096`).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -243,7 +245,10 @@ def main():
     torch.cuda.synchronize()
     torch.cuda.synchronize()
 
-    events = {k: [] for k in ("pack", "pack_sym", "pack8", "gemv8", "gemm8", "gemv", "gemm", "absmean", "search", "fp4_gemv", "fp4_gemm", "fp4_encode",
+    # context, not part of the path: torch's dense bf16 matmul (the vendor BLAS) on the prefill
+    # shape with the unquantized bf16 weight, fp32 output like the W4A16 GEMM
+    w_gate_t = w_gate.t()
+    events = {k: [] for k in ("ref_mm", "pack", "pack_sym", "pack8", "gemv8", "gemm8", "gemv", "gemm", "absmean", "search", "fp4_gemv", "fp4_gemm", "fp4_encode",
                               "layer_awq", "layer_gemv")}
 
     def timed(name, record, fn):
@@ -302,6 +307,7 @@ def main():
         timed("pack_sym", record, lambda: B.aq_quantize_pack(w_gate, G_, packed=pk[0], scales=pk[1], zeros=pk[2],
                                                              sym=True))
         timed("gemv", record, gemv_graph.replay)
+        timed("ref_mm", record, lambda: torch.mm(xg, w_gate_t, out_dtype=torch.float32))
         timed("pack8", record, lambda: B.aq_quantize_pack8(w_gate, G_, codes=pk8[0], scales=pk8[1], zeros=pk8[2]))
         timed("gemv8", record, gemv8_graph.replay)
         timed("gemm8", record, lambda: B.aq_w8a16_gemm(xg, *pk8, G_, out=yg, workspace=ws8))
@@ -342,6 +348,8 @@ def main():
         "pack_sym": {"us": ms["pack_sym"] * 1e3, "GB/s": pack_bytes(N_, K_, G_) / (ms["pack_sym"] * 1e-3) / 1e9},
         "gemv_m1": {"us": ms["gemv"] * 1e3, "GB/s": gemv_gbs},
         "gemm_m4096": {"us": ms["gemm"] * 1e3, "TFLOP/s": gemm_tf},
+        "context_torch_bf16_mm_m4096": {"us": ms["ref_mm"] * 1e3,
+                                        "TFLOP/s": gemm_flop / (ms["ref_mm"] * 1e-3) / 1e12},
         "pack8": {"us": ms["pack8"] * 1e3,
                   "GB/s": (2 * N_ * K_ + N_ * K_ + (N_ * K_ // G_) * 5) / (ms["pack8"] * 1e-3) / 1e9},
         "gemv8_m1": {"us": ms["gemv8"] * 1e3,
