@@ -10,8 +10,9 @@
 // lanes cover a contiguous 1 KiB of each row; the 4 waves of a block stride over
 // the block's rows.  Every |x| (bf16, 8 significant bits) is added in fp64, so
 // the partial sums are exact unless a value is ~2^45 times smaller than its
-// channel's total.  Partials go to a workspace [row slices][K] and a second
-// kernel adds them in a fixed order, so the result is deterministic.
+// channel's total.  Partials go to a workspace [row slices][K] (about 1024 blocks
+// in all) and a second kernel adds them in a fixed order, so the result is
+// deterministic.
 #include "aq_device.h"
 #include "aq_kernels.h"
 
@@ -21,8 +22,8 @@ constexpr int kColsPerBlock = 512;
 
 int absmean_row_slices(int64_t T, int64_t K) {
   const int64_t kx = (K + kColsPerBlock - 1) / kColsPerBlock;
-  int64_t ts = (T + 63) / 64;                 // at least 64 rows (16 per wave) per block
-  const int64_t target = (2048 + kx - 1) / kx;  // about 2048 blocks in total
+  int64_t ts = (T + 127) / 128;                 // at least 128 rows (32 per wave) per block
+  const int64_t target = (1024 + kx - 1) / kx;  // about 1024 blocks in total
   if (ts > target) ts = target;
   if (ts < 1) ts = 1;
   return (int)ts;
@@ -43,12 +44,12 @@ __global__ __launch_bounds__(256) void absmean_partial_kernel(const uint16_t* __
   if (live) {
     const uint16_t* base = X + col0;
     int64_t t = t0 + wid;
-    for (; t + 12 < t1; t += 16) {
-      u32x4 w[4];
+    for (; t + 28 < t1; t += 32) {
+      u32x4 w[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) w[u] = *reinterpret_cast<const u32x4*>(base + (t + 4 * u) * (int64_t)K);
+      for (int u = 0; u < 8; ++u) w[u] = *reinterpret_cast<const u32x4*>(base + (t + 4 * u) * (int64_t)K);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 8; ++u)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           acc[2 * i] += (double)fabsf(bf16_lo(w[u][i]));
@@ -73,21 +74,33 @@ __global__ __launch_bounds__(256) void absmean_partial_kernel(const uint16_t* __
   }
 }
 
-// Finish: 32 channels per block, 8 threads per channel each adding every 8th row
-// slice; the 8 partial sums are then combined in a fixed order (deterministic).
+// Finish: 16 channels per block, 16 threads per channel each adding every 16th row
+// slice (eight loads in flight per batch); the 16 partial sums are then combined in
+// a fixed order (deterministic).
 __global__ __launch_bounds__(256) void absmean_finish_kernel(const double* __restrict__ part, int slices, int K,
                                                              double* __restrict__ sum_abs, float* __restrict__ mean,
                                                              double count) {
-  __shared__ double sm[8][32];
-  const int c = threadIdx.x & 31, r = threadIdx.x >> 5;
-  const int k = blockIdx.x * 32 + c;
+  __shared__ double sm[16][17];
+  const int c = threadIdx.x & 15, r = threadIdx.x >> 4;
+  const int k = blockIdx.x * 16 + c;
   double s = 0.0;
-  if (k < K)
-    for (int i = r; i < slices; i += 8) s += part[(int64_t)i * K + k];
+  if (k < K) {
+    int i = r;
+    for (; i + 16 * 7 < slices; i += 16 * 8) {
+      double v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)(i + 16 * u) * K + k];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; i < slices; i += 16) s += part[(int64_t)i * K + k];
+  }
   sm[r][c] = s;
   __syncthreads();
   if (r == 0 && k < K) {
-    const double tot_chunk = ((sm[0][c] + sm[1][c]) + (sm[2][c] + sm[3][c])) + ((sm[4][c] + sm[5][c]) + (sm[6][c] + sm[7][c]));
+    double tot_chunk = 0.0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) tot_chunk += sm[j][c];
     const double tot = sum_abs[k] + tot_chunk;
     sum_abs[k] = tot;
     if (mean) mean[k] = (float)(tot / count);
@@ -102,7 +115,7 @@ hipError_t launch_act_absmean(const uint16_t* X, int64_t T, int64_t K, double* s
   hipLaunchKernelGGL(absmean_partial_kernel, grid, dim3(256), 0, stream, X, T, (int)K, rows, work);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(absmean_finish_kernel, dim3((unsigned)((K + 31) / 32)), dim3(256), 0, stream, work, slices,
+  hipLaunchKernelGGL(absmean_finish_kernel, dim3((unsigned)((K + 15) / 16)), dim3(256), 0, stream, work, slices,
                      (int)K, sum_abs, mean, (double)count);
   return hipGetLastError();
 }

@@ -82,7 +82,15 @@ __global__ __launch_bounds__(kAmaxThreads) void fp4_amax_partial_kernel(const vo
 __global__ __launch_bounds__(kAmaxThreads) void fp4_amax_finish_kernel(const float* __restrict__ partial, int n,
                                                                          float* __restrict__ ts) {
   float m = 0.0f;
-  for (int i = threadIdx.x; i < n; i += kAmaxThreads) m = fmaxf(m, partial[i]);
+  int i = threadIdx.x;
+  for (; i + 7 * kAmaxThreads < n; i += 8 * kAmaxThreads) {   // eight loads in flight
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = partial[i + u * kAmaxThreads];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m = fmaxf(m, v[u]);
+  }
+  for (; i < n; i += kAmaxThreads) m = fmaxf(m, partial[i]);
   m = block_max(m);
   if (threadIdx.x == 0) {
     const float t = m / 2688.0f;
