@@ -120,13 +120,17 @@ hipError_t launch_cfg8(const uint16_t* X, const uint8_t* C, const float* S, cons
   return hipGetLastError();
 }
 
-// Rows of up to 2048 codes take one batch of two chunks per lane (two rows per wave
-// for M <= 4); longer rows one row per wave with six chunks per lane in flight.
+// Rows of up to 2048 codes: four rows per wave, one chunk per lane and row in flight
+// (M <= 4; measured on [11008, 2048]: 6.5 us at M = 1 against 7.2 us with two rows
+// and two chunks), else one row per wave with both chunks; longer rows one row per
+// wave with six chunks per lane in flight (the best of 1-4 rows on [2048, 11008]).
 template <int M>
 hipError_t launch_m8(const uint16_t* X, const uint8_t* C, const float* S, const uint8_t* Z, float* Y, int N, int K,
                      int gshift, hipStream_t stream) {
-  constexpr int R = M <= 4 ? 2 : 1;
-  if ((K >> 4) <= 128) return launch_cfg8<M, R, 2>(X, C, S, Z, Y, N, K, gshift, stream);
+  if ((K >> 4) <= 128) {
+    if constexpr (M <= 4) return launch_cfg8<M, 4, 1>(X, C, S, Z, Y, N, K, gshift, stream);
+    return launch_cfg8<M, 1, 2>(X, C, S, Z, Y, N, K, gshift, stream);
+  }
   return launch_cfg8<M, 1, 6>(X, C, S, Z, Y, N, K, gshift, stream);
 }
 
