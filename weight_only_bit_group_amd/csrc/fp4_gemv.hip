@@ -11,7 +11,9 @@
 // v_cvt_scalef32_pk_bf16_fp4 (unit scale) turns one code byte into the exact bf16
 // pair (k, k + 1), which lines up with the activation pairs as loaded, so
 // v_dot2_f32_bf16 accumulates each 16-block and the fp32 block scale multiplies
-// the block sum once.
+// the block sum once.  For M <= 4 a chunk's activations are requested before its
+// codes and scales: loads return in order, so activations requested after the
+// weights would wait for the HBM stream.
 #include "aq_device.h"
 #include "aq_kernels.h"
 
@@ -45,7 +47,16 @@ __global__ __launch_bounds__(256) void fp4_gemv_kernel(const uint16_t* __restric
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[m][r] = 0.0f;
 
+  constexpr bool PX = M <= 4;   // activations requested ahead of the weights
   for (int c = lane; c < nchunk; c += 64) {
+    u32x4 xr[PX ? M : 1][4];
+    if constexpr (PX) {
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xr[m][i] = reinterpret_cast<const u32x4*>(X + (int64_t)m * K + (c << 5))[i];
+      asm volatile("" ::: "memory");
+    }
     u32x4 code[R];
     float bs[R][2];
 #pragma unroll
@@ -56,6 +67,7 @@ __global__ __launch_bounds__(256) void fp4_gemv_kernel(const uint16_t* __restric
       bs[r][0] = __builtin_amdgcn_cvt_f32_fp8((int)two, 0);
       bs[r][1] = __builtin_amdgcn_cvt_f32_fp8((int)two, 1);
     }
+    asm volatile("" ::: "memory");
     uint32_t deq[R][16];
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -69,7 +81,7 @@ __global__ __launch_bounds__(256) void fp4_gemv_kernel(const uint16_t* __restric
       uint32_t xw[16];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const u32x4 t = xp4[i];
+        const u32x4 t = PX ? xr[PX ? m : 0][i] : xp4[i];
         xw[4 * i] = t[0]; xw[4 * i + 1] = t[1]; xw[4 * i + 2] = t[2]; xw[4 * i + 3] = t[3];
       }
 #pragma unroll

@@ -14,7 +14,10 @@
 //    activation rows are shared by every wave and stay in the L2) and widened to
 //    fp32; each code byte becomes an fp32 integer (v_cvt_f32_ubyte), and x * q is
 //    exact in fp32 (8 x 8 significant bits).  The chunk sum is corrected by
-//    -z * sum(x) before the fp32 group step S is applied.
+//    -z * sum(x) before the fp32 group step S is applied.  For up to six chunk rows
+//    (M x CPL <= 6) a batch's activations are requested before its weights: loads
+//    return in order, so activations requested after the weights would wait for the
+//    HBM stream.
 //  * Each row's 64 lane partials are reduced with DPP; lane 63 writes the result.
 #include "aq_device.h"
 #include "aq_kernels.h"
@@ -59,8 +62,24 @@ __global__ __launch_bounds__(256) void w8a16_gemv_kernel(const uint16_t* __restr
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[m][r] = 0.0f;
 
+  constexpr bool PX = M * CPL <= 6;   // activations of a batch requested ahead of its weights
   for (int b = 0; b < nbatch; ++b) {
+    u32x4 xr[PX ? M : 1][PX ? CPL : 1][2];
+    if constexpr (PX) {
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        const int c = min(lane + 64 * (b * CPL + j), nchunk - 1);
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          const u32x4* xs16 = reinterpret_cast<const u32x4*>(X + (int64_t)m * K + (c << 4));
+          xr[m][j][0] = xs16[0];
+          xr[m][j][1] = xs16[1];
+        }
+      }
+      asm volatile("" ::: "memory");
+    }
     issue(b);
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       const int c = lane + 64 * (b * CPL + j);
@@ -68,7 +87,8 @@ __global__ __launch_bounds__(256) void w8a16_gemv_kernel(const uint16_t* __restr
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         const u32x4* xs16 = reinterpret_cast<const u32x4*>(X + (int64_t)m * K + (c << 4));
-        const u32x4 xa = xs16[0], xb = xs16[1];
+        const u32x4 xa = PX ? xr[PX ? m : 0][PX ? j : 0][0] : xs16[0];
+        const u32x4 xb = PX ? xr[PX ? m : 0][PX ? j : 0][1] : xs16[1];
         float x[16];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
