@@ -21,8 +21,9 @@ group 64):
   layer    a whole Qwen2.5-3B decoder layer: norm-group AWQ of    (module-level path)
            q|k|v and gate|up (joint search, 65536-token abs-mean,
            4096-token search) plus plain packing of o and down;
-           and the layer's seven decode GEMVs at M = 1, averaged
-           over a graph-replayed stack of 12 layers (536 MB)
+           and the layer's decode GEMVs at M = 1 (q|k|v and
+           gate|up fused: four launches per layer), averaged over
+           a graph-replayed stack of 12 layers (536 MB)
 
 Launches are bracketed by HIP events on the stream they run on (torch's current
 stream, which the binding passes to the library): one event pair per launch,
@@ -226,18 +227,27 @@ def main():
         return out
 
     qlayer = layer_awq()
-    # decode through a stack of LAYER_STACK layers x 7 linears (the AWQ-quantized layer first,
-    # then plainly packed ones): 536 MB of packed weights, so every launch reads HBM
-    stack = [{name: (m.packed, m.scales, m.zeros) for name, m in qlayer.items()}]
+    # decode through a stack of LAYER_STACK layers (the AWQ-quantized layer first, then
+    # plainly packed ones; 536 MB of packed weights, so every launch reads HBM), each as the
+    # four GEMVs of its fused modules: q|k|v and gate|up (the consumers of one norm, stacked
+    # with W4A16Linear.concat), o and down
+    fused_groups = (("q_proj", "k_proj", "v_proj"), ("o_proj",), ("gate_proj", "up_proj"), ("down_proj",))
+    k_in = {name: k for name, n, k in synth.LAYER_LINEARS}
+
+    def fuse(mods):
+        return [L.W4A16Linear.concat([mods[n] for n in names]) for names in fused_groups]
+
+    stack = [fuse(qlayer)]
     for _ in range(LAYER_STACK - 1):
-        stack.append({name: B.aq_quantize_pack(weight_bf16(n, k), G_) for name, n, k in synth.LAYER_LINEARS})
-    x_in = {name: acts_bf16(1, k, round(0.01 * k)) for name, n, k in synth.LAYER_LINEARS}
-    y_out = {name: torch.empty((1, n), dtype=torch.float32, device=dev) for name, n, k in synth.LAYER_LINEARS}
+        stack.append(fuse({name: L.W4A16Linear(*B.aq_quantize_pack(weight_bf16(n, k), G_), G_)
+                           for name, n, k in synth.LAYER_LINEARS}))
+    x_in = [acts_bf16(1, k_in[names[0]], round(0.01 * k_in[names[0]])) for names in fused_groups]
+    y_out = [torch.empty((1, f.out_features), dtype=torch.float32, device=dev) for f in stack[0]]
 
     def layer_decode():
         for lay in stack:
-            for name, _, _ in synth.LAYER_LINEARS:
-                B.aq_w4a16_gemv(x_in[name], *lay[name], G_, out=y_out[name])
+            for i, f in enumerate(lay):
+                B.aq_w4a16_gemv(x_in[i], f.packed, f.scales, f.zeros, G_, out=y_out[i])
 
     side2 = torch.cuda.Stream()
     side2.wait_stream(torch.cuda.current_stream())

@@ -115,6 +115,21 @@ def test_decoder_layer_norm_group_awq_and_module_swap():
                                                                    sc.view(np.uint32)) \
             and np.array_equal(host(m.zeros), zr), n
 
+    # the consumers of each norm fused into one module: every slice of its output equals the
+    # separate module's output (rows are independent), at the GEMV and GEMM sizes
+    for names in (("q_proj", "k_proj", "v_proj"), ("gate_proj", "up_proj")):
+        fused = L.W4A16Linear.concat([mods[n] for n in names])
+        assert fused.split_sizes == [mods[n].out_features for n in names]
+        for rows in (1, T_TEST):
+            step(f"fused {'|'.join(names)} forward, {rows} token(s)")
+            with torch.no_grad():
+                x = cap[names[0]][:rows].float()
+                parts = torch.split(fused(x), fused.split_sizes, -1)
+                for n, part in zip(names, parts):
+                    assert torch.equal(part, mods[n](x)), (n, rows)
+    with pytest.raises(ValueError):
+        L.W4A16Linear.concat([mods["q_proj"], mods["down_proj"]])   # different in_features
+
     # forward of the quantized layer (GEMM at T_TEST rows, GEMV at one row) against the oracle
     pq = dict(pt, ln1=ln1, ln2=ln2)
     po = dict(p, ln1=o1["norm"], ln2=o2["norm"])

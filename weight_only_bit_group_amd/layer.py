@@ -55,6 +55,7 @@ class W4A16Linear(torch.nn.Module):
         self.register_buffer("scales", scales.contiguous())
         self.register_buffer("zeros", zeros.contiguous())
         self.register_buffer("bias", None if bias is None else bias.detach().float().contiguous())
+        self.split_sizes = [self.out_features]
         self._ws = None
 
     @classmethod
@@ -64,6 +65,31 @@ class W4A16Linear(torch.nn.Module):
         sym=True packs the symmetric variant (same format, zero point 8)."""
         p, s, z = B.aq_quantize_pack(weight.detach().contiguous(), group, chan_scale, sym=sym)
         return cls(p, s, z, group, bias)
+
+    @classmethod
+    def concat(cls, mods) -> "W4A16Linear":
+        """One module over the stacked output rows of several W4A16Linear with the same input
+        size and group (the consumers of one norm, e.g. q|k|v or gate|up): one GEMV / GEMM
+        launch instead of one per module.  Output rows are computed independently, so each
+        slice of the result equals the separate module's output; ``split_sizes`` gives the
+        slice widths (``torch.split(y, m.split_sizes, -1)``)."""
+        mods = list(mods)
+        if not mods:
+            raise ValueError("nothing to concatenate")
+        k, g = mods[0].in_features, mods[0].group
+        for m in mods:
+            if not isinstance(m, W4A16Linear):
+                raise TypeError(f"expected W4A16Linear, got {type(m).__name__}")
+            if m.in_features != k or m.group != g:
+                raise ValueError("modules must share in_features and group")
+        bias = None
+        if any(m.bias is not None for m in mods):
+            bias = torch.cat([m.bias if m.bias is not None else
+                              torch.zeros(m.out_features, dtype=torch.float32, device=m.packed.device) for m in mods])
+        out = cls(torch.cat([m.packed for m in mods]), torch.cat([m.scales for m in mods]),
+                  torch.cat([m.zeros for m in mods]), g, bias)
+        out.split_sizes = [m.out_features for m in mods]
+        return out
 
     def _workspace(self, m: int):
         need = B.aq_w4a16_gemm_workspace(m, self.out_features, self.in_features, self.group)
