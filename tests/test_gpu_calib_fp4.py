@@ -162,7 +162,8 @@ def test_fp4_mlp_shapes(n, k):
     check_close(y[rows], fp4.forward(synth.bf16_bits_to_f32(x2[rows]), c, b, ts), f"fp4 [{n},{k}] M=2048 rows")
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 3, 32), (7, 130, 96), (16, 4100, 64), (17, 33, 160), (300, 257, 512)])
+@pytest.mark.parametrize("m,n,k", [(1, 3, 32), (7, 130, 96), (16, 4100, 64), (17, 33, 160), (300, 257, 512),
+                                   (1, 8195, 4096), (2, 4099, 160)])
 def test_fp4_ragged(m, n, k):
     rng = np.random.default_rng(m + n + k)
     c, b, ts = fp4.encode((rng.standard_normal((n, k)) * 0.02).astype(np.float32))

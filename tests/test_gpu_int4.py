@@ -133,8 +133,10 @@ def _exact_case(rng, m, n, k, g):
     return synth.f32_to_bf16_bits(x), x, int4.pack_nibbles(q), s, z
 
 
-@pytest.mark.parametrize("m,n,k,g", [(1, 64, 256, 64), (5, 33, 128, 32), (16, 130, 1024, 128)])
+@pytest.mark.parametrize("m,n,k,g", [(1, 64, 256, 64), (5, 33, 128, 32), (16, 130, 1024, 128), (1, 8195, 256, 64),
+                                     (1, 8197, 2048, 32)])
 def test_gemv_exact_integer_case(m, n, k, g):
+    """(N >= 8192 at M = 1 takes the four-rows-per-wave launch, here with a ragged last wave.)"""
     xb, x, p, s, z = _exact_case(np.random.default_rng(m + n + k), m, n, k, g)
     step(f"aq_w4a16_gemv exact-integer M={m} N={n} K={k} g={g}")
     y = host(B.aq_w4a16_gemv(dev_bf16(xb), dev(p), dev(s), dev(z), g))
@@ -142,7 +144,8 @@ def test_gemv_exact_integer_case(m, n, k, g):
     assert (y.astype(np.float64) == ref).all()
 
 
-@pytest.mark.parametrize("m,n,k,g", [(1, 1, 32, 32), (2, 7, 96, 32), (3, 4099, 320, 64), (16, 8200, 64, 64)])
+@pytest.mark.parametrize("m,n,k,g", [(1, 1, 32, 32), (2, 7, 96, 32), (3, 4099, 320, 64), (16, 8200, 64, 64),
+                                     (1, 8194, 512, 128), (1, 8199, 11008, 64)])
 def test_gemv_ragged_shapes(m, n, k, g):
     rng = np.random.default_rng(n)
     w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
