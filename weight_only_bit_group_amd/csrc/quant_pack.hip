@@ -28,6 +28,39 @@
 
 namespace aq {
 
+namespace {
+
+// The codes of one lane's eight values, each equal to group_code_q: the reciprocal
+// fast path for all eight, and the true division only in a branch taken when a value
+// of the lane lies within the tie slack of a half-integer (rare).  Written per
+// element, the compiler turns that branch into a division computed for every value
+// and a select.
+template <int QM>
+__device__ __forceinline__ void group_codes8(const float (&v)[8], const GroupQ& g, uint32_t (&q)[8]) {
+  float t[8];
+  bool near = false;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    t[i] = v[i] * g.inv;
+    const float fr = t[i] - __builtin_floorf(t[i]);
+    near |= !(fabsf(fr - 0.5f) > fabsf(t[i]) * 4.8e-7f + 1.2e-7f);
+  }
+  if (__builtin_expect(near, 0)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float fr = t[i] - __builtin_floorf(t[i]);
+      if (!(fabsf(fr - 0.5f) > fabsf(t[i]) * 4.8e-7f + 1.2e-7f)) t[i] = v[i] / g.S;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float c = fminf(fmaxf(__builtin_rintf(t[i]) + g.zf, 0.0f), (float)QM);
+    q[i] = g.S == 0.0f ? 0u : (uint32_t)c;
+  }
+}
+
+}  // namespace
+
 // MODE: 0 asymmetric INT4, 1 symmetric INT4, 2 asymmetric INT8.
 template <int G, bool BF16, bool SCALED, int MODE>
 __global__ __launch_bounds__(256) void quant_pack_kernel(const void* __restrict__ W,
@@ -82,10 +115,12 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(const void* __restrict_
     g = group_params_q<QM>(mn, mx);
   }
 
+  uint32_t q[8];
+  group_codes8<QM>(v, g, q);
   if constexpr (MODE == 2) {
     uint32_t b[2] = {0u, 0u};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) b[i >> 2] |= group_code_q<255>(v[i], g) << (8 * (i & 3));
+    for (int i = 0; i < 8; ++i) b[i >> 2] |= q[i] << (8 * (i & 3));
     if (!live) return;
     *reinterpret_cast<uint2*>(packed + e) = uint2{b[0], b[1]};
   } else {
@@ -93,8 +128,8 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(const void* __restrict_
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       // |v / S| <= 7 (1 + 2^-23), so rne(v / S) + 8 stays in 1 .. 15 and the 0 .. 15
-      // clamp of group_code is the -7 .. 7 clamp of the symmetric code
-      const uint32_t c = (SYM && g.S == 0.0f) ? 8u : group_code(v[i], g);
+      // clamp of the code is the -7 .. 7 clamp of the symmetric code
+      const uint32_t c = (SYM && g.S == 0.0f) ? 8u : q[i];
       word |= c << (4 * i);
     }
     if (!live) return;
@@ -146,6 +181,8 @@ __global__ __launch_bounds__(256) void quant_error_kernel(const void* __restrict
   mn = segment_min<LPG>(mn);
   mx = segment_max<LPG>(mx);
   const GroupQ g = group_params(mn, mx);
+  uint32_t qc[8];
+  group_codes8<15>(v, g, qc);
   uint32_t hi[4], lo[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -153,7 +190,7 @@ __global__ __launch_bounds__(256) void quant_error_kernel(const void* __restrict
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int j = 2 * i + h;
-      const float q = (float)group_code(v[j], g);
+      const float q = (float)qc[j];
       const float what = (q - g.zf) * g.S;
       const float err = what / s[j] - w[j];
       h16[h] = f32_to_bf16_rne(err);
