@@ -8,6 +8,8 @@ group 64):
            and its symmetric variant aq_quantize_pack_sym
   gemv     aq_w4a16_gemv at M = 1, once on each of 40 distinct   (decode; 40 copies =
            packed weight copies, so every launch reads HBM         520 MB > the 256 MB MALL)
+           and at M = 16 over the same copies (batched decode,
+           the matrix-core kernel)
   gemm     aq_w4a16_gemm at M = 4096                             (prefill, bf16 MFMA; staged
            path: weights dequantized into a workspace, then the GEMM)
   absmean  aq_act_absmean over 65536 x 2048 calibration tokens   (AWQ statistic)
@@ -264,7 +266,7 @@ def main():
     # context, not part of the path: torch's dense bf16 matmul (the vendor BLAS) on the prefill
     # shape with the unquantized bf16 weight, fp32 output like the W4A16 GEMM
     w_gate_t = w_gate.t()
-    events = {k: [] for k in ("ref_mm", "pack", "pack_sym", "pack8", "gemv8", "gemm8", "gemv", "gemm", "absmean", "search", "fp4_gemv", "fp4_gemm", "fp4_encode",
+    events = {k: [] for k in ("ref_mm", "pack", "pack_sym", "pack8", "gemv8", "gemm8", "gemv", "gemv16", "gemm", "absmean", "search", "fp4_gemv", "fp4_gemm", "fp4_encode",
                               "layer_awq", "layer_gemv")}
 
     def timed(name, record, fn):
@@ -295,6 +297,25 @@ def main():
     gemv_graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(gemv_graph):
         gemv_batch()
+    torch.cuda.synchronize()
+
+    # batched decode: the same 40 copies at M = 16 activation rows (the matrix-core path)
+    x16 = acts_bf16(16, K_, round(0.01 * K_))
+    y16 = torch.empty((16, N_), dtype=torch.float32, device=dev)
+
+    def gemv16_batch():
+        for (p, s, z) in copies:
+            B.aq_w4a16_gemv(x16, p, s, z, G_, out=y16)
+
+    side5 = torch.cuda.Stream()
+    side5.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side5):
+        gemv16_batch()
+    torch.cuda.current_stream().wait_stream(side5)
+    torch.cuda.synchronize()
+    gemv16_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gemv16_graph):
+        gemv16_batch()
     torch.cuda.synchronize()
 
     # INT8: the gate weight's 8-bit codes, 24 distinct copies for the rotating decode GEMV
@@ -338,6 +359,7 @@ def main():
         timed("pack_sym", record, lambda: B.aq_quantize_pack(w_gate, G_, packed=pk[0], scales=pk[1], zeros=pk[2],
                                                              sym=True))
         timed("gemv", record, gemv_graph.replay)
+        timed("gemv16", record, gemv16_graph.replay)
         timed("ref_mm", record, lambda: torch.mm(xg, w_gate_t, out_dtype=torch.float32))
         timed("pack8", record, lambda: B.aq_quantize_pack8(w_gate, G_, codes=pk8[0], scales=pk8[1], zeros=pk8[2]))
         timed("gemv8", record, gemv8_graph.replay)
@@ -367,6 +389,7 @@ def main():
 
     ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in events.items()}
     ms["gemv"] /= N_COPIES
+    ms["gemv16"] /= N_COPIES
     ms["gemv8"] /= N8_COPIES
     ms["fp4_gemv"] /= FP4_COPIES
     ms["layer_gemv"] /= LAYER_STACK
@@ -379,6 +402,8 @@ def main():
         "pack": {"us": ms["pack"] * 1e3, "GB/s": pack_bytes(N_, K_, G_) / (ms["pack"] * 1e-3) / 1e9},
         "pack_sym": {"us": ms["pack_sym"] * 1e3, "GB/s": pack_bytes(N_, K_, G_) / (ms["pack_sym"] * 1e-3) / 1e9},
         "gemv_m1": {"us": ms["gemv"] * 1e3, "GB/s": gemv_gbs},
+        "gemv_m16": {"us": ms["gemv16"] * 1e3,
+                     "GB/s": gemv_bytes(16, N_, K_, G_) / (ms["gemv16"] * 1e-3) / 1e9},
         "gemm_m4096": {"us": ms["gemm"] * 1e3, "TFLOP/s": gemm_tf},
         "context_torch_bf16_mm_m4096": {"us": ms["ref_mm"] * 1e3,
                                         "TFLOP/s": gemm_flop / (ms["ref_mm"] * 1e-3) / 1e12},

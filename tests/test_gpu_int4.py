@@ -134,9 +134,12 @@ def _exact_case(rng, m, n, k, g):
 
 
 @pytest.mark.parametrize("m,n,k,g", [(1, 64, 256, 64), (5, 33, 128, 32), (16, 130, 1024, 128), (1, 8195, 256, 64),
-                                     (1, 8197, 2048, 32)])
+                                     (1, 8197, 2048, 32), (8, 40, 4160, 64), (9, 33, 2080, 32), (12, 17, 4224, 128),
+                                     (16, 300, 32, 32)])
 def test_gemv_exact_integer_case(m, n, k, g):
-    """(N >= 8192 at M = 1 takes the four-rows-per-wave launch, here with a ragged last wave.)"""
+    """(N >= 8192 at M = 1 takes the four-rows-per-wave launch, here with a ragged last wave;
+    M >= 8 takes the matrix-core kernel, here over several 2048-k chunks, a ragged tail
+    chunk and a single group.)"""
     xb, x, p, s, z = _exact_case(np.random.default_rng(m + n + k), m, n, k, g)
     step(f"aq_w4a16_gemv exact-integer M={m} N={n} K={k} g={g}")
     y = host(B.aq_w4a16_gemv(dev_bf16(xb), dev(p), dev(s), dev(z), g))
@@ -145,7 +148,8 @@ def test_gemv_exact_integer_case(m, n, k, g):
 
 
 @pytest.mark.parametrize("m,n,k,g", [(1, 1, 32, 32), (2, 7, 96, 32), (3, 4099, 320, 64), (16, 8200, 64, 64),
-                                     (1, 8194, 512, 128), (1, 8199, 11008, 64)])
+                                     (1, 8194, 512, 128), (1, 8199, 11008, 64), (8, 8197, 2048, 64),
+                                     (13, 1001, 11008, 64), (10, 3, 6144, 128)])
 def test_gemv_ragged_shapes(m, n, k, g):
     rng = np.random.default_rng(n)
     w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)

@@ -15,6 +15,12 @@ hipError_t launch_quant_error(const void* W, bool w_bf16, const float* chan_scal
                               int group, hipStream_t stream);
 hipError_t launch_w4a16_gemv(const uint16_t* X, int M, int K, const uint8_t* P, const float* S, const uint8_t* Z,
                              int N, int group, float* Y, hipStream_t stream);
+// the same product on the matrix cores, M <= 16 (used by launch_w4a16_gemv from a few rows up)
+hipError_t launch_w4a16_gemv_mfma(const uint16_t* X, int M, int K, const uint8_t* P, const float* S,
+                                  const uint8_t* Z, int N, int group, float* Y, hipStream_t stream);
+// the VALU kernel only (any M <= 16)
+hipError_t launch_w4a16_gemv_valu(const uint16_t* X, int M, int K, const uint8_t* P, const float* S,
+                                  const uint8_t* Z, int N, int group, float* Y, hipStream_t stream);
 // `staged`: NULL for the fused kernel, else N * K bf16 of device memory that first
 // receives the dequantized weights (the staged GEMM then loads them like activations)
 hipError_t launch_w4a16_gemm(const uint16_t* X, int M, int K, const uint8_t* P, const float* S, const uint8_t* Z,

@@ -245,8 +245,8 @@ hipError_t launch_m(const uint16_t* X, const uint8_t* P, const float* S, const u
 
 }  // namespace
 
-hipError_t launch_w4a16_gemv(const uint16_t* X, int M, int K, const uint8_t* P, const float* S,
-                             const uint8_t* Z, int N, int group, float* Y, hipStream_t stream) {
+hipError_t launch_w4a16_gemv_valu(const uint16_t* X, int M, int K, const uint8_t* P, const float* S,
+                                  const uint8_t* Z, int N, int group, float* Y, hipStream_t stream) {
   const int gshift = group == 32 ? 5 : group == 64 ? 6 : 7;
   switch (M) {
 #define AQ_CASE(mm) case mm: return launch_m<mm>(X, P, S, Z, Y, N, K, gshift, stream);
@@ -255,6 +255,16 @@ hipError_t launch_w4a16_gemv(const uint16_t* X, int M, int K, const uint8_t* P, 
 #undef AQ_CASE
     default: return hipErrorInvalidValue;
   }
+}
+
+// The VALU kernel up to 7 activation rows, the matrix-core kernel from 8 (measured on
+// the gate [11008, 2048], down [2048, 11008] and q [2048, 2048] shapes: the VALU
+// kernel's time grows with M and crosses the matrix-core kernel's at M = 6..8, e.g.
+// gate 17.1 against 8.2 us at M = 8 and 45 against 10 us at M = 16).
+hipError_t launch_w4a16_gemv(const uint16_t* X, int M, int K, const uint8_t* P, const float* S,
+                             const uint8_t* Z, int N, int group, float* Y, hipStream_t stream) {
+  if (M >= 8) return launch_w4a16_gemv_mfma(X, M, K, P, S, Z, N, group, Y, stream);
+  return launch_w4a16_gemv_valu(X, M, K, P, S, Z, N, group, Y, stream);
 }
 
 }  // namespace aq
