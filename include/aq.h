@@ -88,9 +88,9 @@ aq_status aq_quantize_pack_sym(const void* W, int32_t w_dtype, int64_t N, int64_
                                void* stream);
 
 /*
- * W4A16 decode GEMV, 1 <= M <= 16 activation rows.  Up to 7 rows a VALU kernel
- * (HBM-bound at M = 1); from 8 rows a matrix-core kernel (16x16x32 bf16 MFMA on the
- * exact integers q - z), whose time grows little with M.
+ * W4A16 decode GEMV, 1 <= M <= 16 activation rows.  For a few rows a VALU kernel
+ * (HBM-bound at M = 1); from 8 rows (5 when N >= 8192) a matrix-core kernel
+ * (16x16x32 bf16 MFMA on the exact integers q - z), whose time grows little with M.
  * Source: "模型量化指南" (blog.yoooo.fun), common conventions (the packed linear
  * dequantizes in memory and equals the original layer with W replaced by its
  * dequantized value); "Quantization：模型量化" (xingyuwang.me), sections 4 (W4A16)

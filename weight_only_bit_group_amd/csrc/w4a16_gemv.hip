@@ -257,13 +257,14 @@ hipError_t launch_w4a16_gemv_valu(const uint16_t* X, int M, int K, const uint8_t
   }
 }
 
-// The VALU kernel up to 7 activation rows, the matrix-core kernel from 8 (measured on
-// the gate [11008, 2048], down [2048, 11008] and q [2048, 2048] shapes: the VALU
-// kernel's time grows with M and crosses the matrix-core kernel's at M = 6..8, e.g.
-// gate 17.1 against 8.2 us at M = 8 and 45 against 10 us at M = 16).
+// The VALU kernel for a few activation rows, the matrix-core kernel for more (measured
+// on the gate [11008, 2048], down [2048, 11008] and q [2048, 2048] shapes: the VALU
+// kernel's time grows with M and crosses the matrix-core kernel's between M = 4 and 6
+// over N = 11008 (7.1 against 8.1 us at M = 4, 12.8 against 8.2 at M = 6) and near
+// M = 8 over N = 2048 (q: 5.4 against 5.3 us); at M = 16, 45 against 10 us on gate).
 hipError_t launch_w4a16_gemv(const uint16_t* X, int M, int K, const uint8_t* P, const float* S,
                              const uint8_t* Z, int N, int group, float* Y, hipStream_t stream) {
-  if (M >= 8) return launch_w4a16_gemv_mfma(X, M, K, P, S, Z, N, group, Y, stream);
+  if (M >= 8 || (M >= 5 && N >= 8192)) return launch_w4a16_gemv_mfma(X, M, K, P, S, Z, N, group, Y, stream);
   return launch_w4a16_gemv_valu(X, M, K, P, S, Z, N, group, Y, stream);
 }
 
