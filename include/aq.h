@@ -202,7 +202,8 @@ aq_status aq_quantize_pack8(const void* W, int32_t w_dtype, int64_t N, int64_t K
 /*
  * W8A16 products of the INT8 format: Y[m, n] = sum_g S[n, g] sum_{k in g}
  * X[m, k] (q[n, k] - z[n, g]), fp32 Y [M, N], X [M, K] bf16.
- * aq_w8a16_gemv: 1 <= M <= 16, VALU kernel (HBM-bound at M = 1).
+ * aq_w8a16_gemv: 1 <= M <= 16; VALU kernel up to 3 rows (HBM-bound at M = 1),
+ * 16x16x32 bf16 MFMA on the exact integers q - z from 4 rows.
  * aq_w8a16_gemm: any M; the codes are first dequantized exactly into the bf16
  * matrix (q - z) in `workspace` (N * K * 2 bytes, aq_w8a16_gemm_workspace,
  * 256-byte aligned, caller-owned, contents unspecified afterwards), then a
@@ -220,8 +221,9 @@ aq_status aq_w8a16_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_t* 
 
 /*
  * FP4 decode product: E2M1 codes with an FP8-E4M3 scale per 16-element block
- * and an fp32 tensor scale.  M <= 16 runs a VALU GEMV, larger M a bf16-MFMA
- * GEMM; both use the exact bf16 value e2m1 * e4m3.
+ * and an fp32 tensor scale.  M <= 16 runs a decode kernel (VALU up to 3 rows,
+ * 16x16x32 bf16 MFMA from 4 rows when K % 64 == 0), larger M a bf16-MFMA GEMM; all
+ * use the exact bf16 value e2m1 * e4m3.
  * Source: "Lance-Quant" (zingnex.cn), grid-search / grouping section (NVFP4 =
  * E2M1 codes + FP8 E4M3 scale per 16 elements, block_size 16);
  * "Quantization：模型量化" (xingyuwang.me), section 12 (E4M3 = 1 + 4 + 3 bits).

@@ -163,7 +163,7 @@ def test_fp4_mlp_shapes(n, k):
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 3, 32), (7, 130, 96), (16, 4100, 64), (17, 33, 160), (300, 257, 512),
-                                   (1, 8195, 4096), (2, 4099, 160)])
+                                   (1, 8195, 4096), (2, 4099, 160), (8, 8195, 4096), (12, 33, 2112), (4, 130, 64)])
 def test_fp4_ragged(m, n, k):
     rng = np.random.default_rng(m + n + k)
     c, b, ts = fp4.encode((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
@@ -190,7 +190,7 @@ def test_fp4_staged_equals_fused(m, n, k):
     check_close(ys, fp4.forward(synth.bf16_bits_to_f32(xb), c, b, ts), f"fp4 staged {m}x{n}x{k}")
 
 
-@pytest.mark.parametrize("m", [1, 5, 64, 300])
+@pytest.mark.parametrize("m", [1, 5, 16, 64, 300])
 def test_fp4_exact_case(m):
     """Small-integer X, every E2M1 code, block scales in {1/8 .. 4} and ts = 1: every product and
     partial sum is exact in fp32, so Y equals the fp64 reference bit for bit."""

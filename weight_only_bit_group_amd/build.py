@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libaq.so")
 
-HIP_SOURCES = ("quant_pack.hip", "w4a16_gemv.hip", "w4a16_gemv_mfma.hip", "mfma_gemm.hip", "act_absmean.hip",
+HIP_SOURCES = ("quant_pack.hip", "w4a16_gemv.hip", "decode_mfma.hip", "mfma_gemm.hip", "act_absmean.hip",
                "awq_search.hip", "fp4_gemv.hip", "fp4_quant.hip", "w8a16_gemv.hip")
 CPP_SOURCES = ("aq_api.cpp",)
 

@@ -15,9 +15,19 @@ hipError_t launch_quant_error(const void* W, bool w_bf16, const float* chan_scal
                               int group, hipStream_t stream);
 hipError_t launch_w4a16_gemv(const uint16_t* X, int M, int K, const uint8_t* P, const float* S, const uint8_t* Z,
                              int N, int group, float* Y, hipStream_t stream);
-// the same product on the matrix cores, M <= 16 (used by launch_w4a16_gemv from a few rows up)
+// the same products on the matrix cores, M <= 16 (used by the launch_*_gemv dispatchers
+// from a few rows up); FP4 needs K % 64 == 0
 hipError_t launch_w4a16_gemv_mfma(const uint16_t* X, int M, int K, const uint8_t* P, const float* S,
                                   const uint8_t* Z, int N, int group, float* Y, hipStream_t stream);
+hipError_t launch_w8a16_gemv_mfma(const uint16_t* X, int M, int K, const uint8_t* C, const float* S,
+                                  const uint8_t* Z, int N, int group, float* Y, hipStream_t stream);
+hipError_t launch_fp4_gemv_mfma(const uint16_t* X, int M, int K, const uint8_t* codes, const uint8_t* bscale,
+                                float ts, int N, float* Y, hipStream_t stream);
+// the VALU kernels only (any M <= 16)
+hipError_t launch_w8a16_gemv_valu(const uint16_t* X, int M, int K, const uint8_t* C, const float* S,
+                                  const uint8_t* Z, int N, int group, float* Y, hipStream_t stream);
+hipError_t launch_fp4_gemv_valu(const uint16_t* X, int M, int K, const uint8_t* codes, const uint8_t* bscale,
+                                float ts, int N, float* Y, hipStream_t stream);
 // the VALU kernel only (any M <= 16)
 hipError_t launch_w4a16_gemv_valu(const uint16_t* X, int M, int K, const uint8_t* P, const float* S,
                                   const uint8_t* Z, int N, int group, float* Y, hipStream_t stream);

@@ -119,8 +119,8 @@ static hipError_t launch_m(const uint16_t* X, const uint8_t* C, const uint8_t* B
   return hipGetLastError();
 }
 
-hipError_t launch_fp4_gemv(const uint16_t* X, int M, int K, const uint8_t* codes, const uint8_t* bscale,
-                           float ts, int N, float* Y, hipStream_t stream) {
+hipError_t launch_fp4_gemv_valu(const uint16_t* X, int M, int K, const uint8_t* codes, const uint8_t* bscale,
+                                float ts, int N, float* Y, hipStream_t stream) {
   switch (M) {
 #define AQ_CASE(mm) case mm: return launch_m<mm>(X, codes, bscale, ts, Y, N, K, stream);
     AQ_CASE(1) AQ_CASE(2) AQ_CASE(3) AQ_CASE(4) AQ_CASE(5) AQ_CASE(6) AQ_CASE(7) AQ_CASE(8)
@@ -128,6 +128,14 @@ hipError_t launch_fp4_gemv(const uint16_t* X, int M, int K, const uint8_t* codes
 #undef AQ_CASE
     default: return hipErrorInvalidValue;
   }
+}
+
+// The VALU kernel up to 3 activation rows, the matrix-core kernel from 4 when K % 64 == 0
+// (measured on [14336, 4096]: 18.9 against 16.8 us at M = 4, 62 against 23 us at M = 16).
+hipError_t launch_fp4_gemv(const uint16_t* X, int M, int K, const uint8_t* codes, const uint8_t* bscale,
+                           float ts, int N, float* Y, hipStream_t stream) {
+  if (M >= 4 && K % 64 == 0) return launch_fp4_gemv_mfma(X, M, K, codes, bscale, ts, N, Y, stream);
+  return launch_fp4_gemv_valu(X, M, K, codes, bscale, ts, N, Y, stream);
 }
 
 }  // namespace aq
