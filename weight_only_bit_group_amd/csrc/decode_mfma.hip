@@ -24,9 +24,13 @@
 //    G g + (G / 4) h, so the G / 32 MFMA steps of a group stay inside it and each
 //    group's partial is rescaled once by its fp32 step; for FP4 a lane's 16 k are
 //    one scale block.
-//  * Weights enter the MFMA exactly in bf16, in natural k order: the integers q - z
-//    (|q - z| <= 255 has at most 8 significant bits) or e2m1 * e4m3 (at most 6), so
-//    the activation operand is 8 consecutive bf16 of X loaded as they are.
+//  * Weights enter the MFMA exactly in bf16.  INT4: (code >> 4 s) & 0x000F000F |
+//    0x43004300 is the exact bf16 pair (128 + q_s, 128 + q_{s+4}) (two VALU ops per
+//    pair), the activation operand is permuted into the same (k, k + 4) pairs, and a
+//    second MFMA against the constant -(128 + z) removes the offset, every product and
+//    partial sum an exact integer times x.  INT8: the integers q - z (|q - z| <= 255,
+//    at most 8 significant bits); FP4: e2m1 * e4m3 (at most 6); both in natural k
+//    order, with the activation operand as loaded.
 //  * Block: 16 weight rows.  Per chunk of 2048 k the block loads the rows' codes
 //    and scales with contiguous 16-byte loads (whole cache lines per instruction)
 //    into LDS, where each lane reads its operands in the MFMA layout (rows padded
@@ -46,6 +50,16 @@ namespace {
 enum WFormat { WF_INT4 = 0, WF_INT8 = 1, WF_FP4 = 2 };
 
 constexpr int KC = 2048;   // k per chunk
+
+// (k, k + 4) pairing of 8 activations (four dwords of natural bf16 pairs).
+__device__ __forceinline__ u32x4 pair_k_k4(const u32x4 t) {
+  u32x4 p;
+  p[0] = __builtin_amdgcn_perm(t[2], t[0], 0x05040100u);
+  p[1] = __builtin_amdgcn_perm(t[2], t[0], 0x07060302u);
+  p[2] = __builtin_amdgcn_perm(t[3], t[1], 0x05040100u);
+  p[3] = __builtin_amdgcn_perm(t[3], t[1], 0x07060302u);
+  return p;
+}
 
 // n dwords from LDS (n = 1, 2, 4 or 8; 16-byte aligned for n >= 4)
 template <int NW>
@@ -188,16 +202,23 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const uint16_t* __rest
           zf = s_z.y;
         }
         f32x4 tmp = {0.0f, 0.0f, 0.0f, 0.0f};
+        // INT4: the bf16 pairs (128 + q_s, 128 + q_{s+4}) straight from the code dword,
+        // the activations in the same (k, k + 4) pair order, and a second MFMA with the
+        // constant -(128 + z) subtracting the offset (exact integers, see the header)
+        const uint32_t zb16 = __float_as_uint(-(128.0f + zf)) >> 16;
+        const u32x4 bz = {zb16 | (zb16 << 16), zb16 | (zb16 << 16), zb16 | (zb16 << 16), zb16 | (zb16 << 16)};
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
           u32x4 b;
           if constexpr (WF == WF_INT4) {
-            // codes k = 0 .. 7 of this step: even k in the low nibbles, odd k in the high ones
-            const uint32_t lo = wc[j] & 0x0F0F0F0Fu, hi = (wc[j] >> 4) & 0x0F0F0F0Fu;
-            b[0] = pack_bf16_exact(ubyte_f32<0>(lo) - zf, ubyte_f32<0>(hi) - zf);
-            b[1] = pack_bf16_exact(ubyte_f32<1>(lo) - zf, ubyte_f32<1>(hi) - zf);
-            b[2] = pack_bf16_exact(ubyte_f32<2>(lo) - zf, ubyte_f32<2>(hi) - zf);
-            b[3] = pack_bf16_exact(ubyte_f32<3>(lo) - zf, ubyte_f32<3>(hi) - zf);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) b[q] = ((wc[j] >> (4 * q)) & 0x000F000Fu) | 0x43004300u;
+            const u32x4 xk = pair_k_k4(xa[i][j]);
+            tmp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xk), __builtin_bit_cast(bf16x8, b),
+                                                           tmp, 0, 0, 0);
+            tmp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xk),
+                                                           __builtin_bit_cast(bf16x8, bz), tmp, 0, 0, 0);
+            continue;
           } else if constexpr (INT8) {
             const uint32_t w0 = wc[2 * j], w1 = wc[2 * j + 1];
             b[0] = pack_bf16_exact(ubyte_f32<0>(w0) - zf, ubyte_f32<1>(w0) - zf);
