@@ -28,7 +28,9 @@ group 64):
            a graph-replayed stack of 12 layers (536 MB)
 
 Launches are bracketed by HIP events on the stream they run on (torch's current
-stream, which the binding passes to the library): one event pair per launch,
+stream, which the binding passes to the library): one event pair per launch (five
+back-to-back calls for the short single-kernel rows: pack, pack_sym, pack8,
+absmean, fp4_encode, averaged per call),
 except the decode GEMV batches (INT4, INT8, FP4, the layer stack), which are
 captured once in a HIP graph and replayed back to back between one pair (as a
 decode loop does; eager Python launches would measure the binding's per-call
@@ -269,12 +271,21 @@ def main():
     events = {k: [] for k in ("ref_mm", "pack", "pack_sym", "pack8", "gemv8", "gemm8", "gemv", "gemv16", "gemm", "absmean", "search", "fp4_gemv", "fp4_gemm", "fp4_encode",
                               "layer_awq", "layer_gemv")}
 
+    # Short single-kernel rows run REPEAT identical calls back to back between one event
+    # pair (the host enqueues a call faster than the kernel runs, so the launches follow
+    # each other on the GPU) and report the average per call: one event pair around one
+    # ~20 us kernel would add the events' own overhead (several us) to it.
+    REPEAT = 5
+    repeated = ("pack", "pack_sym", "pack8", "absmean", "fp4_encode")
+
     def timed(name, record, fn):
+        reps = REPEAT if name in repeated else 1
         if record:
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record()
-            fn()
+            for _ in range(reps):
+                fn()
             b.record()
             events[name].append((a, b))
         else:
@@ -388,6 +399,8 @@ def main():
     print("[bench] timed region done", file=sys.stderr, flush=True)
 
     ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in events.items()}
+    for k in repeated:
+        ms[k] /= REPEAT
     ms["gemv"] /= N_COPIES
     ms["gemv16"] /= N_COPIES
     ms["gemv8"] /= N8_COPIES
