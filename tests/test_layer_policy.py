@@ -1,5 +1,6 @@
-"""The per-layer 4/8-bit policy: plan resolution and its fail-fast errors (CPU, no kernel is
-called), following "模型量化指南" (blog.yoooo.fun), "混合精度（按层 4/8-bit）" and "共同约定"."""
+"""The per-layer 4/8-bit policy: plan resolution and its fail-fast errors, following "模型量化指南"
+(blog.yoooo.fun), "混合精度（按层 4/8-bit）" and "共同约定"; and the stacking of one norm's consumers
+into one module (W4A16Linear.concat).  CPU only: no kernel is called."""
 import pytest
 import torch
 
@@ -60,3 +61,33 @@ def test_fail_fast_errors():
                             torch.zeros((64, 2), dtype=torch.uint8), 64)
     with pytest.raises(ValueError, match="already quantized"):
         plan_quantization(m, ("lm_head",))
+
+
+def _packed(n, k, g, bias=None, fill=0):
+    """A W4A16Linear over hand-made CPU buffers (no kernel runs: construction and concat only)."""
+    return W4A16Linear(torch.full((n, k // 2), fill, dtype=torch.uint8), torch.full((n, k // g), 0.5),
+                       torch.full((n, k // g), 3, dtype=torch.uint8), g, bias)
+
+
+def test_concat_stacks_rows_scales_zeros_and_biases():
+    q = _packed(8, 64, 32, bias=torch.arange(8, dtype=torch.float32), fill=1)
+    k = _packed(4, 64, 32, fill=2)                      # no bias: zeros in the stacked bias
+    v = _packed(4, 64, 32, bias=torch.ones(4), fill=3)
+    f = W4A16Linear.concat([q, k, v])
+    assert f.split_sizes == [8, 4, 4] and f.out_features == 16 and f.in_features == 64 and f.group == 32
+    assert torch.equal(f.packed, torch.cat([q.packed, k.packed, v.packed]))
+    assert torch.equal(f.scales, torch.cat([q.scales, k.scales, v.scales]))
+    assert torch.equal(f.zeros, torch.cat([q.zeros, k.zeros, v.zeros]))
+    assert torch.equal(f.bias, torch.cat([torch.arange(8, dtype=torch.float32), torch.zeros(4), torch.ones(4)]))
+    assert W4A16Linear.concat([k, k]).bias is None       # no module has a bias
+
+
+def test_concat_refuses_mismatched_modules():
+    with pytest.raises(ValueError, match="share in_features and group"):
+        W4A16Linear.concat([_packed(8, 64, 32), _packed(8, 128, 32)])
+    with pytest.raises(ValueError, match="share in_features and group"):
+        W4A16Linear.concat([_packed(8, 64, 32), _packed(8, 64, 64)])
+    with pytest.raises(TypeError):
+        W4A16Linear.concat([_packed(8, 64, 32), torch.nn.Linear(64, 8)])
+    with pytest.raises(ValueError):
+        W4A16Linear.concat([])
