@@ -37,7 +37,7 @@ namespace aq {
 
 namespace {
 
-constexpr int kLdsBytes = 48 * 1024;
+constexpr int kLdsBytes = 64 * 1024;
 
 // (k, k+4) pairing of one 8-activation dword quad: xw = 4 dwords of natural bf16 pairs.
 __device__ __forceinline__ u32x4 permute_pairs(const u32x4 t) {
