@@ -31,12 +31,12 @@
 //    partial sum an exact integer times x.  INT8: the integers q - z (|q - z| <= 255,
 //    at most 8 significant bits); FP4: e2m1 * e4m3 (at most 6); both in natural k
 //    order, with the activation operand as loaded.
-//  * Block: 16 weight rows.  Per chunk of 2048 k the block loads the rows' codes
-//    and scales with contiguous 16-byte loads (whole cache lines per instruction)
-//    into LDS, where each lane reads its operands in the MFMA layout (rows padded
-//    by 32 bytes so the 16 rows of one read fall on different banks); the chunk's
-//    groups are split over the 4 waves, whose partial results are added in LDS in a
-//    fixed order at the end (deterministic).  The next chunk's weights are in
+//  * Block: 16 weight rows, 4, 8 or 16 waves.  Per chunk of 2048 or 4096 k the
+//    block loads the rows' codes and scales with contiguous 16-byte loads (whole
+//    cache lines per instruction) into LDS, where each lane reads its operands in the
+//    MFMA layout (rows padded by 32 bytes so the 16 rows of one read fall on
+//    different banks); the chunk's groups are split over the waves, whose partial
+//    results are added in LDS in a fixed order at the end (deterministic).  The next chunk's weights are in
 //    flight while one is used; each wave's activation operands are requested
 //    before the weights (loads return in order, so L2-resident activations
 //    requested after the weights would wait for them).
@@ -48,8 +48,6 @@ namespace aq {
 namespace {
 
 enum WFormat { WF_INT4 = 0, WF_INT8 = 1, WF_FP4 = 2 };
-
-constexpr int KC = 2048;   // k per chunk
 
 // (k, k + 4) pairing of 8 activations (four dwords of natural bf16 pairs).
 __device__ __forceinline__ u32x4 pair_k_k4(const u32x4 t) {
@@ -78,8 +76,8 @@ __device__ __forceinline__ void lds_dwords(const uint8_t* p, uint32_t (&w)[NW]) 
   }
 }
 
-template <int WF, int G>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(const uint16_t* __restrict__ X, int M,
+template <int WF, int G, int NWV, int KC>
+__global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const uint16_t* __restrict__ X, int M,
                                                            const uint8_t* __restrict__ C,
                                                            const float* __restrict__ S,
                                                            const uint8_t* __restrict__ Z, float ts,
@@ -87,18 +85,20 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const uint16_t* __rest
   constexpr bool INT8 = WF == WF_INT8, FP4 = WF == WF_FP4;
   constexpr int CB = INT8 ? KC : KC / 2;   // code bytes per row and full chunk
   constexpr int CROW = CB + 32;            // LDS bytes per row of codes
-  constexpr int NL = CB / 256;             // 16-byte code loads per thread and chunk
+  constexpr int TPR = 4 * NWV;             // loading threads per weight row (64 NWV threads, 16 rows)
+  constexpr int NL = CB / (16 * TPR);      // 16-byte code loads per thread and chunk
   constexpr int NJ = G / 32;               // MFMA steps per group
   constexpr int NW = INT8 ? 2 * NJ : NJ;   // code dwords per lane and group
   constexpr int GPC = KC / G;              // groups per full chunk
-  constexpr int GPW = GPC / 4;             // groups per wave and full chunk
+  constexpr int GPW = GPC / NWV;           // groups per wave and full chunk
   constexpr int SZS = GPC + 1;             // INT4 / INT8: float2 per row of steps / zero points (+1: banks)
   constexpr int BSS = KC / 16 + 4;         // FP4: bytes per row of block scales
-  constexpr int SZL = FP4 ? 1 : (GPC + 15) / 16;   // scale loads per thread and chunk (FP4: 4 ushorts)
+  constexpr int SZL = FP4 ? 1 : (GPC + TPR - 1) / TPR;   // INT4 / INT8 step / zero-point loads per thread
+  constexpr int BPT = (KC / 16) / TPR;     // FP4: block-scale bytes per thread and full chunk (ushort loads)
   __shared__ __attribute__((aligned(16))) uint8_t cs[16 * CROW];
   __shared__ float2 sz[FP4 ? 1 : 16 * SZS];
   __shared__ uint8_t bsl[FP4 ? 16 * BSS : 4];
-  __shared__ f32x4 part[3][64];
+  __shared__ f32x4 part[NWV - 1][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wid = tid >> 6;
@@ -109,38 +109,38 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const uint16_t* __rest
   const bool xrow = r16 < M;               // activation rows past M are zero
   const uint16_t* xp = X + (int64_t)min(r16, M - 1) * K + (G / 4) * h;
 
-  // weight loads of one chunk: thread t takes row t / 16; its 16 lanes cover 256
+  // weight loads of one chunk: thread t takes row t / TPR; its TPR lanes cover 16 TPR
   // contiguous bytes of the row per load; INT4 / INT8 steps and zero points: groups
-  // (t % 16) + 16 i; FP4 block scales: 8 bytes (t % 16) * 8 .. +7 as four ushorts
-  const int lrow = tid >> 4, lcol = tid & 15;
+  // (t % TPR) + TPR i; FP4 block scales: BPT bytes from (t % TPR) BPT, as ushorts
+  const int lrow = tid / TPR, lcol = tid % TPR;
   const int nl = min(n0 + lrow, N - 1);
   const uint8_t* pl = C + (int64_t)nl * rowbytes + 16 * lcol;
   struct WLoad {
     u32x4 c[NL];
     float s[SZL];
     uint32_t z[SZL];
-    uint32_t b[FP4 ? 4 : 1];
+    uint32_t b[FP4 ? BPT / 2 : 1];
   };
   auto cbytes = [&](int kc) { return INT8 ? kc : (kc >> 1); };
   auto load_w = [&](WLoad& w, int c0, int kc) {
     const int cb = cbytes(kc), coff = INT8 ? c0 : (c0 >> 1);
 #pragma unroll
     for (int i = 0; i < NL; ++i)
-      w.c[i] = (256 * i + 16 * lcol < cb) ? *reinterpret_cast<const u32x4*>(pl + coff + 256 * i)
-                                          : u32x4{0u, 0u, 0u, 0u};
+      w.c[i] = (16 * TPR * i + 16 * lcol < cb) ? *reinterpret_cast<const u32x4*>(pl + coff + 16 * TPR * i)
+                                               : u32x4{0u, 0u, 0u, 0u};
     if constexpr (FP4) {
       const int nb = kc >> 4;   // block scales in the chunk
       const uint8_t* bp = Z + (int64_t)nl * (K >> 4) + (c0 >> 4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int bb = min(8 * lcol + 2 * i, nb - 2);
+      for (int i = 0; i < BPT / 2; ++i) {
+        const int bb = min(BPT * lcol + 2 * i, nb - 2);
         w.b[i] = *reinterpret_cast<const uint16_t*>(bp + bb);
       }
     } else {
       const int g0 = c0 / G, gc = kc / G;
 #pragma unroll
       for (int i = 0; i < SZL; ++i) {
-        const int gg = g0 + min(lcol + 16 * i, gc - 1);
+        const int gg = g0 + min(lcol + TPR * i, gc - 1);
         w.s[i] = S[(int64_t)nl * ngroups + gg];
         w.z[i] = Z[(int64_t)nl * ngroups + gg];
       }
@@ -150,17 +150,19 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const uint16_t* __rest
     const int cb = cbytes(kc);
 #pragma unroll
     for (int i = 0; i < NL; ++i)
-      if (256 * i + 16 * lcol < cb) *reinterpret_cast<u32x4*>(&cs[lrow * CROW + 256 * i + 16 * lcol]) = w.c[i];
+      if (16 * TPR * i + 16 * lcol < cb)
+        *reinterpret_cast<u32x4*>(&cs[lrow * CROW + 16 * TPR * i + 16 * lcol]) = w.c[i];
     if constexpr (FP4) {
       const int nb = kc >> 4;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (8 * lcol + 2 * i < nb) *reinterpret_cast<uint16_t*>(&bsl[lrow * BSS + 8 * lcol + 2 * i]) = (uint16_t)w.b[i];
+      for (int i = 0; i < BPT / 2; ++i)
+        if (BPT * lcol + 2 * i < nb)
+          *reinterpret_cast<uint16_t*>(&bsl[lrow * BSS + BPT * lcol + 2 * i]) = (uint16_t)w.b[i];
     } else {
       const int gc = kc / G;
 #pragma unroll
       for (int i = 0; i < SZL; ++i) {
-        const int g = lcol + 16 * i;
+        const int g = lcol + TPR * i;
         if (g < gc) sz[lrow * SZS + g] = make_float2(w.s[i], (float)w.z[i]);
       }
     }
@@ -169,7 +171,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const uint16_t* __rest
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   u32x4 xa[GPW][NJ];
   auto load_x = [&](int c0, int kc) {
-    const int gc = kc / G, per = (gc + 3) / 4, ga = wid * per;
+    const int gc = kc / G, per = (gc + NWV - 1) / NWV, ga = wid * per;
 #pragma unroll
     for (int i = 0; i < GPW; ++i) {
       const int g = min(ga + i, gc - 1);
@@ -182,7 +184,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const uint16_t* __rest
   // chunk, and the wave's groups of the chunk are multiplied
   auto chunk = [&](WLoad& w, int c0) {
     const int kc = min(KC, K - c0);
-    const int gc = kc / G, per = (gc + 3) / 4, ga = wid * per, gb = min(gc, ga + per);
+    const int gc = kc / G, per = (gc + NWV - 1) / NWV, ga = wid * per, gb = min(gc, ga + per);
     __syncthreads();                 // the previous chunk's weights are no longer read
     store_w(w, kc);
     __syncthreads();
@@ -259,12 +261,12 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const uint16_t* __rest
   load_w(wl, 0, min(KC, K));
   for (int c0 = 0; c0 < K; c0 += KC) chunk(wl, c0);
 
-  // the four partial results added in a fixed order: ((w0 + w1) + w2) + w3
+  // the waves' partial results added in a fixed order: ((w0 + w1) + w2) + ...
   if (wid > 0) part[wid - 1][lane] = acc;
   __syncthreads();
   if (wid == 0) {
 #pragma unroll
-    for (int w = 0; w < 3; ++w) {
+    for (int w = 0; w < NWV - 1; ++w) {
       const f32x4 p = part[w][lane];
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[e] += p[e];
@@ -279,17 +281,38 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const uint16_t* __rest
   }
 }
 
+template <int WF, int G, int NWV, int KC>
+hipError_t launch_cfg(const uint16_t* X, int M, int K, const uint8_t* C, const float* S, const uint8_t* Z, float ts,
+                      int N, float* Y, hipStream_t stream) {
+  const dim3 grid((unsigned)((N + 15) / 16)), block(64 * NWV);
+  hipLaunchKernelGGL((decode_mfma_kernel<WF, G, NWV, KC>), grid, block, 0, stream, X, M, C, S, Z, ts, Y, N, K);
+  return hipGetLastError();
+}
+
+// Waves per block and chunk length (measured on gfx950, M = 4 .. 16):
+//  * rows longer than 2048 k: 16 waves over chunks of 4096 k -- a block's weights take
+//    half as many serial round trips to memory, and the extra waves share the
+//    dequantization (2048 x 11008 INT4: 13 us against 21 us with 4 waves and 2048 k);
+//  * shorter rows (one chunk): 8 waves over 2048 k -- the smaller LDS footprint keeps
+//    several blocks per compute unit; INT4 with many blocks (N >= 8192) is a little
+//    faster with 4 waves.
+template <int WF, int G>
+hipError_t launch_group(const uint16_t* X, int M, int K, const uint8_t* C, const float* S, const uint8_t* Z,
+                        float ts, int N, float* Y, hipStream_t stream) {
+  if (K > 2048) return launch_cfg<WF, G, 16, 4096>(X, M, K, C, S, Z, ts, N, Y, stream);
+  if (WF == WF_INT4 && N >= 8192) return launch_cfg<WF, G, 4, 2048>(X, M, K, C, S, Z, ts, N, Y, stream);
+  return launch_cfg<WF, G, 8, 2048>(X, M, K, C, S, Z, ts, N, Y, stream);
+}
+
 template <int WF>
 hipError_t launch_format(const uint16_t* X, int M, int K, const uint8_t* C, const float* S, const uint8_t* Z,
                          float ts, int N, int group, float* Y, hipStream_t stream) {
-  const dim3 grid((unsigned)((N + 15) / 16)), block(256);
   switch (group) {
-    case 32: hipLaunchKernelGGL((decode_mfma_kernel<WF, 32>), grid, block, 0, stream, X, M, C, S, Z, ts, Y, N, K); break;
-    case 64: hipLaunchKernelGGL((decode_mfma_kernel<WF, 64>), grid, block, 0, stream, X, M, C, S, Z, ts, Y, N, K); break;
-    case 128: hipLaunchKernelGGL((decode_mfma_kernel<WF, 128>), grid, block, 0, stream, X, M, C, S, Z, ts, Y, N, K); break;
+    case 32: return launch_group<WF, 32>(X, M, K, C, S, Z, ts, N, Y, stream);
+    case 64: return launch_group<WF, 64>(X, M, K, C, S, Z, ts, N, Y, stream);
+    case 128: return launch_group<WF, 128>(X, M, K, C, S, Z, ts, N, Y, stream);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace
@@ -307,10 +330,7 @@ hipError_t launch_w8a16_gemv_mfma(const uint16_t* X, int M, int K, const uint8_t
 // FP4: K % 64 == 0 (groups of 64 k, each lane's 16 k one scale block)
 hipError_t launch_fp4_gemv_mfma(const uint16_t* X, int M, int K, const uint8_t* codes, const uint8_t* bscale,
                                 float ts, int N, float* Y, hipStream_t stream) {
-  const dim3 grid((unsigned)((N + 15) / 16)), block(256);
-  hipLaunchKernelGGL((decode_mfma_kernel<WF_FP4, 64>), grid, block, 0, stream, X, M, codes, nullptr, bscale, ts, Y,
-                     N, K);
-  return hipGetLastError();
+  return launch_group<WF_FP4, 64>(X, M, K, codes, nullptr, bscale, ts, N, Y, stream);
 }
 
 }  // namespace aq
