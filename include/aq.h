@@ -89,7 +89,7 @@ aq_status aq_quantize_pack_sym(const void* W, int32_t w_dtype, int64_t N, int64_
 
 /*
  * W4A16 decode GEMV, 1 <= M <= 16 activation rows.  For a few rows a VALU kernel
- * (HBM-bound at M = 1); from 8 rows (5 when N >= 8192) a matrix-core kernel
+ * (HBM-bound at M = 1); from 5 rows a matrix-core kernel
  * (16x16x32 bf16 MFMA on the exact integers q - z), whose time grows little with M.
  * Source: "模型量化指南" (blog.yoooo.fun), common conventions (the packed linear
  * dequantizes in memory and equals the original layer with W replaced by its
@@ -221,8 +221,8 @@ aq_status aq_w8a16_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_t* 
 
 /*
  * FP4 decode product: E2M1 codes with an FP8-E4M3 scale per 16-element block
- * and an fp32 tensor scale.  M <= 16 runs a decode kernel (VALU up to 3 rows,
- * 16x16x32 bf16 MFMA from 4 rows when K % 64 == 0), larger M a bf16-MFMA GEMM; all
+ * and an fp32 tensor scale.  M <= 16 runs a decode kernel (VALU up to 2 rows,
+ * 16x16x32 bf16 MFMA from 3 rows when K % 64 == 0), larger M a bf16-MFMA GEMM; all
  * use the exact bf16 value e2m1 * e4m3.
  * Source: "Lance-Quant" (zingnex.cn), grid-search / grouping section (NVFP4 =
  * E2M1 codes + FP8 E4M3 scale per 16 elements, block_size 16);

@@ -138,7 +138,7 @@ def _exact_case(rng, m, n, k, g):
                                      (16, 300, 32, 32), (7, 8195, 1024, 128), (16, 70, 8256, 32)])
 def test_gemv_exact_integer_case(m, n, k, g):
     """(N >= 8192 at M = 1 takes the four-rows-per-wave launch, here with a ragged last wave;
-    M >= 8 (M >= 5 when N >= 8192) takes the matrix-core kernel, here with 4, 8 and 16 waves per
+    M >= 5 takes the matrix-core kernel, here with 4, 8 and 16 waves per
     block, over several 4096-k chunks, a ragged tail chunk and a single group.)"""
     xb, x, p, s, z = _exact_case(np.random.default_rng(m + n + k), m, n, k, g)
     step(f"aq_w4a16_gemv exact-integer M={m} N={n} K={k} g={g}")

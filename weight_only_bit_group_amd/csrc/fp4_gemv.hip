@@ -130,11 +130,13 @@ hipError_t launch_fp4_gemv_valu(const uint16_t* X, int M, int K, const uint8_t* 
   }
 }
 
-// The VALU kernel up to 3 activation rows, the matrix-core kernel from 4 when K % 64 == 0
-// (measured on [14336, 4096]: 18.9 against 16.8 us at M = 4, 62 against 23 us at M = 16).
+// The VALU kernel up to 2 activation rows, the matrix-core kernel from 3 when K % 64 == 0
+// (measured at M = 3: 8.2 against 7.2 us on [11008, 2048], 7.4 against 6.7 on
+// [4096, 4096], 4.5 against 4.6 on [2048, 2048]; at M = 16 on [14336, 4096], 62 against
+// 23 us).  Rows with K % 64 != 0 take the VALU kernel at any M.
 hipError_t launch_fp4_gemv(const uint16_t* X, int M, int K, const uint8_t* codes, const uint8_t* bscale,
                            float ts, int N, float* Y, hipStream_t stream) {
-  if (M >= 4 && K % 64 == 0) return launch_fp4_gemv_mfma(X, M, K, codes, bscale, ts, N, Y, stream);
+  if (M >= 3 && K % 64 == 0) return launch_fp4_gemv_mfma(X, M, K, codes, bscale, ts, N, Y, stream);
   return launch_fp4_gemv_valu(X, M, K, codes, bscale, ts, N, Y, stream);
 }
 

@@ -222,9 +222,10 @@ hipError_t launch_cfg(const uint16_t* X, const uint8_t* P, const float* S, const
 template <int M>
 hipError_t launch_m(const uint16_t* X, const uint8_t* P, const float* S, const uint8_t* Z, float* Y, int N, int K,
                     int gshift, hipStream_t stream) {
+  static_assert(M >= 1 && M <= 4, "the VALU GEMV serves 1 .. 4 activation rows");
   const size_t lds = (size_t)M * (K >> 1) * 4 + (size_t)M * (K >> 3) * 4;
   const bool lds_x = lds <= (size_t)kLdsBytes;
-  constexpr int R = M <= 4 ? 2 : 1;
+  constexpr int R = 2;
   const int nchunk = K >> 5;
   if (lds_x) {
     if (nchunk <= 64) {
@@ -236,7 +237,7 @@ hipError_t launch_m(const uint16_t* X, const uint8_t* P, const float* S, const u
     // long rows (K > 4096, e.g. a down projection): one row per wave and up to six
     // chunks per lane in flight, so the whole row is requested at once and twice as
     // many waves share the HBM latency
-    if (M <= 4 && nchunk > 128) return launch_cfg<M, 1, 6, true>(X, P, S, Z, Y, N, K, gshift, stream);
+    if (nchunk > 128) return launch_cfg<M, 1, 6, true>(X, P, S, Z, Y, N, K, gshift, stream);
     return launch_cfg<M, R, 2, true>(X, P, S, Z, Y, N, K, gshift, stream);
   }
   if (nchunk <= 64) return launch_cfg<M, R, 1, false>(X, P, S, Z, Y, N, K, gshift, stream);
@@ -245,26 +246,26 @@ hipError_t launch_m(const uint16_t* X, const uint8_t* P, const float* S, const u
 
 }  // namespace
 
+// M = 1 .. 4 (more rows take the matrix-core kernel)
 hipError_t launch_w4a16_gemv_valu(const uint16_t* X, int M, int K, const uint8_t* P, const float* S,
                                   const uint8_t* Z, int N, int group, float* Y, hipStream_t stream) {
   const int gshift = group == 32 ? 5 : group == 64 ? 6 : 7;
   switch (M) {
 #define AQ_CASE(mm) case mm: return launch_m<mm>(X, P, S, Z, Y, N, K, gshift, stream);
-    AQ_CASE(1) AQ_CASE(2) AQ_CASE(3) AQ_CASE(4) AQ_CASE(5) AQ_CASE(6) AQ_CASE(7) AQ_CASE(8)
-    AQ_CASE(9) AQ_CASE(10) AQ_CASE(11) AQ_CASE(12) AQ_CASE(13) AQ_CASE(14) AQ_CASE(15) AQ_CASE(16)
+    AQ_CASE(1) AQ_CASE(2) AQ_CASE(3) AQ_CASE(4)
 #undef AQ_CASE
     default: return hipErrorInvalidValue;
   }
 }
 
-// The VALU kernel for a few activation rows, the matrix-core kernel for more (measured
-// on the gate [11008, 2048], down [2048, 11008] and q [2048, 2048] shapes: the VALU
-// kernel's time grows with M and crosses the matrix-core kernel's between M = 4 and 6
-// over N = 11008 (7.1 against 8.1 us at M = 4, 12.8 against 8.2 at M = 6) and near
-// M = 8 over N = 2048 (q: 5.4 against 5.3 us); at M = 16, 45 against 10 us on gate).
+// The VALU kernel up to 4 activation rows, the matrix-core kernel from 5 (measured on
+// the gate [11008, 2048], down [2048, 11008], q [2048, 2048] and [4096, 4096] shapes:
+// the VALU kernel's time grows with M; at M = 4 it is 7.1 against 7.3 us on gate and
+// 10.5 against 12.6 on down, at M = 5 10.9 against 7.7 on gate, 17.0 against 12.6 on
+// down and 4.1 against 4.2 on q; at M = 16 45 against 10 us on gate).
 hipError_t launch_w4a16_gemv(const uint16_t* X, int M, int K, const uint8_t* P, const float* S,
                              const uint8_t* Z, int N, int group, float* Y, hipStream_t stream) {
-  if (M >= 8 || (M >= 5 && N >= 8192)) return launch_w4a16_gemv_mfma(X, M, K, P, S, Z, N, group, Y, stream);
+  if (M >= 5) return launch_w4a16_gemv_mfma(X, M, K, P, S, Z, N, group, Y, stream);
   return launch_w4a16_gemv_valu(X, M, K, P, S, Z, N, group, Y, stream);
 }
 

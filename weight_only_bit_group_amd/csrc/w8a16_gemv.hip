@@ -141,35 +141,34 @@ hipError_t launch_cfg8(const uint16_t* X, const uint8_t* C, const float* S, cons
 }
 
 // Rows of up to 2048 codes: four rows per wave, one chunk per lane and row in flight
-// (M <= 4; measured on [11008, 2048]: 6.5 us at M = 1 against 7.2 us with two rows
-// and two chunks), else one row per wave with both chunks; longer rows one row per
-// wave with six chunks per lane in flight (the best of 1-4 rows on [2048, 11008]).
+// (measured on [11008, 2048]: 6.5 us at M = 1 against 7.2 us with two rows and two
+// chunks); longer rows one row per wave with six chunks per lane in flight (the best
+// of 1-4 rows on [2048, 11008]).
 template <int M>
 hipError_t launch_m8(const uint16_t* X, const uint8_t* C, const float* S, const uint8_t* Z, float* Y, int N, int K,
                      int gshift, hipStream_t stream) {
-  if ((K >> 4) <= 128) {
-    if constexpr (M <= 4) return launch_cfg8<M, 4, 1>(X, C, S, Z, Y, N, K, gshift, stream);
-    return launch_cfg8<M, 1, 2>(X, C, S, Z, Y, N, K, gshift, stream);
-  }
+  static_assert(M >= 1 && M <= 3, "the VALU W8A16 GEMV serves 1 .. 3 activation rows");
+  if ((K >> 4) <= 128) return launch_cfg8<M, 4, 1>(X, C, S, Z, Y, N, K, gshift, stream);
   return launch_cfg8<M, 1, 6>(X, C, S, Z, Y, N, K, gshift, stream);
 }
 
 }  // namespace
 
+// M = 1 .. 3 (more rows take the matrix-core kernel)
 hipError_t launch_w8a16_gemv_valu(const uint16_t* X, int M, int K, const uint8_t* C, const float* S,
                                   const uint8_t* Z, int N, int group, float* Y, hipStream_t stream) {
   const int gshift = group == 32 ? 5 : group == 64 ? 6 : 7;
   switch (M) {
 #define AQ_CASE(mm) case mm: return launch_m8<mm>(X, C, S, Z, Y, N, K, gshift, stream);
-    AQ_CASE(1) AQ_CASE(2) AQ_CASE(3) AQ_CASE(4) AQ_CASE(5) AQ_CASE(6) AQ_CASE(7) AQ_CASE(8)
-    AQ_CASE(9) AQ_CASE(10) AQ_CASE(11) AQ_CASE(12) AQ_CASE(13) AQ_CASE(14) AQ_CASE(15) AQ_CASE(16)
+    AQ_CASE(1) AQ_CASE(2) AQ_CASE(3)
 #undef AQ_CASE
     default: return hipErrorInvalidValue;
   }
 }
 
 // The VALU kernel up to 3 activation rows, the matrix-core kernel from 4 (measured on
-// [11008, 2048]: 9.4 against 9.0 us at M = 4, 32 against 11 us at M = 16).
+// [11008, 2048]: 7.7 against 8.6 us at M = 3, 9.8 against 8.9 at M = 4, 32 against 11
+// at M = 16; on [2048, 11008] 15.4 against 14.2 us at M = 4).
 hipError_t launch_w8a16_gemv(const uint16_t* X, int M, int K, const uint8_t* C, const float* S, const uint8_t* Z,
                              int N, int group, float* Y, hipStream_t stream) {
   if (M >= 4) return launch_w8a16_gemv_mfma(X, M, K, C, S, Z, N, group, Y, stream);
