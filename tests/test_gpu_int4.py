@@ -65,6 +65,10 @@ def _edge_matrix(rng, n, k, g):
     if n > 3:
         vg[3, 0] = 0.0                                # all-zero group
         vg[3, -1] *= np.float32(1e-30)                # tiny range
+    if n > 5:                                         # range of one ulp: |v / S| ~ 1.3e8 > 2^22,
+        one_up = np.nextafter(np.float32(1.0), np.float32(2.0))   # codes clamp to 15 / 0
+        vg[4, 0] = np.where(np.arange(g) % 3 == 0, one_up, np.float32(1.0))
+        vg[5, 0] = -vg[4, 0]
     return w
 
 

@@ -19,10 +19,10 @@
 // per weight (codes [N, K]).
 //
 // Mapping: W[N, K] row-major is a flat run of N*K/g groups of g contiguous
-// elements.  Each lane owns 8 consecutive elements (one 16-byte bf16 load or two
-// 16-byte fp32 loads), so a group spans g/8 lanes and its min/max is a
-// g/8-lane butterfly; a wave covers 512 elements.  Stores are 4 bytes of codes
-// per lane (256 contiguous bytes per wave), one fp32 S and one u8 z per group.
+// elements.  Each lane owns U units of 8 consecutive elements (one 16-byte bf16 load
+// or two 16-byte fp32 loads per unit), so a group spans g/(8U) lanes and its min/max
+// is a g/(8U)-lane butterfly.  Stores are 4U bytes of codes per lane (8U for 8-bit
+// codes, contiguous across the wave), one fp32 S and one u8 z per group.
 #include "aq_device.h"
 #include "aq_kernels.h"
 
@@ -30,78 +30,128 @@ namespace aq {
 
 namespace {
 
-// The codes of one lane's eight values, each equal to group_code_q: the reciprocal
-// fast path for all eight, and the true division only in a branch taken when a value
-// of the lane lies within the tie slack of a half-integer (rare).  Written per
-// element, the compiler turns that branch into a division computed for every value
-// and a select.
+constexpr float kRound = 12582912.0f;   // 1.5 * 2^23
+
+// Whether t (= v * (1/S)) may round differently from fl32(v / S): t is within 1.5 ulp
+// of the quotient, so only values near a half-integer can; with d = t - rne(t) (exact
+// for |t| < 2^22) that is 0.5 - |d| <= 4.8e-7 |t| + 1.2e-7 (about 4 ulp of t; NaN
+// counts as near).
+__device__ __forceinline__ bool near_tie(float t, float d) {
+  return !(fabsf(d) < __builtin_fmaf(fabsf(t), -4.8e-7f, 0.5f - 1.2e-7f));
+}
+
+// The codes of one lane's eight values, q = clamp(rne(fl32(v / S)) + z, 0, QM), each
+// returned as the bits of the float kRound + q (q in the low byte, the bits above it
+// constant).  rne comes from adding 1.5 * 2^23: the sum's unit in the last place is 1
+// while |t| < 2^22, and the constant is even, so halfway cases go to the even integer
+// as rne does; for larger |t| the sum is not rne(t), but then rne(t) + z lies far
+// outside 0 .. QM and the clamp (one v_med3 on kRound + 0 .. QM) gives the same code.
+// t = v * (1/S) for all eight, the true division only in a branch taken when a value
+// of the lane is near a tie (rare); written per element, the compiler would compute
+// the division for every value and select.  A constant group (S = 0) has 1/S = 0, so
+// t = 0 and the code is z (inputs are finite).
 template <int QM>
 __device__ __forceinline__ void group_codes8(const float (&v)[8], const GroupQ& g, uint32_t (&q)[8]) {
-  float t[8];
+  float t[8], r[8];
   bool near = false;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     t[i] = v[i] * g.inv;
-    const float fr = t[i] - __builtin_floorf(t[i]);
-    near |= !(fabsf(fr - 0.5f) > fabsf(t[i]) * 4.8e-7f + 1.2e-7f);
+    r[i] = t[i] + kRound;
+    near |= near_tie(t[i], t[i] - (r[i] - kRound));
   }
   if (__builtin_expect(near, 0)) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float fr = t[i] - __builtin_floorf(t[i]);
-      if (!(fabsf(fr - 0.5f) > fabsf(t[i]) * 4.8e-7f + 1.2e-7f)) t[i] = v[i] / g.S;
-    }
+    for (int i = 0; i < 8; ++i)
+      if (near_tie(t[i], t[i] - (r[i] - kRound))) r[i] = v[i] / g.S + kRound;
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float c = fminf(fmaxf(__builtin_rintf(t[i]) + g.zf, 0.0f), (float)QM);
-    q[i] = g.S == 0.0f ? 0u : (uint32_t)c;
-  }
+  for (int i = 0; i < 8; ++i)
+    q[i] = __float_as_uint(__builtin_amdgcn_fmed3f(r[i] + g.zf, kRound, kRound + (float)QM));
+}
+
+// Low bytes of four code words (as returned by group_codes8) as the bytes of one dword.
+__device__ __forceinline__ uint32_t bytes4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x0C0C0400u);   // a.b0, b.b0, 0, 0
+  const uint32_t hi = __builtin_amdgcn_perm(d, c, 0x0C0C0400u);   // c.b0, d.b0, 0, 0
+  return lo | (hi << 16);
+}
+// Eight 4-bit codes (even index in the low nibble of each byte) as one dword.
+__device__ __forceinline__ uint32_t nibbles8(const uint32_t (&q)[8]) {
+  uint32_t p[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) p[j] = q[2 * j] | (q[2 * j + 1] << 4);   // low byte: q0 | q1 << 4
+  return bytes4(p[0], p[1], p[2], p[3]);
 }
 
 }  // namespace
 
+// 8-element units per lane: two for the packing kernels (16 elements, two loads in
+// flight per lane, the group's parameters and lane reductions shared by twice the
+// elements: 17.4 -> 13.0 us on [11008, 2048] bf16), one for the error kernel (its
+// per-element division and bf16 splits make it slower with two: 30.6 against 32.4 us)
+constexpr int kPackU = 2;
+constexpr int kErrorU = 1;
+
+// One lane's U units of 8 consecutive elements as fp32 (times the channel scale
+// when one is given).
+template <int U, bool BF16, bool SCALED>
+__device__ __forceinline__ void load_units(const void* W, const float* chan_scale, int64_t e, int64_t K,
+                                           float (&v)[U][8]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (BF16) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(W) + e + 8 * u);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[u][2 * i] = bf16_lo(w[i]);
+        v[u][2 * i + 1] = bf16_hi(w[i]);
+      }
+    } else {
+      const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(W) + e + 8 * u);
+      const float4 a = p[0], b = p[1];
+      v[u][0] = a.x; v[u][1] = a.y; v[u][2] = a.z; v[u][3] = a.w;
+      v[u][4] = b.x; v[u][5] = b.y; v[u][6] = b.z; v[u][7] = b.w;
+    }
+  }
+  if (SCALED) {
+    const int64_t k0 = e % K;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float4* sp = reinterpret_cast<const float4*>(chan_scale + k0 + 8 * u);
+      const float4 a = sp[0], b = sp[1];
+      v[u][0] = v[u][0] * a.x; v[u][1] = v[u][1] * a.y; v[u][2] = v[u][2] * a.z; v[u][3] = v[u][3] * a.w;
+      v[u][4] = v[u][4] * b.x; v[u][5] = v[u][5] * b.y; v[u][6] = v[u][6] * b.z; v[u][7] = v[u][7] * b.w;
+    }
+  }
+}
+
 // MODE: 0 asymmetric INT4, 1 symmetric INT4, 2 asymmetric INT8.
-template <int G, bool BF16, bool SCALED, int MODE>
+template <int G, bool BF16, bool SCALED, int MODE, int U>
 __global__ __launch_bounds__(256) void quant_pack_kernel(const void* __restrict__ W,
                                                          const float* __restrict__ chan_scale,
                                                          uint8_t* __restrict__ packed,
                                                          float* __restrict__ scales,
                                                          uint8_t* __restrict__ zeros,
                                                          int64_t total, int64_t K) {
-  constexpr int LPG = G / 8;  // lanes per group
+  constexpr int EPL = 8 * U;     // elements per lane
+  constexpr int LPG = G / EPL;   // lanes per group
+  static_assert(LPG >= 1, "a lane's elements lie in one group");
   const int64_t lane_id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t e0 = lane_id * 8;
-  const bool live = e0 < total;
+  const int64_t e0 = lane_id * EPL;
+  const bool live = e0 < total;   // total is a multiple of G, so a live lane's EPL elements all exist
   const int64_t e = live ? e0 : 0;
 
-  float v[8];
-  if (BF16) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(W) + e);
+  float v[U][8];
+  load_units<U, BF16, SCALED>(W, chan_scale, e, K, v);
+  float mn = v[0][0], mx = v[0][0];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = bf16_lo(w[i]);
-      v[2 * i + 1] = bf16_hi(w[i]);
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      mn = fminf(mn, v[u][i]);
+      mx = fmaxf(mx, v[u][i]);
     }
-  } else {
-    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(W) + e);
-    const float4 a = p[0], b = p[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  }
-  if (SCALED) {
-    const int64_t k0 = e % K;
-    const float4* sp = reinterpret_cast<const float4*>(chan_scale + k0);
-    const float4 a = sp[0], b = sp[1];
-    v[0] = v[0] * a.x; v[1] = v[1] * a.y; v[2] = v[2] * a.z; v[3] = v[3] * a.w;
-    v[4] = v[4] * b.x; v[5] = v[5] * b.y; v[6] = v[6] * b.z; v[7] = v[7] * b.w;
-  }
-  float mn = v[0], mx = v[0];
-#pragma unroll
-  for (int i = 1; i < 8; ++i) {
-    mn = fminf(mn, v[i]);
-    mx = fmaxf(mx, v[i]);
-  }
   mn = segment_min<LPG>(mn);
   mx = segment_max<LPG>(mx);
   constexpr bool SYM = MODE == 1;
@@ -115,25 +165,32 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(const void* __restrict_
     g = group_params_q<QM>(mn, mx);
   }
 
-  uint32_t q[8];
-  group_codes8<QM>(v, g, q);
-  if constexpr (MODE == 2) {
-    uint32_t b[2] = {0u, 0u};
+  // symmetric: |v / S| <= 7 (1 + 2^-23), so rne(v / S) + 8 stays in 1 .. 15 and the
+  // 0 .. 15 clamp of the code is the -7 .. 7 clamp of the symmetric code; an all-zero
+  // group (S = 0, 1/S = 0) gets code 8
+  uint32_t out[MODE == 2 ? 2 * U : U];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) b[i >> 2] |= q[i] << (8 * (i & 3));
-    if (!live) return;
-    *reinterpret_cast<uint2*>(packed + e) = uint2{b[0], b[1]};
-  } else {
-    uint32_t word = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      // |v / S| <= 7 (1 + 2^-23), so rne(v / S) + 8 stays in 1 .. 15 and the 0 .. 15
-      // clamp of the code is the -7 .. 7 clamp of the symmetric code
-      const uint32_t c = (SYM && g.S == 0.0f) ? 8u : q[i];
-      word |= c << (4 * i);
+  for (int u = 0; u < U; ++u) {
+    uint32_t q[8];
+    group_codes8<QM>(v[u], g, q);
+    if constexpr (MODE == 2) {
+      out[2 * u] = bytes4(q[0], q[1], q[2], q[3]);
+      out[2 * u + 1] = bytes4(q[4], q[5], q[6], q[7]);
+    } else {
+      out[u] = nibbles8(q);
     }
-    if (!live) return;
-    *reinterpret_cast<uint32_t*>(packed + e / 2) = word;
+  }
+  if (!live) return;
+  constexpr int OUT_BYTES = MODE == 2 ? 8 * U : 4 * U;   // code bytes per lane
+  uint8_t* dst = packed + (MODE == 2 ? e : e / 2);
+  if constexpr (OUT_BYTES == 4) {
+    *reinterpret_cast<uint32_t*>(dst) = out[0];
+  } else if constexpr (OUT_BYTES == 8) {
+    *reinterpret_cast<uint2*>(dst) = uint2{out[0], out[1]};
+  } else {
+#pragma unroll
+    for (int i = 0; i < OUT_BYTES / 16; ++i)
+      *reinterpret_cast<u32x4*>(dst + 16 * i) = u32x4{out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]};
   }
   if ((threadIdx.x % LPG) == 0) {
     const int64_t grp = e / G;
@@ -147,70 +204,74 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(const void* __restrict_
 // after E_hi).  Same lane mapping and the same (bit-exact) group parameters and
 // codes as the packing kernel; the dequantized value (q - z) * S is divided by
 // s_k and the original weight subtracted in fp32.
-template <int G, bool BF16>
+template <int G, bool BF16, int U>
 __global__ __launch_bounds__(256) void quant_error_kernel(const void* __restrict__ W,
                                                           const float* __restrict__ chan_scale,
                                                           uint16_t* __restrict__ E, int64_t total, int64_t K) {
-  constexpr int LPG = G / 8;
+  constexpr int EPL = 8 * U;
+  constexpr int LPG = G / EPL;
+  static_assert(LPG >= 1, "a lane's elements lie in one group");
   const int64_t lane_id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t e0 = lane_id * 8;
+  const int64_t e0 = lane_id * EPL;
   const bool live = e0 < total;
   const int64_t e = live ? e0 : 0;
-  float w[8], v[8], s[8];
-  if (BF16) {
-    const u32x4 x = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(W) + e);
+  float w[U][8], v[U][8];
+  load_units<U, BF16, false>(W, nullptr, e, K, w);
+  const int64_t k0 = e % K;
+  float mn = 0.0f, mx = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { w[2 * i] = bf16_lo(x[i]); w[2 * i + 1] = bf16_hi(x[i]); }
-  } else {
-    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(W) + e);
-    const float4 a = p[0], b = p[1];
-    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w; w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
-  }
-  {
-    const float4* sp = reinterpret_cast<const float4*>(chan_scale + (e % K));
+  for (int u = 0; u < U; ++u) {
+    const float4* sp = reinterpret_cast<const float4*>(chan_scale + k0 + 8 * u);
     const float4 a = sp[0], b = sp[1];
-    s[0] = a.x; s[1] = a.y; s[2] = a.z; s[3] = a.w; s[4] = b.x; s[5] = b.y; s[6] = b.z; s[7] = b.w;
-  }
-  float mn, mx;
+    const float s[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    v[i] = w[i] * s[i];
-    mn = i ? fminf(mn, v[i]) : v[i];
-    mx = i ? fmaxf(mx, v[i]) : v[i];
+    for (int i = 0; i < 8; ++i) {
+      v[u][i] = w[u][i] * s[i];
+      mn = (u || i) ? fminf(mn, v[u][i]) : v[u][i];
+      mx = (u || i) ? fmaxf(mx, v[u][i]) : v[u][i];
+    }
   }
   mn = segment_min<LPG>(mn);
   mx = segment_max<LPG>(mx);
   const GroupQ g = group_params(mn, mx);
-  uint32_t qc[8];
-  group_codes8<15>(v, g, qc);
-  uint32_t hi[4], lo[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t h16[2], l16[2];
+  for (int u = 0; u < U; ++u) {
+    uint32_t qc[8];
+    group_codes8<15>(v[u], g, qc);
+    const float4* sp = reinterpret_cast<const float4*>(chan_scale + k0 + 8 * u);
+    const float4 a = sp[0], b = sp[1];
+    const float s[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t hi[4], lo[4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int j = 2 * i + h;
-      const float q = (float)qc[j];
-      const float what = (q - g.zf) * g.S;
-      const float err = what / s[j] - w[j];
-      h16[h] = f32_to_bf16_rne(err);
-      l16[h] = f32_to_bf16_rne(err - __uint_as_float(h16[h] << 16));
+    for (int i = 0; i < 4; ++i) {
+      uint32_t h16[2], l16[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int j = 2 * i + h;
+        const float what = (__uint_as_float(qc[j]) - (kRound + g.zf)) * g.S;   // (q - z) S, q - z exact
+        const float err = what / s[j] - w[u][j];
+        h16[h] = f32_to_bf16_rne(err);
+        l16[h] = f32_to_bf16_rne(err - __uint_as_float(h16[h] << 16));
+      }
+      hi[i] = h16[0] | (h16[1] << 16);
+      lo[i] = l16[0] | (l16[1] << 16);
     }
-    hi[i] = h16[0] | (h16[1] << 16);
-    lo[i] = l16[0] | (l16[1] << 16);
+    if (live) {
+      *reinterpret_cast<u32x4*>(E + e + 8 * u) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+      *reinterpret_cast<u32x4*>(E + total + e + 8 * u) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    }
   }
-  if (!live) return;
-  *reinterpret_cast<u32x4*>(E + e) = u32x4{hi[0], hi[1], hi[2], hi[3]};
-  *reinterpret_cast<u32x4*>(E + total + e) = u32x4{lo[0], lo[1], lo[2], lo[3]};
 }
 
 hipError_t launch_quant_error(const void* W, bool w_bf16, const float* chan_scale, uint16_t* E, int64_t N,
                               int64_t K, int group, hipStream_t stream) {
   const int64_t total = N * K;
-  const dim3 block(256), grid((unsigned)((total / 8 + 255) / 256));
+  const dim3 block(256), grid((unsigned)((total / (8 * kErrorU) + 255) / 256));
 #define AQ_QE(GG)                                                                                               \
-  if (w_bf16) hipLaunchKernelGGL((quant_error_kernel<GG, true>), grid, block, 0, stream, W, chan_scale, E, total, K); \
-  else hipLaunchKernelGGL((quant_error_kernel<GG, false>), grid, block, 0, stream, W, chan_scale, E, total, K);
+  if (w_bf16)                                                                                                   \
+    hipLaunchKernelGGL((quant_error_kernel<GG, true, kErrorU>), grid, block, 0, stream, W, chan_scale, E, total, K); \
+  else                                                                                                          \
+    hipLaunchKernelGGL((quant_error_kernel<GG, false, kErrorU>), grid, block, 0, stream, W, chan_scale, E, total, K);
   switch (group) {
     case 32: AQ_QE(32) break;
     case 64: AQ_QE(64) break;
@@ -224,16 +285,17 @@ hipError_t launch_quant_error(const void* W, bool w_bf16, const float* chan_scal
 template <int G, int MODE>
 static hipError_t launch_g(const void* W, bool bf16, const float* s, uint8_t* packed, float* scales,
                            uint8_t* zeros, int64_t N, int64_t K, hipStream_t stream) {
+  constexpr int U = kPackU;
   const int64_t total = N * K;
-  const int64_t lanes = total / 8;
+  const int64_t lanes = total / (8 * U);
   const dim3 block(256);
   const dim3 grid((unsigned)((lanes + 255) / 256));
   if (bf16) {
-    if (s) hipLaunchKernelGGL((quant_pack_kernel<G, true, true, MODE>), grid, block, 0, stream, W, s, packed, scales, zeros, total, K);
-    else hipLaunchKernelGGL((quant_pack_kernel<G, true, false, MODE>), grid, block, 0, stream, W, s, packed, scales, zeros, total, K);
+    if (s) hipLaunchKernelGGL((quant_pack_kernel<G, true, true, MODE, U>), grid, block, 0, stream, W, s, packed, scales, zeros, total, K);
+    else hipLaunchKernelGGL((quant_pack_kernel<G, true, false, MODE, U>), grid, block, 0, stream, W, s, packed, scales, zeros, total, K);
   } else {
-    if (s) hipLaunchKernelGGL((quant_pack_kernel<G, false, true, MODE>), grid, block, 0, stream, W, s, packed, scales, zeros, total, K);
-    else hipLaunchKernelGGL((quant_pack_kernel<G, false, false, MODE>), grid, block, 0, stream, W, s, packed, scales, zeros, total, K);
+    if (s) hipLaunchKernelGGL((quant_pack_kernel<G, false, true, MODE, U>), grid, block, 0, stream, W, s, packed, scales, zeros, total, K);
+    else hipLaunchKernelGGL((quant_pack_kernel<G, false, false, MODE, U>), grid, block, 0, stream, W, s, packed, scales, zeros, total, K);
   }
   return hipGetLastError();
 }
