@@ -18,8 +18,10 @@
 // Kernels: a grid-stride max of |w| into per-block partials, a one-block finish
 // that forms ts (max is order-free, so the result is deterministic), and the
 // encoder, one thread per 16-element block (64 or 32 contiguous bytes in, 8 bytes
-// of codes and one scale byte out).  All divisions are IEEE fp32 divisions and
-// the library is built without contraction, as the formulas above require.
+// of codes and one scale byte out).  Every quotient is the correctly rounded fp32
+// quotient (IEEE divisions, or a reciprocal with an fma correction that equals
+// them), and the library is built without contraction, as the formulas above
+// require.
 #include "aq_device.h"
 #include "aq_kernels.h"
 
@@ -117,10 +119,17 @@ __device__ __forceinline__ float e4m3_value(uint32_t b) {
 }
 
 // Nearest E2M1 magnitude code of r >= 0 over {0, .5, 1, 1.5, 2, 3, 4, 6}; exact
-// midpoints go to the even code, values from 6 up saturate to code 7.
+// midpoints go to the even code, values past 6 saturate to code 7.  Below 1 the grid
+// is the multiples of 0.5, so the code is rne(2 r) (the low bits of 2 r + 1.5 * 2^23,
+// one fma, exact); from 1 up the grid is the fp32 binades rounded to one mantissa
+// bit (1, 1.5 | 2, 3 | 4, 6 | 8 ..), so the code is the exponent : mantissa-bit pair
+// of r rounded to nearest even on its bit pattern, minus the pair of 1.0 (254) plus
+// 2, capped at 7.
 __device__ __forceinline__ uint32_t e2m1_code(float r) {
-  return (uint32_t)(r > 0.25f) + (uint32_t)(r >= 0.75f) + (uint32_t)(r > 1.25f) + (uint32_t)(r >= 1.75f) +
-         (uint32_t)(r > 2.5f) + (uint32_t)(r >= 3.5f) + (uint32_t)(r > 5.0f);
+  const uint32_t lo = __float_as_uint(__builtin_fmaf(r, 2.0f, 12582912.0f)) & 7u;
+  const uint32_t u = __float_as_uint(r);
+  const uint32_t hi = min(((u + 0x1FFFFFu + ((u >> 22) & 1u)) >> 22) - 252u, 7u);
+  return r < 1.0f ? lo : hi;
 }
 
 template <bool BF16>
@@ -139,18 +148,40 @@ __global__ __launch_bounds__(256) void fp4_encode_kernel(const void* __restrict_
   const float six_ts = 6.0f * ts;
   const uint32_t sb = e4m3_rne_sat(amax / six_ts);
   const float scale = e4m3_value(sb) * ts;
-  uint32_t q[16];
+  // r = fl32(|w| / scale) without a division per value: with inv = fl32(1 / scale),
+  // q0 = fl32(|w| inv) is within an ulp of the quotient, the remainder |w| - q0 scale
+  // is exact under fma, and fl32(q0 + rem inv) is the correctly rounded quotient
+  // (Markstein's theorem; it needs no underflow or overflow, which a scale in
+  // [2^-90, 2^90] guarantees wherever the quotient is near a code boundary).  Other
+  // scales take the divisions; a zero scale (all-zero block) gives codes 0.
+  uint32_t mag[16];
+  if (scale >= 0x1p-90f && scale <= 0x1p90f) {
+    const float inv = 1.0f / scale;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t mag = scale == 0.0f ? 0u : e2m1_code(fabsf(v[i]) / scale);
-    q[i] = (v[i] < 0.0f && mag != 0u) ? (mag | 8u) : mag;
+    for (int i = 0; i < 16; ++i) {
+      const float a = fabsf(v[i]);
+      const float q0 = a * inv;
+      const float rem = __builtin_fmaf(-q0, scale, a);
+      mag[i] = e2m1_code(__builtin_fmaf(rem, inv, q0));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mag[i] = scale == 0.0f ? 0u : e2m1_code(fabsf(v[i]) / scale);
   }
-  uint2 out;
-  out.x = q[0] | (q[1] << 4) | (q[2] << 8) | (q[3] << 12) | (q[4] << 16) | (q[5] << 20) | (q[6] << 24) |
-          (q[7] << 28);
-  out.y = q[8] | (q[9] << 4) | (q[10] << 8) | (q[11] << 12) | (q[12] << 16) | (q[13] << 20) | (q[14] << 24) |
-          (q[15] << 28);
-  *reinterpret_cast<uint2*>(codes + b * 8) = out;
+  // codes with the sign (bit 3) of the negative values whose magnitude code is not 0:
+  // (m + 7) & 8 is 8 exactly for m = 1 .. 7, and no nibble of m + 0x77777777 carries
+  uint32_t word[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t m = 0, sgn = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      m |= mag[8 * h + i] << (4 * i);
+      sgn |= (__float_as_uint(v[8 * h + i]) >> 31) << (4 * i + 3);
+    }
+    word[h] = m | (sgn & (m + 0x77777777u));
+  }
+  *reinterpret_cast<uint2*>(codes + b * 8) = uint2{word[0], word[1]};
   bscale[b] = (uint8_t)sb;
 }
 
