@@ -87,51 +87,4 @@ __device__ __forceinline__ float segment_max(float v) {
   return v;
 }
 
-// ---- group-wise asymmetric INT4 parameters --------------------------------
-// S = fl32(fl32(max - min) / 15); z = clamp(rne(fl32(-min / S)), 0, 15); a constant
-// group (S == 0) stores S = 0, z = 0 and codes 0.  All divisions are IEEE
-// correctly rounded (the library is compiled without fast-math, without
-// contraction, and with fp32 denormals preserved).
-struct GroupQ {
-  float S;
-  float zf;   // zero point as an exact float in 0..15 (0..255 for 8-bit codes)
-  float inv;  // correctly rounded 1/S (or 0 for a constant group)
-};
-
-// Asymmetric min-max parameters for the unsigned range 0 .. QM (15: INT4, 255: INT8):
-// S = fl32(fl32(max - min) / QM), z = clamp(rne(fl32(-min / S)), 0, QM).
-template <int QM>
-__device__ __forceinline__ GroupQ group_params_q(float mn, float mx) {
-  GroupQ g;
-  float r = mx - mn;
-  float s = r / (float)QM;
-  if (s == 0.0f) {
-    g.S = 0.0f; g.zf = 0.0f; g.inv = 0.0f;
-    return g;
-  }
-  float z = __builtin_rintf((-mn) / s);
-  z = fminf(fmaxf(z, 0.0f), (float)QM);
-  g.S = s; g.zf = z; g.inv = 1.0f / s;
-  return g;
-}
-__device__ __forceinline__ GroupQ group_params(float mn, float mx) { return group_params_q<15>(mn, mx); }
-
-// q = clamp(rne(fl32(v / S)) + z, 0, QM).
-// Fast path: t = v * (1/S) differs from fl32(v / S) by at most one ulp-scale
-// error, so rne(t) equals rne(fl32(v / S)) unless t lies within a few ulps of a
-// rounding boundary (a half-integer); only then is the true division done.
-template <int QM>
-__device__ __forceinline__ uint32_t group_code_q(float v, const GroupQ& g) {
-  if (g.S == 0.0f) return 0u;
-  float t = v * g.inv;
-  float fr = t - __builtin_floorf(t);
-  // |t - fl32(v/S)| <= 1.5 * 2^-23 |t|; t - floor(t) adds at most 2^-24 when -1 < t < 0.
-  float slack = fabsf(t) * 4.8e-7f + 1.2e-7f;
-  if (!(fabsf(fr - 0.5f) > slack)) t = v / g.S;   // also taken when 1/S overflowed (NaN)
-  float q = __builtin_rintf(t) + g.zf;
-  q = fminf(fmaxf(q, 0.0f), (float)QM);
-  return (uint32_t)q;
-}
-__device__ __forceinline__ uint32_t group_code(float v, const GroupQ& g) { return group_code_q<15>(v, g); }
-
 }  // namespace aq

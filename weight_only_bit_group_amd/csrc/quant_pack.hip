@@ -32,42 +32,92 @@ namespace {
 
 constexpr float kRound = 12582912.0f;   // 1.5 * 2^23
 
-// Whether t (= v * (1/S)) may round differently from fl32(v / S): t is within 1.5 ulp
-// of the quotient, so only values near a half-integer can; with d = t - rne(t) (exact
-// for |t| < 2^22) that is 0.5 - |d| <= 4.8e-7 |t| + 1.2e-7 (about 4 ulp of t; NaN
-// counts as near).
-__device__ __forceinline__ bool near_tie(float t, float d) {
-  return !(fabsf(d) < __builtin_fmaf(fabsf(t), -4.8e-7f, 0.5f - 1.2e-7f));
+// A group's parameters as the codes use them:
+//   S = fl32(fl32(max - min) / QM) (symmetric: fl32(max |v| / 7)),
+//   z = clamp(rne(fl32(-min / S)), 0, QM) (symmetric: 8),
+// all-zero range: S = 0, z = 0 (symmetric 8), codes z.
+struct PackQ {
+  float S;
+  float zf;    // zero point, an exact float
+  float inv;   // 1/S within 1 ulp (v_rcp_f32); 0 when S = 0
+  float thr;   // tie threshold of the group's values (see near_tie)
+  float kz;    // kRound + zf (exact)
+};
+
+// Whether t = v * inv may round differently from fl32(v / S): t is within 2 ulp of the
+// quotient (inv within 1 ulp of 1/S, the product rounded), so only t within about 4 ulp
+// of a half-integer can; with d = t - rne(t) (exact for |t| < 2^22) that is
+// |d| >= 0.5 - (4.8e-7 |t| + 1.2e-7).  The threshold is taken once per group, at its
+// largest |t| (so no smaller than any value's own slack); NaN (from a non-finite inv)
+// counts as near.
+__device__ __forceinline__ float tie_threshold(float tmax) { return __builtin_fmaf(tmax, -4.8e-7f, 0.5f - 1.2e-7f); }
+__device__ __forceinline__ bool near_tie(float d, float thr) { return !(fabsf(d) < thr); }
+
+// fl32(r / Q) for a constant Q: with y = fl32(1 / Q), q0 = fl32(r y) is within an ulp of
+// r / Q, and fl32(q0 + (r - q0 Q) y), the remainder exact under fma, is the correctly
+// rounded quotient (Markstein's theorem; it needs no underflow, hence the division
+// below 2^-100).
+template <int Q>
+__device__ __forceinline__ float div_const(float r) {
+  constexpr float y = 1.0f / (float)Q;
+  if (__builtin_expect(!(r >= 0x1p-100f), 0)) return r / (float)Q;
+  const float q0 = r * y;
+  return __builtin_fmaf(__builtin_fmaf(-q0, (float)Q, r), y, q0);
+}
+
+// Parameters of a group with minimum mn and maximum mx.  MODE: 0 asymmetric INT4,
+// 1 symmetric INT4, 2 asymmetric INT8.  z = rne(fl32(-mn / S)) is taken from
+// -mn * inv (sum with kRound, as for the codes) unless that is near a tie.
+template <int MODE>
+__device__ __forceinline__ PackQ pack_params(float mn, float mx) {
+  constexpr int QM = MODE == 2 ? 255 : 15;
+  const float amax = fmaxf(-mn, mx);   // max |v|
+  PackQ g;
+  g.S = MODE == 1 ? div_const<7>(amax) : div_const<QM>(mx - mn);
+  g.inv = g.S == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(g.S);
+  g.thr = tie_threshold(amax * g.inv);
+  if constexpr (MODE == 1) {
+    g.zf = 8.0f;
+  } else {
+    const float tz = -mn * g.inv;
+    float z = (tz + kRound) - kRound;
+    if (__builtin_expect(near_tie(tz - z, g.thr), 0)) z = __builtin_rintf(-mn / g.S);
+    g.zf = g.S == 0.0f ? 0.0f : fminf(fmaxf(z, 0.0f), (float)QM);
+  }
+  g.kz = kRound + g.zf;
+  return g;
 }
 
 // The codes of one lane's eight values, q = clamp(rne(fl32(v / S)) + z, 0, QM), each
 // returned as the bits of the float kRound + q (q in the low byte, the bits above it
 // constant).  rne comes from adding 1.5 * 2^23: the sum's unit in the last place is 1
 // while |t| < 2^22, and the constant is even, so halfway cases go to the even integer
-// as rne does; for larger |t| the sum is not rne(t), but then rne(t) + z lies far
-// outside 0 .. QM and the clamp (one v_med3 on kRound + 0 .. QM) gives the same code.
-// t = v * (1/S) for all eight, the true division only in a branch taken when a value
-// of the lane is near a tie (rare); written per element, the compiler would compute
-// the division for every value and select.  A constant group (S = 0) has 1/S = 0, so
-// t = 0 and the code is z (inputs are finite).
+// as rne does.  Away from ties rne(t) + z = rne(t + z), so the sum is taken with
+// kRound + z at once; a tie is always near (|d| = 1/2) and is redone in the branch,
+// rounded before z is added.  For larger |t| the sum is not rne(t), but then rne(t) + z
+// lies far outside 0 .. QM and the clamp (one v_med3 on kRound + 0 .. QM) gives the same
+// code.  t = v * inv for all eight, the true division only in a branch taken when a
+// value of the lane is near a tie (rare); written per element, the compiler would
+// compute the division for every value and select.  A constant group (S = 0) has
+// inv = 0, so t = 0 and the code is z (inputs are finite).
 template <int QM>
-__device__ __forceinline__ void group_codes8(const float (&v)[8], const GroupQ& g, uint32_t (&q)[8]) {
+__device__ __forceinline__ void group_codes8(const float (&v)[8], const PackQ& g, uint32_t (&q)[8]) {
   float t[8], r[8];
   bool near = false;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     t[i] = v[i] * g.inv;
-    r[i] = t[i] + kRound;
-    near |= near_tie(t[i], t[i] - (r[i] - kRound));
+    r[i] = t[i] + g.kz;
+    near |= near_tie(t[i] - (r[i] - g.kz), g.thr);
   }
   if (__builtin_expect(near, 0)) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (near_tie(t[i], t[i] - (r[i] - kRound))) r[i] = v[i] / g.S + kRound;
+      if (near_tie(t[i] - (r[i] - g.kz), g.thr)) r[i] = (v[i] / g.S + kRound) + g.zf;
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    q[i] = __float_as_uint(__builtin_amdgcn_fmed3f(r[i] + g.zf, kRound, kRound + (float)QM));
+    q[i] = __float_as_uint(__builtin_amdgcn_fmed3f(r[i], kRound, kRound + (float)QM));
 }
 
 // Low bytes of four code words (as returned by group_codes8) as the bytes of one dword.
@@ -154,16 +204,8 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(const void* __restrict_
     }
   mn = segment_min<LPG>(mn);
   mx = segment_max<LPG>(mx);
-  constexpr bool SYM = MODE == 1;
   constexpr int QM = MODE == 2 ? 255 : 15;
-  GroupQ g;
-  if constexpr (SYM) {
-    g.S = fmaxf(-mn, mx) / 7.0f;   // max |v| / 7 (fmaxf(-min, max) is max |v| exactly)
-    g.zf = 8.0f;
-    g.inv = g.S == 0.0f ? 0.0f : 1.0f / g.S;
-  } else {
-    g = group_params_q<QM>(mn, mx);
-  }
+  const PackQ g = pack_params<MODE>(mn, mx);
 
   // symmetric: |v / S| <= 7 (1 + 2^-23), so rne(v / S) + 8 stays in 1 .. 15 and the
   // 0 .. 15 clamp of the code is the -7 .. 7 clamp of the symmetric code; an all-zero
@@ -233,7 +275,7 @@ __global__ __launch_bounds__(256) void quant_error_kernel(const void* __restrict
   }
   mn = segment_min<LPG>(mn);
   mx = segment_max<LPG>(mx);
-  const GroupQ g = group_params(mn, mx);
+  const PackQ g = pack_params<0>(mn, mx);
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     uint32_t qc[8];
@@ -248,7 +290,7 @@ __global__ __launch_bounds__(256) void quant_error_kernel(const void* __restrict
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int j = 2 * i + h;
-        const float what = (__uint_as_float(qc[j]) - (kRound + g.zf)) * g.S;   // (q - z) S, q - z exact
+        const float what = (__uint_as_float(qc[j]) - g.kz) * g.S;   // (q - z) S, q - z exact
         const float err = what / s[j] - w[u][j];
         h16[h] = f32_to_bf16_rne(err);
         l16[h] = f32_to_bf16_rne(err - __uint_as_float(h16[h] << 16));
