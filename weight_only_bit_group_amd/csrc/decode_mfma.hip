@@ -189,10 +189,8 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const uint16_t* _
     store_w(w, kc);
     __syncthreads();
     if (c0 + KC < K) load_w(w, c0 + KC, min(KC, K - c0 - KC));   // next chunk's weights, in flight meanwhile
-#pragma unroll
-    for (int i = 0; i < GPW; ++i) {
-      const int g = ga + i;
-      if (g < gb) {   // uniform
+    // group g of the chunk, with the activation registers xa[i]
+    auto group = [&](int i, int g) {
         uint32_t wc[NW];
         lds_dwords<NW>(&cs[r16 * CROW + g * (INT8 ? G : G / 2) + (INT8 ? G / 4 : G / 8) * h], wc);
         float sc = 1.0f, zf = 0.0f;
@@ -251,7 +249,16 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const uint16_t* _
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(sc, tmp[e], acc[e]);
         }
-      }
+    };
+    if (gb - ga == GPW) {
+      // a full share (every wave of a full chunk): straight-line code, so the LDS reads
+      // and dequantization of the next groups can be scheduled under this group's MFMAs
+#pragma unroll
+      for (int i = 0; i < GPW; ++i) group(i, ga + i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < GPW; ++i)
+        if (ga + i < gb) group(i, ga + i);   // uniform
     }
     if (c0 + KC < K) load_x(c0 + KC, min(KC, K - c0 - KC));
   };
