@@ -7,7 +7,8 @@
 // xingyuwang.me, section 12: E4M3 = 1 + 4 + 3 bits).
 //
 // Design: as the INT4 GEMV -- one wave per R output rows, lane l reading the
-// 16-byte code chunks c = l, l + 64, ... (32 codes = two scale blocks).  gfx950's
+// 16-byte code chunks c = l, l + 64, ... (32 codes = two scale blocks), CPL of them
+// requested at once.  gfx950's
 // v_cvt_scalef32_pk_bf16_fp4 (unit scale) turns one code byte into the exact bf16
 // pair (k, k + 1), which lines up with the activation pairs as loaded, so
 // v_dot2_f32_bf16 accumulates each 16-block and the fp32 block scale multiplies
@@ -28,7 +29,7 @@ __device__ __forceinline__ uint32_t fp4_pair(uint32_t src, int sel) {
   }
 }
 
-template <int M, int R>
+template <int M, int R, int CPL>
 __global__ __launch_bounds__(256) void fp4_gemv_kernel(const uint16_t* __restrict__ X,
                                                         const uint8_t* __restrict__ C,
                                                         const uint8_t* __restrict__ B,
@@ -48,50 +49,69 @@ __global__ __launch_bounds__(256) void fp4_gemv_kernel(const uint16_t* __restric
     for (int r = 0; r < R; ++r) acc[m][r] = 0.0f;
 
   constexpr bool PX = M <= 4;   // activations requested ahead of the weights
-  for (int c = lane; c < nchunk; c += 64) {
-    u32x4 xr[PX ? M : 1][4];
+  // CPL chunks per lane in flight: chunks c0, c0 + 64, ..., all requested before any is used
+  for (int c0 = lane; c0 < nchunk; c0 += 64 * CPL) {
+    int cc[CPL];
+    bool ok[CPL];
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) {
+      ok[u] = c0 + 64 * u < nchunk;
+      cc[u] = min(c0 + 64 * u, nchunk - 1);   // in-bounds address for a lane past the row's end
+    }
+    u32x4 xr[CPL][PX ? M : 1][4];
     if constexpr (PX) {
 #pragma unroll
-      for (int m = 0; m < M; ++m)
+      for (int u = 0; u < CPL; ++u)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xr[m][i] = reinterpret_cast<const u32x4*>(X + (int64_t)m * K + (c << 5))[i];
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            xr[u][m][i] = reinterpret_cast<const u32x4*>(X + (int64_t)m * K + (cc[u] << 5))[i];
       asm volatile("" ::: "memory");
     }
-    u32x4 code[R];
-    float bs[R][2];
+    u32x4 code[CPL][R];
+    uint32_t two[CPL][R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int row = min(n0 + r, N - 1);
-      code[r] = *reinterpret_cast<const u32x4*>(C + (int64_t)row * kbytes + (c << 4));
-      const uint32_t two = *reinterpret_cast<const uint16_t*>(B + (int64_t)row * nblk + (c << 1));
-      bs[r][0] = __builtin_amdgcn_cvt_f32_fp8((int)two, 0);
-      bs[r][1] = __builtin_amdgcn_cvt_f32_fp8((int)two, 1);
-    }
-    asm volatile("" ::: "memory");
-    uint32_t deq[R][16];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) deq[r][4 * i + s] = fp4_pair(code[r][i], s);
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const u32x4* xp4 = reinterpret_cast<const u32x4*>(X + (int64_t)m * K + (c << 5));
-      uint32_t xw[16];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const u32x4 t = PX ? xr[PX ? m : 0][i] : xp4[i];
-        xw[4 * i] = t[0]; xw[4 * i + 1] = t[1]; xw[4 * i + 2] = t[2]; xw[4 * i + 3] = t[3];
-      }
+    for (int u = 0; u < CPL; ++u)
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        float d0 = 0.0f, d1 = 0.0f;
+        const int row = min(n0 + r, N - 1);
+        code[u][r] = *reinterpret_cast<const u32x4*>(C + (int64_t)row * kbytes + (cc[u] << 4));
+        two[u][r] = *reinterpret_cast<const uint16_t*>(B + (int64_t)row * nblk + (cc[u] << 1));
+      }
+    asm volatile("" ::: "memory");
 #pragma unroll
-        for (int j = 0; j < 8; ++j) d0 = dot2_bf16(deq[r][j], xw[j], d0);
+    for (int u = 0; u < CPL; ++u) {
+      if (!ok[u]) continue;
+      uint32_t deq[R][16];
+      float bs[R][2];
 #pragma unroll
-        for (int j = 8; j < 16; ++j) d1 = dot2_bf16(deq[r][j], xw[j], d1);
-        acc[m][r] = __builtin_fmaf(bs[r][1], d1, __builtin_fmaf(bs[r][0], d0, acc[m][r]));
+      for (int r = 0; r < R; ++r) {
+        bs[r][0] = __builtin_amdgcn_cvt_f32_fp8((int)two[u][r], 0);
+        bs[r][1] = __builtin_amdgcn_cvt_f32_fp8((int)two[u][r], 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int s = 0; s < 4; ++s) deq[r][4 * i + s] = fp4_pair(code[u][r][i], s);
+      }
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const u32x4* xp4 = reinterpret_cast<const u32x4*>(X + (int64_t)m * K + (cc[u] << 5));
+        uint32_t xw[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const u32x4 t = PX ? xr[u][PX ? m : 0][i] : xp4[i];
+          xw[4 * i] = t[0]; xw[4 * i + 1] = t[1]; xw[4 * i + 2] = t[2]; xw[4 * i + 3] = t[3];
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) d0 = dot2_bf16(deq[r][j], xw[j], d0);
+#pragma unroll
+          for (int j = 8; j < 16; ++j) d1 = dot2_bf16(deq[r][j], xw[j], d1);
+          acc[m][r] = __builtin_fmaf(bs[r][1], d1, __builtin_fmaf(bs[r][0], d0, acc[m][r]));
+        }
       }
     }
   }
@@ -105,18 +125,44 @@ __global__ __launch_bounds__(256) void fp4_gemv_kernel(const uint16_t* __restric
     }
 }
 
+template <int M, int R, int CPL>
+static hipError_t launch_cfg(const uint16_t* X, const uint8_t* C, const uint8_t* B, float ts, float* Y, int N,
+                             int K, hipStream_t stream) {
+  const int waves = (N + R - 1) / R;
+  hipLaunchKernelGGL((fp4_gemv_kernel<M, R, CPL>), dim3((waves + 3) / 4), dim3(256), 0, stream, X, C, B, ts, Y, N,
+                     K);
+  return hipGetLastError();
+}
+
+// Rows per wave by N (more rows per wave over a wide N); for one activation row, two
+// chunks per lane in flight, four over rows of more than 128 chunks (K > 4096), so a
+// wave's row is requested in one or two round trips (measured at M = 1: [4096, 14336]
+// 14.3 -> 9.9 us, [14336, 4096] 9.05 -> 8.9 us; at M = 2 the extra registers cost more
+// than they gain, so one chunk).
 template <int M>
 static hipError_t launch_m(const uint16_t* X, const uint8_t* C, const uint8_t* B, float ts, float* Y, int N,
                            int K, hipStream_t stream) {
-  int R = 1;
-  if (N >= 8192) R = 4;
-  else if (N >= 4096) R = 2;
-  const int waves = (N + R - 1) / R;
-  const dim3 grid((waves + 3) / 4), block(256);
-  if (R == 4) hipLaunchKernelGGL((fp4_gemv_kernel<M, 4>), grid, block, 0, stream, X, C, B, ts, Y, N, K);
-  else if (R == 2) hipLaunchKernelGGL((fp4_gemv_kernel<M, 2>), grid, block, 0, stream, X, C, B, ts, Y, N, K);
-  else hipLaunchKernelGGL((fp4_gemv_kernel<M, 1>), grid, block, 0, stream, X, C, B, ts, Y, N, K);
-  return hipGetLastError();
+  const int nchunk = K >> 5;
+  const int cpl = M == 1 ? (nchunk > 128 ? 4 : 2) : 1;
+  if (N >= 8192) {
+    if constexpr (M == 1) {
+      if (cpl == 4) return launch_cfg<M, 4, 4>(X, C, B, ts, Y, N, K, stream);
+      if (cpl == 2) return launch_cfg<M, 4, 2>(X, C, B, ts, Y, N, K, stream);
+    }
+    return launch_cfg<M, 4, 1>(X, C, B, ts, Y, N, K, stream);
+  }
+  if (N >= 4096) {
+    if constexpr (M == 1) {
+      if (cpl == 4) return launch_cfg<M, 2, 4>(X, C, B, ts, Y, N, K, stream);
+      if (cpl == 2) return launch_cfg<M, 2, 2>(X, C, B, ts, Y, N, K, stream);
+    }
+    return launch_cfg<M, 2, 1>(X, C, B, ts, Y, N, K, stream);
+  }
+  if constexpr (M == 1) {
+    if (cpl == 4) return launch_cfg<M, 1, 4>(X, C, B, ts, Y, N, K, stream);
+    if (cpl == 2) return launch_cfg<M, 1, 2>(X, C, B, ts, Y, N, K, stream);
+  }
+  return launch_cfg<M, 1, 1>(X, C, B, ts, Y, N, K, stream);
 }
 
 hipError_t launch_fp4_gemv_valu(const uint16_t* X, int M, int K, const uint8_t* codes, const uint8_t* bscale,
