@@ -140,15 +140,20 @@ hipError_t launch_cfg8(const uint16_t* X, const uint8_t* C, const float* S, cons
   return hipGetLastError();
 }
 
-// Rows of up to 2048 codes: four rows per wave, one chunk per lane and row in flight
-// (measured on [11008, 2048]: 6.5 us at M = 1 against 7.2 us with two rows and two
-// chunks); longer rows one row per wave with six chunks per lane in flight (the best
-// of 1-4 rows on [2048, 11008]).
+// Rows of up to 2048 codes: four rows per wave; over a wide N (>= 8192) one chunk per
+// lane and row in flight (measured on [11008, 2048]: 6.1 us at M = 1 against 6.5 with
+// two chunks, 7.2 with two rows and two chunks), over a narrower N two, so the fewer
+// waves each request a whole 2048-code row at once ([2048, 2048] 4.1 -> 3.7 us,
+// [4096, 2048] 4.6 -> 4.2 us); longer rows one row per wave with six chunks per lane in
+// flight (the best of 1-4 rows on [2048, 11008]).
 template <int M>
 hipError_t launch_m8(const uint16_t* X, const uint8_t* C, const float* S, const uint8_t* Z, float* Y, int N, int K,
                      int gshift, hipStream_t stream) {
   static_assert(M >= 1 && M <= 3, "the VALU W8A16 GEMV serves 1 .. 3 activation rows");
-  if ((K >> 4) <= 128) return launch_cfg8<M, 4, 1>(X, C, S, Z, Y, N, K, gshift, stream);
+  if ((K >> 4) <= 128) {
+    if (N >= 8192) return launch_cfg8<M, 4, 1>(X, C, S, Z, Y, N, K, gshift, stream);
+    return launch_cfg8<M, 4, 2>(X, C, S, Z, Y, N, K, gshift, stream);
+  }
   return launch_cfg8<M, 1, 6>(X, C, S, Z, Y, N, K, gshift, stream);
 }
 
