@@ -165,7 +165,8 @@ def test_fp4_mlp_shapes(n, k):
 @pytest.mark.parametrize("m,n,k", [(1, 3, 32), (7, 130, 96), (16, 4100, 64), (17, 33, 160), (300, 257, 512),
                                    (1, 8195, 4096), (2, 4099, 160), (8, 8195, 4096), (12, 33, 2112), (4, 130, 64),
                                    (6, 70, 8256), (16, 9000, 2048), (3, 1001, 4160),
-                                   (1, 4099, 160), (1, 130, 4160), (1, 70, 14368)])
+                                   (1, 4099, 160), (1, 130, 4160), (1, 70, 14368), (5, 40, 8192),
+                                   (11, 17, 4096)])
 def test_fp4_ragged(m, n, k):
     rng = np.random.default_rng(m + n + k)
     c, b, ts = fp4.encode((rng.standard_normal((n, k)) * 0.02).astype(np.float32))

@@ -139,7 +139,8 @@ def _exact_case(rng, m, n, k, g):
 
 @pytest.mark.parametrize("m,n,k,g", [(1, 64, 256, 64), (5, 33, 128, 32), (16, 130, 1024, 128), (1, 8195, 256, 64),
                                      (1, 8197, 2048, 32), (8, 40, 4160, 64), (9, 33, 2080, 32), (12, 17, 4224, 128),
-                                     (16, 300, 32, 32), (7, 8195, 1024, 128), (16, 70, 8256, 32)])
+                                     (16, 300, 32, 32), (7, 8195, 1024, 128), (16, 70, 8256, 32),
+                                     (8, 70, 8192, 128), (5, 33, 4096, 64)])
 def test_gemv_exact_integer_case(m, n, k, g):
     """(N >= 8192 at M = 1 takes the four-rows-per-wave launch, here with a ragged last wave;
     M >= 5 takes the matrix-core kernel, here with 4, 8 and 16 waves per

@@ -74,7 +74,8 @@ def test_gemm8_shapes(m, name):
                                      (300, 200, 768, 128), (1, 1003, 512, 64), (4, 1001, 2048, 128),
                                      (2, 1002, 4096, 32), (12, 1001, 4160, 32), (8, 8197, 2048, 64),
                                      (16, 17, 64, 64), (5, 1001, 6272, 128), (16, 257, 8256, 64),
-                                     (1, 1001, 2048, 64), (3, 130, 1536, 32)])
+                                     (1, 1001, 2048, 64), (3, 130, 1536, 32), (6, 33, 4096, 128),
+                                     (9, 40, 8192, 32)])
 def test_int8_exact_integer_case(m, n, k, g):
     """Integer X (|x| <= 16), random codes and zero points, S = 2^-6: every product and partial
     sum is exact in fp32, so the GEMV / GEMM output equals the fp64 reference bit for bit (from
