@@ -66,6 +66,7 @@
 // each operand; its 16 results are column (lane % 32), rows
 // 8 (i / 4) + 4 (lane / 32) + (i % 4), so they share one weight row n and need
 // one S per block per group.
+#include <algorithm>
 #include <type_traits>
 
 #include "aq_device.h"
@@ -752,20 +753,22 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_kernel(GemmArgs a) {
 // Staged weights: the codes of one weight matrix dequantized once into a bf16 matrix
 // W16[N, K] (K contiguous) that the INT4S / FP4S GEMMs load like activations.  INT4:
 // the exact integer q - z (group step applied in the GEMM); FP4: the exact product
-// e2m1(code) * e4m3(block scale).  One thread converts 16 codes (8 bytes in, 32 out).
+// e2m1(code) * e4m3(block scale).  One thread converts 16 codes (8 bytes in, 32 out)
+// of a range of `rows` rows with rows * K / 16 <= 2^30 (the launcher splits larger
+// matrices), so the thread's row and chunk come from 32-bit arithmetic.
 template <bool FP4>
 __global__ __launch_bounds__(256) void stage_weights_kernel(const uint8_t* __restrict__ codes,
-                                                            const uint8_t* __restrict__ aux, int N, int K, int G,
-                                                            uint16_t* __restrict__ W16) {
-  const int cpr = K >> 4;                                        // 16-code chunks per row
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)N * cpr) return;
-  const int n = (int)(idx / cpr), c = (int)(idx - (int64_t)n * cpr);
-  const uint2 wv = *reinterpret_cast<const uint2*>(codes + (int64_t)n * (K >> 1) + c * 8);
+                                                            const uint8_t* __restrict__ aux, int rows, int K,
+                                                            int gshift, uint16_t* __restrict__ W16) {
+  const uint32_t cpr = (uint32_t)K >> 4;                        // 16-code chunks per row
+  const uint32_t idx = blockIdx.x * 256u + threadIdx.x;
+  if (idx >= (uint32_t)rows * cpr) return;
+  const uint32_t n = idx / cpr, c = idx - n * cpr;
+  const uint2 wv = *reinterpret_cast<const uint2*>(codes + (size_t)n * (uint32_t)(K >> 1) + c * 8u);
   const uint32_t w[2] = {wv.x, wv.y};
   uint32_t o[8];
   if constexpr (!FP4) {
-    const float z = (float)aux[(int64_t)n * (K / G) + (c * 16) / G];
+    const float z = (float)aux[(size_t)n * (uint32_t)(K >> gshift) + ((c << 4) >> gshift)];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       uint32_t lo = w[u] & 0x0F0F0F0Fu, hi = (w[u] >> 4) & 0x0F0F0F0Fu;
@@ -775,7 +778,7 @@ __global__ __launch_bounds__(256) void stage_weights_kernel(const uint8_t* __res
         o[4 * u + b] = pack_bf16_exact((float)((lo >> (8 * b)) & 0xFFu) - z, (float)((hi >> (8 * b)) & 0xFFu) - z);
     }
   } else {
-    const float sc = __builtin_amdgcn_cvt_f32_fp8((int)aux[(int64_t)n * (K >> 4) + c], 0);
+    const float sc = __builtin_amdgcn_cvt_f32_fp8((int)aux[(size_t)n * (uint32_t)(K >> 4) + c], 0);
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -790,22 +793,23 @@ __global__ __launch_bounds__(256) void stage_weights_kernel(const uint8_t* __res
         o[4 * u + b] = pack_bf16_exact(bf16_lo(e2) * sc, bf16_hi(e2) * sc);
       }
   }
-  u32x4* dst = reinterpret_cast<u32x4*>(W16 + (int64_t)n * K + c * 16);
+  u32x4* dst = reinterpret_cast<u32x4*>(W16 + (size_t)n * (uint32_t)K + c * 16u);
   dst[0] = u32x4{o[0], o[1], o[2], o[3]};
   dst[1] = u32x4{o[4], o[5], o[6], o[7]};
 }
 
 // 8-bit codes: the exact integer q - z (|q - z| <= 255 has at most 8 significant
-// bits, exact in bf16); one thread converts 16 code bytes (16 in, 32 out).
+// bits, exact in bf16); one thread converts 16 code bytes (16 in, 32 out), 32-bit
+// indexing over a row range as above.
 __global__ __launch_bounds__(256) void stage_weights8_kernel(const uint8_t* __restrict__ codes,
-                                                             const uint8_t* __restrict__ zeros, int N, int K, int G,
-                                                             uint16_t* __restrict__ W16) {
-  const int cpr = K >> 4;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)N * cpr) return;
-  const int n = (int)(idx / cpr), c = (int)(idx - (int64_t)n * cpr);
-  const u32x4 w = *reinterpret_cast<const u32x4*>(codes + (int64_t)n * K + c * 16);
-  const float z = (float)zeros[(int64_t)n * (K / G) + (c * 16) / G];
+                                                             const uint8_t* __restrict__ zeros, int rows, int K,
+                                                             int gshift, uint16_t* __restrict__ W16) {
+  const uint32_t cpr = (uint32_t)K >> 4;
+  const uint32_t idx = blockIdx.x * 256u + threadIdx.x;
+  if (idx >= (uint32_t)rows * cpr) return;
+  const uint32_t n = idx / cpr, c = idx - n * cpr;
+  const u32x4 w = *reinterpret_cast<const u32x4*>(codes + (size_t)n * (uint32_t)K + c * 16u);
+  const float z = (float)zeros[(size_t)n * (uint32_t)(K >> gshift) + ((c << 4) >> gshift)];
   uint32_t o[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -813,17 +817,27 @@ __global__ __launch_bounds__(256) void stage_weights8_kernel(const uint8_t* __re
     o[2 * i + 1] =
         pack_bf16_exact(ubyte_f32<2>(w[i]) - z, ubyte_f32<3>(w[i]) - z);
   }
-  u32x4* dst = reinterpret_cast<u32x4*>(W16 + (int64_t)n * K + c * 16);
+  u32x4* dst = reinterpret_cast<u32x4*>(W16 + (size_t)n * (uint32_t)K + c * 16u);
   dst[0] = u32x4{o[0], o[1], o[2], o[3]};
   dst[1] = u32x4{o[4], o[5], o[6], o[7]};
 }
 
+int log2_group(int G) { return G == 16 ? 4 : G == 32 ? 5 : G == 64 ? 6 : 7; }
+
+// The staging kernels over row ranges of at most 2^30 chunks (32-bit indexing).
+// FP4 passes G = 16 (one block scale per 16 codes).
 template <bool FP4>
 hipError_t stage_weights(const uint8_t* codes, const uint8_t* aux, int N, int K, int G, uint16_t* W16,
                          hipStream_t stream) {
-  const int64_t chunks = (int64_t)N * (K >> 4);
-  hipLaunchKernelGGL((stage_weights_kernel<FP4>), dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream, codes,
-                     aux, N, K, G, W16);
+  const int gshift = log2_group(G);
+  const int64_t cpr = K >> 4;
+  const int64_t max_rows = cpr > 0 ? std::max<int64_t>(1, (int64_t(1) << 30) / cpr) : N;
+  for (int64_t n0 = 0; n0 < N; n0 += max_rows) {
+    const int rows = (int)std::min<int64_t>(max_rows, N - n0);
+    const int64_t chunks = rows * cpr;
+    hipLaunchKernelGGL((stage_weights_kernel<FP4>), dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream,
+                       codes + n0 * (K >> 1), aux + n0 * (K >> gshift), rows, K, gshift, W16 + n0 * K);
+  }
   return hipGetLastError();
 }
 
@@ -895,9 +909,15 @@ hipError_t launch_w8a16_gemm(const uint16_t* X, int M, int K, const uint8_t* C, 
                              int N, int group, float* Y, uint16_t* staged, hipStream_t stream) {
   // always staged: the 8-bit codes are dequantized once into the bf16 matrix, then
   // the staged INT4 GEMM (same per-group step rescale) runs on it
-  const int64_t chunks = (int64_t)N * (K >> 4);
-  hipLaunchKernelGGL(stage_weights8_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream, C, Z, N, K,
-                     group, staged);
+  const int gshift = log2_group(group);
+  const int64_t cpr = K >> 4;
+  const int64_t max_rows = cpr > 0 ? std::max<int64_t>(1, (int64_t(1) << 30) / cpr) : N;
+  for (int64_t n0 = 0; n0 < N; n0 += max_rows) {   // row ranges of at most 2^30 chunks (32-bit indexing)
+    const int rows = (int)std::min<int64_t>(max_rows, N - n0);
+    const int64_t chunks = rows * cpr;
+    hipLaunchKernelGGL(stage_weights8_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream,
+                       C + n0 * K, Z + n0 * (K >> gshift), rows, K, gshift, staged + n0 * K);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   GemmArgs a = {};
