@@ -143,11 +143,18 @@ __device__ __forceinline__ uint32_t nibbles8(const uint32_t (&q)[8]) {
 constexpr int kPackU = 2;
 constexpr int kErrorU = 1;
 
+// Column of flat element e of a row-major [N, K] matrix: a 32-bit remainder while the
+// matrix has fewer than 2^32 elements (a uniform branch), else the 64-bit one.
+__device__ __forceinline__ int64_t column_of(int64_t e, int64_t K, int64_t total) {
+  if (total <= 0xFFFFFFFFll) return (int64_t)((uint32_t)e % (uint32_t)K);
+  return e % K;
+}
+
 // One lane's U units of 8 consecutive elements as fp32 (times the channel scale
 // when one is given).
 template <int U, bool BF16, bool SCALED>
 __device__ __forceinline__ void load_units(const void* W, const float* chan_scale, int64_t e, int64_t K,
-                                           float (&v)[U][8]) {
+                                           int64_t total, float (&v)[U][8]) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (BF16) {
@@ -165,7 +172,7 @@ __device__ __forceinline__ void load_units(const void* W, const float* chan_scal
     }
   }
   if (SCALED) {
-    const int64_t k0 = e % K;
+    const int64_t k0 = column_of(e, K, total);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const float4* sp = reinterpret_cast<const float4*>(chan_scale + k0 + 8 * u);
@@ -193,7 +200,7 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(const void* __restrict_
   const int64_t e = live ? e0 : 0;
 
   float v[U][8];
-  load_units<U, BF16, SCALED>(W, chan_scale, e, K, v);
+  load_units<U, BF16, SCALED>(W, chan_scale, e, K, total, v);
   float mn = v[0][0], mx = v[0][0];
 #pragma unroll
   for (int u = 0; u < U; ++u)
@@ -258,8 +265,8 @@ __global__ __launch_bounds__(256) void quant_error_kernel(const void* __restrict
   const bool live = e0 < total;
   const int64_t e = live ? e0 : 0;
   float w[U][8], v[U][8];
-  load_units<U, BF16, false>(W, nullptr, e, K, w);
-  const int64_t k0 = e % K;
+  load_units<U, BF16, false>(W, nullptr, e, K, total, w);
+  const int64_t k0 = column_of(e, K, total);
   float mn = 0.0f, mx = 0.0f;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -283,20 +290,22 @@ __global__ __launch_bounds__(256) void quant_error_kernel(const void* __restrict
     const float4* sp = reinterpret_cast<const float4*>(chan_scale + k0 + 8 * u);
     const float4 a = sp[0], b = sp[1];
     const float s[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    // E_hi = bf16(err), E_lo = bf16(err - E_hi), round to nearest even, two values per
+    // v_cvt_pk_bf16_f32 (equal to the bitwise rounding for every non-NaN fp32)
     uint32_t hi[4], lo[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint32_t h16[2], l16[2];
+      float err[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int j = 2 * i + h;
         const float what = (__uint_as_float(qc[j]) - g.kz) * g.S;   // (q - z) S, q - z exact
-        const float err = what / s[j] - w[u][j];
-        h16[h] = f32_to_bf16_rne(err);
-        l16[h] = f32_to_bf16_rne(err - __uint_as_float(h16[h] << 16));
+        err[h] = what / s[j] - w[u][j];
       }
-      hi[i] = h16[0] | (h16[1] << 16);
-      lo[i] = l16[0] | (l16[1] << 16);
+      const bf16x2 eh = {(__bf16)err[0], (__bf16)err[1]};
+      hi[i] = __builtin_bit_cast(uint32_t, eh);
+      const bf16x2 el = {(__bf16)(err[0] - bf16_lo(hi[i])), (__bf16)(err[1] - bf16_hi(hi[i]))};
+      lo[i] = __builtin_bit_cast(uint32_t, el);
     }
     if (live) {
       *reinterpret_cast<u32x4*>(E + e + 8 * u) = u32x4{hi[0], hi[1], hi[2], hi[3]};
