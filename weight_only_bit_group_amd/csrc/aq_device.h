@@ -26,15 +26,9 @@ __device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
   return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 
-// Round-to-nearest-even fp32 -> bf16 bits (finite inputs).
 // Byte i of w as an fp32 integer (a single v_cvt_f32_ubyte<i>).
 template <int I>
 __device__ __forceinline__ float ubyte_f32(uint32_t w) { return (float)((w >> (8 * I)) & 0xFFu); }
-
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
