@@ -144,6 +144,15 @@ static hipError_t launch_m(const uint16_t* X, const uint8_t* C, const uint8_t* B
                            int K, hipStream_t stream) {
   const int nchunk = K >> 5;
   const int cpl = M == 1 ? (nchunk > 128 ? 4 : 2) : 1;
+  if constexpr (M == 1) {
+    // one row over a wide N with rows of more than 2048 codes: two rows per wave, so twice
+    // the waves share the memory latency ([14336, 4096] 8.9 -> 8.66 us; at K = 2048 four
+    // rows per wave stay faster)
+    if (N >= 8192 && nchunk > 64) {
+      if (cpl == 4) return launch_cfg<M, 2, 4>(X, C, B, ts, Y, N, K, stream);
+      return launch_cfg<M, 2, 2>(X, C, B, ts, Y, N, K, stream);
+    }
+  }
   if (N >= 8192) {
     if constexpr (M == 1) {
       if (cpl == 4) return launch_cfg<M, 4, 4>(X, C, B, ts, Y, N, K, stream);
