@@ -155,7 +155,8 @@ def test_gemv_exact_integer_case(m, n, k, g):
 @pytest.mark.parametrize("m,n,k,g", [(1, 1, 32, 32), (2, 7, 96, 32), (3, 4099, 320, 64), (16, 8200, 64, 64),
                                      (1, 8194, 512, 128), (1, 8199, 11008, 64), (8, 8197, 2048, 64),
                                      (13, 1001, 11008, 64), (10, 3, 6144, 128), (5, 8203, 1024, 64),
-                                     (6, 8192, 256, 32), (2, 1003, 11008, 64), (3, 70, 8192, 32)])
+                                     (6, 8192, 256, 32), (2, 1003, 11008, 64), (3, 70, 8192, 32),
+                                     (2, 8195, 2048, 64), (2, 9000, 1024, 128)])
 def test_gemv_ragged_shapes(m, n, k, g):
     rng = np.random.default_rng(n)
     w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)

@@ -229,9 +229,10 @@ hipError_t launch_m(const uint16_t* X, const uint8_t* P, const float* S, const u
   const int nchunk = K >> 5;
   if (lds_x) {
     if (nchunk <= 64) {
-      // a single row over a wide N (e.g. the MLP projections): four rows per wave, so
-      // half as many blocks stage the activations (4.5 -> 4.35 us on [11008, 2048])
-      if (M == 1 && N >= 8192) return launch_cfg<M, 4, 1, true>(X, P, S, Z, Y, N, K, gshift, stream);
+      // one or two rows over a wide N (e.g. the MLP projections): four rows per wave, so
+      // half as many blocks stage the activations (M = 1: 4.5 -> 4.35 us on [11008, 2048];
+      // M = 2: 5.45 -> 5.26 us; from M = 3 two rows per wave stay faster)
+      if (M <= 2 && N >= 8192) return launch_cfg<M, 4, 1, true>(X, P, S, Z, Y, N, K, gshift, stream);
       return launch_cfg<M, R, 1, true>(X, P, S, Z, Y, N, K, gshift, stream);
     }
     // long rows (K > 4096, e.g. a down projection): one row per wave and up to six
