@@ -108,8 +108,3 @@ def dequantize(codes, block_scales, ts) -> np.ndarray:
 def forward(x_f32, codes, block_scales, ts) -> np.ndarray:
     """Y[M, N] = X @ W_hat^T, fp64."""
     return np.asarray(x_f32, dtype=np.float64) @ dequantize(codes, block_scales, ts).T
-
-
-def forward_rows(x_f32, codes, block_scales, ts, rows) -> np.ndarray:
-    rows = np.asarray(rows)
-    return np.asarray(x_f32, dtype=np.float64) @ dequantize(codes[rows], block_scales[rows], ts).T

@@ -205,14 +205,6 @@ def forward(x_f32, packed, scales, zeros, group: int) -> np.ndarray:
     return x @ dequantize(packed, scales, zeros, group).T
 
 
-def forward_rows(x_f32, packed, scales, zeros, group: int, rows) -> np.ndarray:
-    """Selected output columns Y[:, rows] computed one weight row at a time (fp64)."""
-    x = np.asarray(x_f32, dtype=np.float64)
-    rows = np.asarray(rows)
-    w = dequantize(packed[rows], scales[rows], zeros[rows], group)
-    return x @ w.T
-
-
 def storage_bytes(n: int, k: int, group: int, bits: int = 4):
     """(code bytes, metadata bytes) of the packed format: bits/8 per weight, fp32 S + u8 z per group."""
     return n * k * bits // 8, (n * k // group) * (4 + 1)

@@ -234,7 +234,7 @@ def test_storage_ratio_matches_page():
 
 
 def test_golden_regression():
-    """The committed oracle outputs for a small seeded case (written by oracle/make_golden.py)."""
+    """The committed oracle outputs for a small seeded case (written by tests/golden/make_golden.py)."""
     with open(os.path.join(GOLDEN, "int4_small.json")) as f:
         gold = json.load(f)
     case = synth.single_linear(0)
@@ -344,3 +344,41 @@ def test_int8_min_to_zero_and_dequant_bound():
     e8 = np.abs(what - w).mean()
     e4 = np.abs(int4.dequantize(*int4.quantize_pack(w, 64), 64) - w).mean()
     assert 12 < e4 / e8 < 22
+
+
+def test_forward8_exact_integer_case():
+    """P10 for the 8-bit format: integer X (|x| <= 64), codes 0..255, per-group zero points and
+    S = 2^-8 make every product and sum exact; the fp64 forward equals an exact integer
+    computation element by element (non-square shapes and distinct zero points per group, so a
+    transposed operand or a wrong group index fails)."""
+    rng = np.random.default_rng(23)
+    m, n, k, g = 3, 10, 192, 64
+    x = rng.integers(-64, 65, (m, k)).astype(np.float32)
+    q = rng.integers(0, 256, (n, k)).astype(np.uint8)
+    z = rng.integers(0, 256, (n, k // g)).astype(np.uint8)
+    s = np.full((n, k // g), 2.0 ** -8, dtype=np.float32)
+    y = int4.forward8(x, q, s, z, g)
+    assert y.shape == (m, n)
+    xi = x.astype(np.int64)
+    zi = np.repeat(z.astype(np.int64), g, axis=1)
+    assert (y * 256 == xi @ (q.astype(np.int64) - zi).T).all()
+
+
+def test_forward8_matches_rational_reference():
+    """P11 for the 8-bit format: the fp64 forward agrees with an exact rational evaluation of
+    sum_g S[n, g] sum_{k in g} x (q - z) on a tiny random case with distinct steps per group."""
+    rng = np.random.default_rng(24)
+    m, n, k, g = 2, 3, 96, 32
+    w = rng.standard_normal((n, k)).astype(np.float32)
+    x = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32)))
+    q, s, z = int4.quantize_codes8(w, g)
+    assert len(set(s.ravel().tolist())) == s.size
+    y = int4.forward8(x, q, s, z, g)
+    for i in range(m):
+        for j in range(n):
+            acc = Fraction(0)
+            for grp in range(k // g):
+                part = sum((Fraction(float(x[i, kk])) * (int(q[j, kk]) - int(z[j, grp]))
+                            for kk in range(grp * g, (grp + 1) * g)), Fraction(0))
+                acc += part * Fraction(float(s[j, grp]))
+            assert abs(float(acc) - y[i, j]) <= 1e-12 * max(1.0, abs(float(acc)))
