@@ -174,14 +174,36 @@ aq_status aq_act_absmean(const uint16_t* X, int64_t T, int64_t K, double* sum_ab
  * triple are device outputs; workspace >= aq_awq_search_workspace(...) bytes.
  * Synchronises `stream` once (candidate-scale upload) before the first launch.
  * Errors: EINVAL for T <= 0 (empty calibration data), n_grid outside 1..64,
- *         K % group, group not in {32,64,128}, small workspace, NULL /
- *         misaligned pointers, non-finite or negative absmean values.
+ *         K % group, group not in {32,64,128}, T, N or K >= 2^22 (the error
+ *         GEMM's 32-bit offsets), small workspace, NULL / misaligned pointers,
+ *         non-finite or negative absmean values.  The workspace query returns 0
+ *         for arguments the search refuses.
  */
 size_t aq_awq_search_workspace(int64_t T, int64_t N, int64_t K, int32_t group, int32_t n_grid);
 aq_status aq_awq_search(const uint16_t* X_sub, int64_t T, const float* absmean_host, const void* W,
                         int32_t w_dtype, int64_t N, int64_t K, int32_t group, int32_t n_grid, double* mse,
                         int32_t* best, float* best_scale, uint8_t* packed, float* scales, uint8_t* zeros,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The RMSNorm fold of the AWQ channel scale.
+ * Source: "Lance-Quant" (zingnex.cn), grid-search / grouping section (the scale
+ * chosen for a normalisation and its consuming linears is folded into that
+ * RMSNorm: the linears hold Q(W diag(s)), the norm weight becomes w / s, so the
+ * layer computes the same function); OmniQuant tutorial (cyqw.cn), section 2.2.2
+ * (the per-channel equivalent transform (X / s)(s W) = X W).
+ *
+ *   folded[k] = fl32(norm_w[k] / chan_scale[k])      (one IEEE fp32 division)
+ *
+ * norm_w [K] fp32 or bf16 (w_dtype), chan_scale [K] fp32 (aq_awq_search's
+ * best_scale), folded [K] fp32 output; all device pointers (4-byte aligned,
+ * 2 for a bf16 norm_w).  A zero chan_scale entry gives an infinite result
+ * (aq_awq_search's scales are positive).
+ * Errors: EINVAL for a bad w_dtype, K <= 0 or K >= 2^30, NULL / misaligned
+ *         pointers.
+ */
+aq_status aq_awq_fold_norm(const void* norm_w, int32_t w_dtype, const float* chan_scale, int64_t K, float* folded,
+                           void* stream);
 
 /*
  * Group-wise asymmetric INT8 quantization (one code byte per weight).

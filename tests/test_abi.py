@@ -175,6 +175,24 @@ def test_search_einval(lib):
     bad[5] = -1
     assert call(m=bad.ctypes.data) == _lib.AQ_EINVAL
     assert lib.aq_awq_search_workspace(0, N, K, g, ng) == 0
+    # the error GEMM's 32-bit offsets: T, N and K below 2^22 (refused before any launch)
+    for kw in (dict(T=1 << 22), dict(N=1 << 22), dict(K=1 << 22)):
+        assert call(**kw) == _lib.AQ_EINVAL and "2^22" in _lib.last_error(), kw
+    assert lib.aq_awq_search_workspace(1 << 22, N, K, g, ng) == 0
+    assert lib.aq_awq_search_workspace(T, 1 << 22, K, g, ng) == 0
+    assert lib.aq_awq_search_workspace(T, N, 1 << 22, g, ng) == 0
+    assert lib.aq_awq_search_workspace(T, N, (1 << 22) - 64, g, ng) > 0
+
+
+def test_fold_norm_einval(lib):
+    f = lib.aq_awq_fold_norm
+    assert f(FAKE, 0, FAKE, 0, FAKE, None) == _lib.AQ_EINVAL
+    assert f(FAKE, 0, FAKE, 1 << 30, FAKE, None) == _lib.AQ_EINVAL
+    assert f(FAKE, 5, FAKE, 64, FAKE, None) == _lib.AQ_EINVAL and "w_dtype" in _lib.last_error()
+    assert f(None, 0, FAKE, 64, FAKE, None) == _lib.AQ_EINVAL
+    assert f(FAKE + 2, 0, FAKE, 64, FAKE, None) == _lib.AQ_EINVAL   # fp32 norm weight: 4-byte aligned
+    assert f(FAKE, 0, FAKE + 1, 64, FAKE, None) == _lib.AQ_EINVAL
+    assert f(FAKE, 0, FAKE, 64, None, None) == _lib.AQ_EINVAL
 
 
 def test_fp4_einval(lib):
@@ -221,6 +239,7 @@ def test_injected_runtime_failure(lib, monkeypatch):
     assert _prod8(lib, "aq_w8a16_gemm", M=128) == _lib.AQ_ERUNTIME
     ws = lib.aq_act_absmean_workspace(64, 64)
     assert lib.aq_act_absmean(FAKE, 64, 64, FAKE, None, 64, FAKE, ws, None) == _lib.AQ_ERUNTIME
+    assert lib.aq_awq_fold_norm(FAKE + 2, 1, FAKE, 64, FAKE, None) == _lib.AQ_ERUNTIME   # bf16: 2-byte aligned
     # validation still wins over the injected fault
     assert _qp(lib, g=5) == _lib.AQ_EINVAL
 

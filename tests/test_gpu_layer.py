@@ -183,3 +183,21 @@ def test_quantize_modules_mixed_4_8_bit_policy():
                 trip = int4.quantize_pack_sym(weights[name], g) if sym else int4.quantize_pack(weights[name], g)
                 ref = int4.forward(x, *trip, g)
             check_close(y, ref + biases[name], f"policy {name} M={m}")
+
+
+def test_fold_norm_is_the_ieee_quotient():
+    """aq_awq_fold_norm: fl32(w / s) per channel, bit for bit, for fp32 and bf16 norm weights
+    (bf16 widened exactly), with scales spanning many binades and a ragged K."""
+    from weight_only_bit_group_amd import binding as B
+    rng = np.random.default_rng(12)
+    k = 2049
+    w = rng.uniform(0.5, 1.5, k).astype(np.float32)
+    s = np.exp(rng.uniform(-8, 8, k)).astype(np.float32)
+    step("aq_awq_fold_norm fp32 / bf16, K = 2049")
+    got = host(B.aq_awq_fold_norm(torch.from_numpy(w).cuda(), torch.from_numpy(s).cuda()))
+    assert np.array_equal(got.view(np.uint32), (w / s).astype(np.float32).view(np.uint32))
+    wb = synth.f32_to_bf16_bits(w)
+    got = host(B.aq_awq_fold_norm(torch.from_numpy(wb.view(np.int16)).cuda().view(torch.bfloat16),
+                                  torch.from_numpy(s).cuda()))
+    want = (synth.bf16_bits_to_f32(wb) / s).astype(np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))

@@ -91,3 +91,31 @@ def test_concat_refuses_mismatched_modules():
         W4A16Linear.concat([_packed(8, 64, 32), torch.nn.Linear(64, 8)])
     with pytest.raises(ValueError):
         W4A16Linear.concat([])
+
+
+def test_quantized_modules_keep_no_staging_buffer(monkeypatch):
+    """The staged GEMM's bf16 staging matrix (N * K * 2 bytes, as large as the dense weight) is a
+    per-call allocation: after a forward at M = 2048 the module holds only its packed triple
+    (and bias), so swapping linears for W4A16Linear keeps the memory saving.  CPU only: the
+    binding's GEMM is replaced by a stand-in that allocates the staging matrix as the binding
+    does and returns zeros."""
+    from weight_only_bit_group_amd import layer as L
+    n, k, g, m = 256, 512, 64, 2048
+    seen = []
+
+    def fake_gemm(x, packed, scales, zeros, group, out=None, workspace=None):
+        seen.append(workspace)
+        staging = torch.empty(n * k * 2, dtype=torch.uint8)   # what the binding allocates per call
+        assert staging.numel() == n * k * 2
+        return torch.zeros(x.shape[0], packed.shape[0])
+
+    monkeypatch.setattr(L.B, "aq_w4a16_gemm", fake_gemm)
+    mod = W4A16Linear(torch.zeros(n, k // 2, dtype=torch.uint8), torch.zeros(n, k // g), torch.zeros(n, k // g,
+                      dtype=torch.uint8), g)
+    mod(torch.zeros(m, k))
+    assert seen == [None]      # no workspace passed in: the binding sizes and frees it per call
+    held = sum(t.numel() * t.element_size() for t in list(mod.buffers()) + [v for v in vars(mod).values()
+                                                                              if isinstance(v, torch.Tensor)])
+    assert held == n * k // 2 + n * (k // g) * 5
+    assert not any(isinstance(v, torch.Tensor) and v.numel() * v.element_size() >= n * k * 2
+                   for v in vars(mod).values())

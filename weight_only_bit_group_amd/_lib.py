@@ -32,6 +32,7 @@ SIGNATURES = {
     "aq_act_absmean": (_I32, [_P, _I64, _I64, _P, _P, _I64, _P, _SZ, _P]),
     "aq_awq_search_workspace": (_SZ, [_I64, _I64, _I64, _I32, _I32]),
     "aq_awq_search": (_I32, [_P, _I64, _P, _P, _I32, _I64, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "aq_awq_fold_norm": (_I32, [_P, _I32, _P, _I64, _P, _P]),
     "aq_fp4_gemm_workspace": (_SZ, [_I64, _I64, _I64]),
     "aq_fp4_gemm": (_I32, [_P, _I64, _I64, _P, _P, ctypes.c_float, _I64, _P, _P, _SZ, _P]),
     "aq_fp4_quantize_workspace": (_SZ, [_I64, _I64]),

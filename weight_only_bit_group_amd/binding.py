@@ -190,6 +190,25 @@ def aq_awq_search(X_sub, absmean_host, W, group: int, n_grid: int = 20, workspac
     return {"mse": mse, "best": best, "best_scale": best_scale, "packed": packed, "scales": scales, "zeros": zeros}
 
 
+def aq_awq_fold_norm(norm_w, chan_scale, out=None):
+    """folded [K] fp32 = fl32(norm_w / chan_scale) on the device (norm_w fp32 or bf16; other float
+    dtypes are widened to fp32 first, exactly)."""
+    if norm_w.dtype not in (torch.float32, torch.bfloat16):
+        norm_w = norm_w.float()
+    _need(norm_w, "norm_w", norm_w.dtype, 1)
+    _need(chan_scale, "chan_scale", torch.float32, 1)
+    k = norm_w.shape[0]
+    if chan_scale.shape[0] != k:
+        raise ValueError("norm_w and chan_scale must have the same length")
+    if out is None:
+        out = torch.empty(k, dtype=torch.float32, device=norm_w.device)
+    _need(out, "folded", torch.float32, 1)
+    st = _lib.load().aq_awq_fold_norm(norm_w.data_ptr(), _wdtype(norm_w), chan_scale.data_ptr(), k, out.data_ptr(),
+                                      _stream(norm_w))
+    check(st, "aq_awq_fold_norm")
+    return out
+
+
 def aq_fp4_gemm_workspace(M: int, N: int, K: int) -> int:
     return int(_lib.load().aq_fp4_gemm_workspace(M, N, K))
 

@@ -77,9 +77,16 @@ struct SearchLayout {
   int nblocks;
 };
 
+// The search's error GEMM takes T as its M: T, N and K below 2^22 keep its 32-bit
+// load / store offsets and its tile count (below 2^29) in range.
+bool search_dims_ok(int64_t T, int64_t N, int64_t K) {
+  return T > 0 && N > 0 && K > 0 && T < kGemmDimLimit && N < kGemmDimLimit && K < kGemmDimLimit &&
+         aq::sumsq_gemm_blocks(T, N) < (int64_t(1) << 30);
+}
+
 SearchLayout search_layout(int64_t T, int64_t N, int64_t K, int32_t n_grid) {
   SearchLayout L;
-  L.nblocks = aq::sumsq_gemm_blocks((int)T, (int)N);
+  L.nblocks = (int)aq::sumsq_gemm_blocks(T, N);
   L.sgrid = 0;
   L.e = round_up((size_t)n_grid * (size_t)K * sizeof(float), 256);
   L.partial = L.e + round_up((size_t)N * (size_t)K * 2 * 2, 256);   // E_hi and E_lo planes
@@ -293,8 +300,7 @@ aq_status aq_act_absmean(const uint16_t* X, int64_t T, int64_t K, double* sum_ab
 }
 
 size_t aq_awq_search_workspace(int64_t T, int64_t N, int64_t K, int32_t group, int32_t n_grid) {
-  if (T <= 0 || N <= 0 || K <= 0 || n_grid < 1 || n_grid > 64 || !valid_group(group)) return 0;
-  if (T >= kDimLimit || N >= kDimLimit || K >= kDimLimit) return 0;
+  if (n_grid < 1 || n_grid > 64 || !valid_group(group) || !search_dims_ok(T, N, K)) return 0;
   return search_layout(T, N, K, n_grid).total;
 }
 
@@ -303,13 +309,15 @@ aq_status aq_awq_search(const uint16_t* X_sub, int64_t T, const float* absmean_h
                         int32_t* best, float* best_scale, uint8_t* packed, float* scales, uint8_t* zeros,
                         void* workspace, size_t workspace_bytes, void* stream) {
   AQ_REQUIRE(T > 0, "aq_awq_search: empty calibration data (T = %lld)", (long long)T);
-  AQ_REQUIRE(T < kDimLimit, "aq_awq_search: T out of range");
+  AQ_REQUIRE(T < kGemmDimLimit, "aq_awq_search: T must be below 2^22 (got %lld)", (long long)T);
   AQ_REQUIRE(w_dtype == AQ_F32 || w_dtype == AQ_BF16, "aq_awq_search: bad w_dtype %d", w_dtype);
   AQ_REQUIRE(valid_group(group), "aq_awq_search: group must be 32, 64 or 128 (got %d)", group);
   AQ_REQUIRE(n_grid >= 1 && n_grid <= 64, "aq_awq_search: n_grid must be in 1..64 (got %d)", n_grid);
-  AQ_REQUIRE(N > 0 && N < kDimLimit, "aq_awq_search: N out of range (%lld)", (long long)N);
-  AQ_REQUIRE(K > 0 && K < kDimLimit && K % group == 0, "aq_awq_search: K (%lld) must be a multiple of group (%d)",
-             (long long)K, group);
+  AQ_REQUIRE(N > 0 && N < kGemmDimLimit, "aq_awq_search: N must be in 1 .. 2^22 - 1 (got %lld)", (long long)N);
+  AQ_REQUIRE(K > 0 && K < kGemmDimLimit && K % group == 0,
+             "aq_awq_search: K (%lld) must be a multiple of group (%d) below 2^22", (long long)K, group);
+  AQ_REQUIRE(search_dims_ok(T, N, K), "aq_awq_search: too many error-GEMM tiles for T = %lld, N = %lld",
+             (long long)T, (long long)N);
   AQ_PTR(X_sub, 16, "X_sub");
   AQ_REQUIRE(absmean_host != nullptr, "absmean_host must not be NULL");
   AQ_PTR(W, 16, "W");
@@ -365,6 +373,20 @@ aq_status aq_awq_search(const uint16_t* X_sub, int64_t T, const float* absmean_h
   if (e != hipSuccess) return runtime_status(e, "aq_awq_search: select kernel");
   return runtime_status(aq::launch_quant_pack(W, bf16, best_scale, packed, scales, zeros, N, K, group, false, s),
                         "aq_awq_search: final pack");
+}
+
+aq_status aq_awq_fold_norm(const void* norm_w, int32_t w_dtype, const float* chan_scale, int64_t K, float* folded,
+                           void* stream) {
+  AQ_REQUIRE(w_dtype == AQ_F32 || w_dtype == AQ_BF16, "aq_awq_fold_norm: w_dtype must be AQ_F32 or AQ_BF16 (got %d)",
+             w_dtype);
+  AQ_REQUIRE(K > 0 && K < kDimLimit, "aq_awq_fold_norm: K out of range (%lld)", (long long)K);
+  AQ_PTR(norm_w, w_dtype == AQ_BF16 ? 2 : 4, "norm_w");
+  AQ_PTR(chan_scale, 4, "chan_scale");
+  AQ_PTR(folded, 4, "folded");
+  if (fault_injected()) return fail(AQ_ERUNTIME, "aq_awq_fold_norm: injected launch failure");
+  return runtime_status(aq::launch_fold_norm(norm_w, w_dtype == AQ_BF16, chan_scale, (int)K, folded,
+                                             (hipStream_t)stream),
+                        "aq_awq_fold_norm");
 }
 
 size_t aq_fp4_gemm_workspace(int64_t M, int64_t N, int64_t K) {

@@ -51,12 +51,13 @@ size_t fp4_quantize_workspace_bytes(int64_t N, int64_t K);
 // ts: one fp32 on the device (written); partial: fp4_quantize_workspace_bytes of device memory
 hipError_t launch_fp4_quantize(const void* W, bool w_bf16, int64_t N, int64_t K, uint8_t* codes, uint8_t* bscale,
                                float* ts, float* partial, hipStream_t stream);
-int sumsq_gemm_blocks(int M, int N);
+int64_t sumsq_gemm_blocks(int64_t M, int64_t N);
 hipError_t launch_sumsq_gemm(const uint16_t* X, int M, int K, const uint16_t* E, int N, double* partial,
                              hipStream_t stream);
 int absmean_row_slices(int64_t T, int64_t K);
 hipError_t launch_act_absmean(const uint16_t* X, int64_t T, int64_t K, double* sum_abs, float* mean, int64_t count,
                               double* work, hipStream_t stream);
+hipError_t launch_fold_norm(const void* w, bool w_bf16, const float* s, int K, float* out, hipStream_t stream);
 hipError_t launch_search_select(const double* partial, int nblocks, int n_grid, double count, const float* sgrid,
                                 int K, double* mse, int32_t* best, float* best_scale, hipStream_t stream);
 

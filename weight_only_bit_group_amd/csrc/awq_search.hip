@@ -49,6 +49,26 @@ __global__ __launch_bounds__(256) void search_pick_kernel(const double* __restri
   for (int k = threadIdx.x; k < K; k += 256) best_scale[k] = src[k];
 }
 
+// The RMSNorm fold of the chosen channel scale: the norm's consumers hold
+// Q(W diag(s)), so the norm's output is divided by s through its weight,
+// w'_k = fl32(w_k / s_k), one IEEE fp32 division per channel ("Lance-Quant",
+// grid-search / grouping section: the scale is folded into the preceding norm).
+template <bool BF16>
+__global__ __launch_bounds__(256) void fold_norm_kernel(const void* __restrict__ w, const float* __restrict__ s,
+                                                        int K, float* __restrict__ out) {
+  const int k = blockIdx.x * 256 + threadIdx.x;
+  if (k >= K) return;
+  const float wk = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(w)[k]) : static_cast<const float*>(w)[k];
+  out[k] = wk / s[k];
+}
+
+hipError_t launch_fold_norm(const void* w, bool w_bf16, const float* s, int K, float* out, hipStream_t stream) {
+  const dim3 grid((unsigned)((K + 255) / 256));
+  if (w_bf16) hipLaunchKernelGGL(fold_norm_kernel<true>, grid, dim3(256), 0, stream, w, s, K, out);
+  else hipLaunchKernelGGL(fold_norm_kernel<false>, grid, dim3(256), 0, stream, w, s, K, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_search_select(const double* partial, int nblocks, int n_grid, double count, const float* sgrid,
                                 int K, double* mse, int32_t* best, float* best_scale, hipStream_t stream) {
   hipLaunchKernelGGL(search_mse_kernel, dim3(n_grid), dim3(256), 0, stream, partial, nblocks, count, mse);

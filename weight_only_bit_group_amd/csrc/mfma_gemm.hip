@@ -943,7 +943,11 @@ hipError_t launch_fp4_gemm(const uint16_t* X, int M, int K, const uint8_t* codes
   return launch_tiles<B_FP4, 64>(a, stream);
 }
 
-int sumsq_gemm_blocks(int M, int N) { return M > kWideM ? tiles(M, N, 256) : tiles(M, N, 128); }  // SPLIT tiles
+// SPLIT tiles (64-bit: the caller bounds the count before launching)
+int64_t sumsq_gemm_blocks(int64_t M, int64_t N) {
+  const int64_t bm = M > kWideM ? 256 : 128;
+  return ((M + bm - 1) / bm) * ((N + BN - 1) / BN);
+}
 
 hipError_t launch_sumsq_gemm(const uint16_t* X, int M, int K, const uint16_t* E, int N, double* partial,
                              hipStream_t stream) {

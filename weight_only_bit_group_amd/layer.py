@@ -56,7 +56,6 @@ class W4A16Linear(torch.nn.Module):
         self.register_buffer("zeros", zeros.contiguous())
         self.register_buffer("bias", None if bias is None else bias.detach().float().contiguous())
         self.split_sizes = [self.out_features]
-        self._ws = None
 
     @classmethod
     def from_weight(cls, weight: torch.Tensor, group: int, chan_scale: torch.Tensor | None = None,
@@ -91,14 +90,6 @@ class W4A16Linear(torch.nn.Module):
         out.split_sizes = [m.out_features for m in mods]
         return out
 
-    def _workspace(self, m: int):
-        need = B.aq_w4a16_gemm_workspace(m, self.out_features, self.in_features, self.group)
-        if need == 0:
-            return torch.empty(0, dtype=torch.uint8, device=self.packed.device)
-        if self._ws is None or self._ws.numel() < need:
-            self._ws = torch.empty(need, dtype=torch.uint8, device=self.packed.device)
-        return self._ws
-
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         if x.shape[-1] != self.in_features:
             raise ValueError(f"expected {self.in_features} input features, got {x.shape[-1]}")
@@ -107,7 +98,9 @@ class W4A16Linear(torch.nn.Module):
         if m <= 16:
             y = B.aq_w4a16_gemv(x2, self.packed, self.scales, self.zeros, self.group)
         else:
-            y = B.aq_w4a16_gemm(x2, self.packed, self.scales, self.zeros, self.group, workspace=self._workspace(m))
+            # the staging matrix (as large as a bf16 copy of W) is allocated per call: torch's
+            # caching allocator hands the block back in stream order, and no module keeps one
+            y = B.aq_w4a16_gemm(x2, self.packed, self.scales, self.zeros, self.group)
         if self.bias is not None:
             y = y + self.bias
         return y.reshape(*x.shape[:-1], self.out_features)
@@ -155,7 +148,7 @@ def norm_group_awq(norm_weight: torch.Tensor, linears, x_norm: torch.Tensor, gro
     B.aq_act_absmean(x, sum_abs, t, mean)          # EINVAL (ValueError) for T == 0
     w_cat = torch.cat(ws, dim=0).contiguous()
     res = B.aq_awq_search(x[:search_tokens].contiguous(), mean.cpu(), w_cat, group, n_grid)
-    folded = norm_weight.detach().float() / res["best_scale"]
+    folded = B.aq_awq_fold_norm(norm_weight.detach().contiguous(), res["best_scale"])
     out, n0 = [], 0
     for lin, w in zip(linears, ws):
         n1 = n0 + w.shape[0]
@@ -181,7 +174,6 @@ class W8A16Linear(torch.nn.Module):
         self.register_buffer("scales", scales.contiguous())
         self.register_buffer("zeros", zeros.contiguous())
         self.register_buffer("bias", None if bias is None else bias.detach().float().contiguous())
-        self._ws = None
 
     @classmethod
     def from_weight(cls, weight: torch.Tensor, group: int, chan_scale: torch.Tensor | None = None,
@@ -197,10 +189,8 @@ class W8A16Linear(torch.nn.Module):
         if m <= 16:
             y = B.aq_w8a16_gemv(x2, self.codes, self.scales, self.zeros, self.group)
         else:
-            need = B.aq_w8a16_gemm_workspace(m, self.out_features, self.in_features, self.group)
-            if self._ws is None or self._ws.numel() < need:
-                self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.codes.device)
-            y = B.aq_w8a16_gemm(x2, self.codes, self.scales, self.zeros, self.group, workspace=self._ws)
+            # per-call staging matrix, as for W4A16Linear
+            y = B.aq_w8a16_gemm(x2, self.codes, self.scales, self.zeros, self.group)
         if self.bias is not None:
             y = y + self.bias
         return y.reshape(*x.shape[:-1], self.out_features)
