@@ -150,6 +150,24 @@ aq_status aq_act_absmean(const uint16_t* X, int64_t T, int64_t K, double* sum_ab
                          int64_t total_count, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * aq_act_absmean without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops, harnesses that
+ * forbid allocation).  Same arguments (less the workspace), results (bit for
+ * bit) and errors as aq_act_absmean.  The partial sums live in a file-scope
+ * device array of the library (8 MiB per GPU, held until the process ends), so:
+ *   - it serves any (T, K) with aq_act_absmean_workspace(T, K) <= 8 MiB (every
+ *     K up to 2^20 channels, any T); larger sizes return AQ_EINVAL;
+ *   - every call on one GPU shares that GPU's array: calls that overlap on one
+ *     GPU (different streams, or host threads without ordering) race and give
+ *     wrong sums; calls ordered on one stream are safe (each call rewrites every
+ *     partial it reads, nothing has to start at zero);
+ *   - it uses the array of the current device: `stream` must belong to it.
+ * No device memory is allocated or freed by the call.
+ */
+aq_status aq_act_absmean_noalloc(const uint16_t* X, int64_t T, int64_t K, double* sum_abs, float* mean_out,
+                                 int64_t total_count, void* stream);
+
+/*
  * AWQ alpha-grid search and final packing.
  * Source: "Lance-Quant" (zingnex.cn), grid-search / grouping section (grid
  * search of the AWQ scale for a norm and its consuming linears, then INT4 group

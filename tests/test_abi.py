@@ -148,6 +148,24 @@ def test_absmean_einval(lib):
     assert f(FAKE, 1024, 256, FAKE, FAKE + 1, 1024, FAKE, ws, None) == _lib.AQ_EINVAL
 
 
+def test_absmean_noalloc_einval(lib):
+    """The allocation-free abs-mean: the same argument checks as aq_act_absmean, and sizes whose
+    partial sums exceed its 8 MiB scratch are refused before anything runs (every K up to 2^20
+    fits)."""
+    f = lib.aq_act_absmean_noalloc
+    assert f(FAKE, 0, 256, FAKE, None, 0, None) == _lib.AQ_EINVAL
+    assert "empty calibration" in _lib.last_error()
+    assert f(FAKE, 1024, 250, FAKE, None, 1024, None) == _lib.AQ_EINVAL     # K % 8
+    assert f(FAKE, 1024, 256, FAKE, None, 100, None) == _lib.AQ_EINVAL     # count < T
+    assert f(FAKE, 1024, 256, FAKE + 4, None, 1024, None) == _lib.AQ_EINVAL
+    assert f(None, 1024, 256, FAKE, None, 1024, None) == _lib.AQ_EINVAL
+    big = 1048584                                                          # partials of 8.4 MB
+    assert lib.aq_act_absmean_workspace(1 << 20, big) > 8 << 20
+    assert f(FAKE, 1 << 20, big, FAKE, None, 1 << 20, None) == _lib.AQ_EINVAL
+    assert "scratch" in _lib.last_error()
+    assert lib.aq_act_absmean_workspace(1 << 20, 1 << 20) <= 8 << 20
+
+
 def test_search_einval(lib):
     T, N, K, g, ng = 64, 32, 128, 64, 20
     ws = lib.aq_awq_search_workspace(T, N, K, g, ng)
@@ -240,6 +258,7 @@ def test_injected_runtime_failure(lib, monkeypatch):
     ws = lib.aq_act_absmean_workspace(64, 64)
     assert lib.aq_act_absmean(FAKE, 64, 64, FAKE, None, 64, FAKE, ws, None) == _lib.AQ_ERUNTIME
     assert lib.aq_awq_fold_norm(FAKE + 2, 1, FAKE, 64, FAKE, None) == _lib.AQ_ERUNTIME   # bf16: 2-byte aligned
+    assert lib.aq_act_absmean_noalloc(FAKE, 64, 64, FAKE, None, 64, None) == _lib.AQ_ERUNTIME
     # validation still wins over the injected fault
     assert _qp(lib, g=5) == _lib.AQ_EINVAL
 

@@ -30,6 +30,7 @@ SIGNATURES = {
     "aq_w4a16_gemm": (_I32, [_P, _I64, _I64, _P, _P, _P, _I64, _I32, _P, _P, _SZ, _P]),
     "aq_act_absmean_workspace": (_SZ, [_I64, _I64]),
     "aq_act_absmean": (_I32, [_P, _I64, _I64, _P, _P, _I64, _P, _SZ, _P]),
+    "aq_act_absmean_noalloc": (_I32, [_P, _I64, _I64, _P, _P, _I64, _P]),
     "aq_awq_search_workspace": (_SZ, [_I64, _I64, _I64, _I32, _I32]),
     "aq_awq_search": (_I32, [_P, _I64, _P, _P, _I32, _I64, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "aq_awq_fold_norm": (_I32, [_P, _I32, _P, _I64, _P, _P]),

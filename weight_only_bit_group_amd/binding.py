@@ -153,6 +153,19 @@ def aq_act_absmean(X, sum_abs, total_count: int, mean_out=None, workspace=None):
     return sum_abs, mean_out
 
 
+def aq_act_absmean_noalloc(X, sum_abs, total_count: int, mean_out=None):
+    """aq_act_absmean with the library's own scratch (no workspace, nothing allocated)."""
+    _need(X, "X", torch.bfloat16, 2)
+    _need(sum_abs, "sum_abs", torch.float64, 1)
+    t, k = X.shape
+    if mean_out is not None:
+        _need(mean_out, "mean_out", torch.float32, 1)
+    st = _lib.load().aq_act_absmean_noalloc(X.data_ptr(), t, k, sum_abs.data_ptr(), _ptr(mean_out), total_count,
+                                            _stream(X))
+    check(st, "aq_act_absmean_noalloc")
+    return sum_abs, mean_out
+
+
 def aq_awq_search_workspace(T: int, N: int, K: int, group: int, n_grid: int = 20) -> int:
     return int(_lib.load().aq_awq_search_workspace(T, N, K, group, n_grid))
 

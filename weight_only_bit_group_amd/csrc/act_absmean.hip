@@ -13,10 +13,41 @@
 // channel's total.  Partials go to a workspace [row slices][K] (about 1024 blocks
 // in all) and a second kernel adds them in a fixed order, so the result is
 // deterministic.
+#include <mutex>
+
 #include "aq_device.h"
 #include "aq_kernels.h"
 
 namespace aq {
+
+// Scratch of the allocation-free entry point: the fp64 partial sums [row slices][K],
+// a file-scope device array (one copy per GPU, held until the process ends).  Host
+// code never passes the array's name to a kernel (on the host it is only a stand-in
+// symbol): its device address comes from hipGetSymbolAddress, looked up once per
+// device with that device current, and cached.
+constexpr size_t kScratchDoubles = size_t(1) << 20;   // 8 MiB
+static __device__ __align__(256) double scratch[kScratchDoubles];
+
+size_t absmean_scratch_bytes() { return kScratchDoubles * sizeof(double); }
+
+hipError_t absmean_scratch(double** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static double* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = static_cast<double*>(p);
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 constexpr int kColsPerBlock = 512;
 

@@ -299,6 +299,29 @@ aq_status aq_act_absmean(const uint16_t* X, int64_t T, int64_t K, double* sum_ab
                         "aq_act_absmean");
 }
 
+aq_status aq_act_absmean_noalloc(const uint16_t* X, int64_t T, int64_t K, double* sum_abs, float* mean_out,
+                                 int64_t total_count, void* stream) {
+  AQ_REQUIRE(T > 0, "aq_act_absmean_noalloc: empty calibration data (T = %lld)", (long long)T);
+  AQ_REQUIRE(T < (int64_t(1) << 40), "aq_act_absmean_noalloc: T out of range");
+  AQ_REQUIRE(K > 0 && K < kDimLimit && K % 8 == 0,
+             "aq_act_absmean_noalloc: K must be a positive multiple of 8 (got %lld)", (long long)K);
+  AQ_REQUIRE(total_count >= T, "aq_act_absmean_noalloc: total_count (%lld) must include this chunk's T (%lld)",
+             (long long)total_count, (long long)T);
+  AQ_PTR(X, 16, "X");
+  AQ_PTR(sum_abs, 8, "sum_abs");
+  if (mean_out) AQ_REQUIRE(aligned(mean_out, 4), "mean_out must be 4-byte aligned");
+  const size_t need = aq_act_absmean_workspace(T, K);
+  AQ_REQUIRE(need <= aq::absmean_scratch_bytes(),
+             "aq_act_absmean_noalloc: %lld channels need %zu bytes of partial sums, beyond the %zu-byte scratch",
+             (long long)K, need, aq::absmean_scratch_bytes());
+  if (fault_injected()) return fail(AQ_ERUNTIME, "aq_act_absmean_noalloc: injected launch failure");
+  double* scratch = nullptr;
+  const hipError_t e = aq::absmean_scratch(&scratch);
+  if (e != hipSuccess) return runtime_status(e, "aq_act_absmean_noalloc: scratch address");
+  return runtime_status(aq::launch_act_absmean(X, T, K, sum_abs, mean_out, total_count, scratch, (hipStream_t)stream),
+                        "aq_act_absmean_noalloc");
+}
+
 size_t aq_awq_search_workspace(int64_t T, int64_t N, int64_t K, int32_t group, int32_t n_grid) {
   if (n_grid < 1 || n_grid > 64 || !valid_group(group) || !search_dims_ok(T, N, K)) return 0;
   return search_layout(T, N, K, n_grid).total;

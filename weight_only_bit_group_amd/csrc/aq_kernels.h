@@ -55,6 +55,10 @@ int64_t sumsq_gemm_blocks(int64_t M, int64_t N);
 hipError_t launch_sumsq_gemm(const uint16_t* X, int M, int K, const uint16_t* E, int N, double* partial,
                              hipStream_t stream);
 int absmean_row_slices(int64_t T, int64_t K);
+// the allocation-free entry point's scratch: its size, and its device address on the
+// current device (looked up once per device)
+size_t absmean_scratch_bytes();
+hipError_t absmean_scratch(double** ptr);
 hipError_t launch_act_absmean(const uint16_t* X, int64_t T, int64_t K, double* sum_abs, float* mean, int64_t count,
                               double* work, hipStream_t stream);
 hipError_t launch_fold_norm(const void* w, bool w_bf16, const float* s, int K, float* out, hipStream_t stream);
