@@ -27,6 +27,11 @@ group 64):
            gate|up fused: four launches per layer), averaged over
            a graph-replayed stack of 12 layers (536 MB)
 
+  widen    the configurations around the headline shape: decode at M = 4 and at group
+           128 (M = 1, 4, 16); the prefill GEMM at M = 512 (gate and q shapes); a
+           36-layer stream of all seven linears (random weights packed on the device,
+           1.6 GB) at M = 512 and M = 4096; FP4 on the [4096, 14336] (K = 14336) shape
+
 Launches are bracketed by HIP events on the stream they run on (torch's current
 stream, which the binding passes to the library): one event pair per launch (five
 back-to-back calls for the short single-kernel rows: pack, pack_sym, pack8,
@@ -39,6 +44,12 @@ the decode GEMV's HBM throughput (algorithmic bytes / average launch duration);
 the GEMM's TFLOP/s and the other stages are reported beside it, and, as context
 only, torch's dense bf16 matmul (the vendor BLAS) on the unquantized prefill
 weight (`context_torch_bf16_mm_m4096`).
+
+Beside the path (outside the timed steps) the run measures the ceilings the roofline
+fractions are also stated against (libaq_probe.so): an empty kernel, a pure streaming
+read of exactly the decode GEMV's bytes at its launch shape and at the best of a few
+shapes, and MFMA-only loops.  Every row reports the mean over the timed steps and the
+10th / 50th / 90th percentiles of the per-step values.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -67,6 +78,8 @@ CAL_T, CAL_SUB = 65536, 4096
 LAYER_STACK = 12
 N8_COPIES = 24
 FP4_COPIES = 12
+PRE_LAYERS = 36
+PRE_M = (512, 4096)
 
 
 def gemv_bytes(m, n, k, g):
@@ -102,31 +115,222 @@ def _traffic(kernel_key, files, launches_bytes):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(budget_s=12.0):
-    """The CPU oracle, untuned, on a bounded sample of the same workload (decode GEMV at M = 1)."""
-    from oracle import int4
+def _timeit(fn, budget_s, max_calls=1000):
+    """(calls, seconds) of fn repeated until budget_s has passed (at least once)."""
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or calls >= max_calls:
+            return calls, el
+
+
+def cpu_baseline(budget_s=6.0):
+    """The CPU oracle, untuned, timed on this host on bounded samples of the same workloads.
+
+    `value` is the headline's decode GEMV (gate shape, M = 1); `items` holds the other
+    configurations, each with the sample it ran and, where only part of the workload ran,
+    the stated extrapolation to the whole.
+    """
+    from oracle import awq, fp4, int4, stats
     from weight_only_bit_group_amd import synth
     try:
         import threadpoolctl
         threads = max(i["num_threads"] for i in threadpoolctl.threadpool_info()) or 1
     except Exception:  # pragma: no cover
         threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
-    wb = synth.layer_weight_bf16(1, "gate_proj")
-    w = synth.bf16_bits_to_f32(wb)
-    p, s, z = int4.quantize_pack(w, G_)
+    cores = len(os.sched_getaffinity(0))
+    items = {}
+    w = {name: synth.bf16_bits_to_f32(synth.layer_weight_bf16(1, name)) for name, _, _ in synth.LAYER_LINEARS}
+    packs = {name: int4.quantize_pack(w[name], G_) for name in w}
+
+    # C2 headline: decode GEMV, gate shape, M = 1
+    p, s_, z = packs["gate_proj"]
     x = synth.bf16_bits_to_f32(synth.layer_activations_bf16(1, 1, K_))
-    calls, t0 = 0, time.perf_counter()
-    while True:
-        int4.forward(x, p, s, z, G_)
-        calls += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or calls >= 200:
-            break
+    calls, el = _timeit(lambda: int4.forward(x, p, s_, z, G_), budget_s, 200)
     gbs = calls * gemv_bytes(1, N_, K_, G_) / el / 1e9
+
+    # C1: the 256 x 256 fp32 single linear, pack + M = 8 product
+    c1 = synth.single_linear(0)
+    xc1 = synth.bf16_bits_to_f32(c1["X"])
+    calls1, el1 = _timeit(lambda: int4.forward(xc1, *int4.quantize_pack(c1["W"], 128), 128), 1.0)
+    items["c1_pack_and_gemm"] = {"ms": round(el1 / calls1 * 1e3, 3), "sample": "full (W 256x256 fp32, X 8x256)"}
+
+    # C2: pack of the gate weight, and the seven linears of one layer at M = 1
+    t0 = time.perf_counter()
+    int4.quantize_pack(w["gate_proj"], G_)
+    el_pack = time.perf_counter() - t0
+    items["c2_pack_gate"] = {"ms": round(el_pack * 1e3, 1),
+                             "GB/s": round(pack_bytes(N_, K_, G_) / el_pack / 1e9, 4), "sample": "full, one call"}
+    xs = {k: synth.bf16_bits_to_f32(synth.layer_activations_bf16(1, 1, k)) for k in (2048, 11008)}
+    t0 = time.perf_counter()
+    for name, n, k in synth.LAYER_LINEARS:
+        int4.forward(xs[k], *packs[name], G_)
+    el_layer = time.perf_counter() - t0
+    lb = sum(gemv_bytes(1, n, k, G_) for _, n, k in synth.LAYER_LINEARS)
+    items["c2_layer_gemv_m1"] = {"ms": round(el_layer * 1e3, 1), "GB/s": round(lb / el_layer / 1e9, 4),
+                                 "sample": "full: the 7 linears of one layer at M = 1, g = 64"}
+
+    # C3: prefill GEMM at M = 4096 on the gate linear (one of the 7 x 36 linears)
+    x3 = synth.bf16_bits_to_f32(synth.layer_activations_bf16(3, 4096, K_))
+    t0 = time.perf_counter()
+    int4.forward(x3, p, s_, z, G_)
+    el3 = time.perf_counter() - t0
+    items["c3_gemm_gate_m4096"] = {"ms": round(el3 * 1e3, 1),
+                                   "GFLOP/s": round(2.0 * 4096 * N_ * K_ / el3 / 1e9, 2),
+                                   "sample": "stated subset: the gate linear only (1 of 252 in the 36-layer stream)"}
+
+    # C4: abs-mean statistic (exact fsum per channel) and the alpha search
+    xcal = synth.bf16_bits_to_f32(synth.calibration_rows_bf16(4, 8192, K_))
+    t0 = time.perf_counter()
+    stats.absmean(xcal)
+    el4 = time.perf_counter() - t0
+    items["c4_absmean"] = {"ms_extrapolated": round(el4 * 8 * 1e3, 1),
+                           "GB/s": round(2.0 * 8192 * K_ / el4 / 1e9, 4),
+                           "sample": "8192 of the 65536 tokens (x8 extrapolated to the whole)"}
+    xsub = xcal[:4096]
+    m = stats.absmean(xsub)
+    for tag, name in (("q", "q_proj"), ("gate", "gate_proj")):
+        # one candidate of the grid (alpha = 0.35): scales, qdq error matrix, output MSE
+        t0 = time.perf_counter()
+        awq.output_mse(xsub, awq.error_matrix(w[name], G_, awq.candidate_scale(m, 0.35)))
+        el_a = time.perf_counter() - t0
+        n_, k_ = synth.LINEAR_SHAPES[name]
+        items[f"c4_search_{tag}"] = {"ms_extrapolated": round(el_a * 20 * 1e3, 1),
+                                     "sample": f"{name} [{n_}, {k_}], T = 4096: one of the 20 alphas timed, "
+                                               f"x20 extrapolated to the grid"}
+
+    # C5: FP4 decode at M = 1 on both MLP shapes, M = 2048 on 256 output rows
+    for tag, (n5, k5) in (("up", (FP4_N, FP4_K)), ("down", (FP4_K, FP4_N))):
+        c5, b5, t5 = synth.random_fp4_operands(5, n5, k5)
+        x5 = synth.bf16_bits_to_f32(synth.layer_activations_bf16(5, 1, k5))
+        t0 = time.perf_counter()
+        fp4.forward(x5, c5, b5, t5)
+        el5 = time.perf_counter() - t0
+        items[f"c5_fp4_gemv_m1_{tag}"] = {"ms": round(el5 * 1e3, 1),
+                                          "GB/s": round(fp4_bytes(1, n5, k5) / el5 / 1e9, 4),
+                                          "sample": f"full: W [{n5}, {k5}] (N, K), M = 1"}
+    c5, b5, t5 = synth.random_fp4_operands(5, FP4_N, FP4_K)
+    x5 = synth.bf16_bits_to_f32(synth.layer_activations_bf16(5, 2048, FP4_K))
+    t0 = time.perf_counter()
+    fp4.forward(x5, c5[:256], b5[:256], t5)
+    el5 = time.perf_counter() - t0
+    items["c5_fp4_gemm_m2048"] = {"GFLOP/s": round(2.0 * 2048 * 256 * FP4_K / el5 / 1e9, 2),
+                                  "sample": "stated subset: 256 of the 14336 output rows at M = 2048"}
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "sample": f"oracle.int4.forward (fp64 dequantize + matvec) on the gate shape at M=1, "
-                      f"{calls} calls in {el:.1f} s on {len(os.sched_getaffinity(0))} visible host cores "
-                      f"(numpy elementwise single-threaded, BLAS {threads} threads)"}
+                      f"{calls} calls in {el:.1f} s on {cores} visible host cores "
+                      f"(numpy elementwise single-threaded, BLAS {threads} threads)",
+            "host_cores_visible": cores, "blas_threads": int(threads), "items": items}
+
+
+def _graph(fn):
+    """fn captured once in a HIP graph (after one eager run on a side stream)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def _replay_us(graph, launches, reps=20):
+    """Per-launch microseconds of a graph of `launches` back-to-back kernels (median of reps)."""
+    import torch
+    vals = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        graph.replay()
+        b.record()
+        b.synchronize()
+        vals.append(a.elapsed_time(b) * 1e3 / launches)
+    return float(np.median(vals))
+
+
+def ceilings(dev):
+    """Measured ceilings (libaq_probe.so), outside the timed steps."""
+    import torch
+    from weight_only_bit_group_amd import probe
+    stream = torch.cuda.current_stream().cuda_stream
+    sink = torch.zeros(256, dtype=torch.float32, device=dev)
+    out = {}
+    g = _graph(lambda: [probe.empty(1, 64, torch.cuda.current_stream().cuda_stream) for _ in range(N_COPIES)])
+    out["empty_kernel_us"] = round(_replay_us(g, N_COPIES), 3)
+    gemv_grid = ((N_ + 3) // 4 + 3) // 4     # the M = 1 gate GEMV: four rows per wave, four waves per block
+    g = _graph(lambda: [probe.empty(gemv_grid, 256, torch.cuda.current_stream().cuda_stream)
+                        for _ in range(N_COPIES)])
+    out["empty_kernel_gemv_grid_us"] = round(_replay_us(g, N_COPIES), 3)
+    nbytes = gemv_bytes(1, N_, K_, G_)
+    stride = (nbytes + 255) // 256 * 256
+    buf = torch.randint(0, 255, (N_COPIES * stride,), dtype=torch.uint8, device=dev)
+    units = nbytes // 16
+
+    def read_graph(blocks, unroll):
+        return _graph(lambda: [probe.stream_read(buf.data_ptr() + i * stride, nbytes, blocks, unroll, sink.data_ptr(),
+                                                 torch.cuda.current_stream().cuda_stream)
+                               for i in range(N_COPIES)])
+
+    sweep = {}
+    for blocks in (256, 512, gemv_grid, 1024, 2048):
+        need = -(-units // (blocks * 256))
+        unroll = next((u for u in (1, 2, 4, 5, 8) if u >= need), 8)
+        sweep[f"{blocks}x256_u{unroll}"] = round(_replay_us(read_graph(blocks, unroll), N_COPIES), 3)
+    at_shape = sweep[f"{gemv_grid}x256_u{next(u for u in (1, 2, 4, 5, 8) if u >= -(-units // (gemv_grid * 256)))}"]
+    best = min(sweep.values())
+    out["stream_read_bytes"] = nbytes
+    out["stream_read_us"] = sweep
+    out["stream_read_gemv_shape_us"] = at_shape
+    out["stream_read_gemv_shape_GBs"] = round(nbytes / (at_shape * 1e-6) / 1e9, 1)
+    out["stream_read_best_us"] = best
+    out["stream_read_best_GBs"] = round(nbytes / (best * 1e-6) / 1e9, 1)
+    del buf
+    # a large streaming read (HBM bandwidth with the launch amortised): 4 GiB in one launch
+    big = torch.empty(1 << 32, dtype=torch.uint8, device=dev)
+    big.fill_(1)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(5):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        probe.stream_read(big.data_ptr(), big.numel(), 4096, 8, sink.data_ptr(), stream)
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b) * 1e-3)
+    out["stream_read_4GiB_GBs"] = round(big.numel() / float(np.median(ts)) / 1e9, 1)
+    del big
+    # MFMA-only loops: 2 and 4 waves per SIMD (512 / 1024 blocks of 4 waves on 256 CUs)
+    for big_tile, name, accs in ((True, "32x32x16", 4), (False, "16x16x32", 8)):
+        flop_per = 2 * 32 * 32 * 16 if big_tile else 2 * 16 * 16 * 32
+        for blocks in (512, 1024):
+            iters = 4096
+            ts = []
+            for _ in range(4):
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                probe.mfma_loop(big_tile, blocks, iters, sink.data_ptr(), stream)
+                b.record()
+                b.synchronize()
+                ts.append(a.elapsed_time(b) * 1e-3)
+            flops = blocks * 4 * iters * accs * flop_per
+            out[f"mfma_{name}_{blocks // 256}w_TFLOPs"] = round(flops / float(np.median(ts)) / 1e12, 1)
+    out["mfma_best_TFLOPs"] = max(v for k, v in out.items() if k.startswith("mfma_"))
+    return out
+
+
+def _pct(vals):
+    v = np.asarray(vals, dtype=np.float64)
+    return float(v.mean()), float(np.percentile(v, 10)), float(np.percentile(v, 50)), float(np.percentile(v, 90))
 
 
 def main():
@@ -135,6 +339,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the W4A16 path has no multi-GPU mode here (asked for --gpus {args.gpus}); "
@@ -162,21 +367,21 @@ def main():
         w.view(-1)[idx] *= 10.0
         return w.to(torch.bfloat16)
 
-    def acts_bf16(m, k, outlier_ch, scale=20.0):
+    def acts_bf16(m, k, outlier_ch=None, scale=20.0):
         x = torch.randn((m, k), generator=gen, device=dev, dtype=torch.float32)
-        ch = torch.randperm(k, generator=gen, device=dev)[:outlier_ch]
+        ch = torch.randperm(k, generator=gen, device=dev)[:round(0.01 * k) if outlier_ch is None else outlier_ch]
         x[:, ch] *= scale
         return x.to(torch.bfloat16)
 
-    # weights: the gate projection and 40 distinct packed copies for the rotating GEMV
+    # weights: the gate projection and 40 distinct packed copies for the rotating GEMV, at
+    # group 64 and (other weights) at group 128
     w_gate = weight_bf16(N_, K_)
-    copies = []
-    for i in range(N_COPIES):
-        copies.append(B.aq_quantize_pack(w_gate if i == 0 else weight_bf16(N_, K_), G_))
+    copies = [B.aq_quantize_pack(w_gate if i == 0 else weight_bf16(N_, K_), G_) for i in range(N_COPIES)]
+    copies128 = [B.aq_quantize_pack(weight_bf16(N_, K_), 128) for _ in range(N_COPIES)]
     torch.cuda.synchronize()
-    x1 = acts_bf16(1, K_, round(0.01 * K_))
+    x1 = acts_bf16(1, K_)
     y1 = torch.empty((1, N_), dtype=torch.float32, device=dev)
-    xg = acts_bf16(M_GEMM, K_, round(0.01 * K_))
+    xg = acts_bf16(M_GEMM, K_)
     yg = torch.empty((M_GEMM, N_), dtype=torch.float32, device=dev)
     pk = [torch.empty_like(t) for t in copies[0]]
     # calibration activations: z * c_k, c_k = exp(1.5 N(0,1))
@@ -189,19 +394,18 @@ def main():
     absmean_host = mean.cpu().numpy().copy()
     xsub = xcal[:CAL_SUB].contiguous()
     ws_search = torch.empty(B.aq_awq_search_workspace(CAL_SUB, N_, K_, G_, 20), dtype=torch.uint8, device=dev)
-    codes_np, bsc_np, ts = synth.random_fp4_operands(5, FP4_N, FP4_K)
-    codes = torch.from_numpy(codes_np).to(dev)
-    bsc = torch.from_numpy(bsc_np).to(dev)
-    # FP4 decode: 12 distinct operand copies (12 x 33 MB > the 256 MB MALL), graph-replayed
-    fp4_copies = [(codes, bsc)] + [tuple(torch.from_numpy(a).to(dev) for a in
-                                         synth.random_fp4_operands(5 + i, FP4_N, FP4_K)[:2])
-                                   for i in range(1, FP4_COPIES)]
-    xf1 = acts_bf16(1, FP4_K, round(0.01 * FP4_K))
-    xf2 = acts_bf16(FP4_M, FP4_K, round(0.01 * FP4_K))
-    yf1 = torch.empty((1, FP4_N), dtype=torch.float32, device=dev)
-    yf2 = torch.empty((FP4_M, FP4_N), dtype=torch.float32, device=dev)
+    # FP4 on both MLP shapes: [14336, 4096] ("up", the headline FP4 shape) and [4096, 14336]
+    # ("down", K = 14336); 12 distinct operand copies each (12 x 33 MB > the 256 MB MALL)
+    fp4_ops = {}
+    for tag, (n5, k5) in (("up", (FP4_N, FP4_K)), ("down", (FP4_K, FP4_N))):
+        ops = [tuple(torch.from_numpy(a).to(dev) for a in synth.random_fp4_operands(5 + i, n5, k5)[:2])
+               for i in range(FP4_COPIES)]
+        fp4_ops[tag] = dict(n=n5, k=k5, ops=ops, x1=acts_bf16(1, k5), xm=acts_bf16(FP4_M, k5),
+                            y1=torch.empty((1, n5), dtype=torch.float32, device=dev),
+                            ym=torch.empty((FP4_M, n5), dtype=torch.float32, device=dev),
+                            ws=torch.empty(B.aq_fp4_gemm_workspace(FP4_M, n5, k5), dtype=torch.uint8, device=dev))
+    ts = float(synth.random_fp4_operands(5, FP4_N, FP4_K)[2])
     ws_gemm = torch.empty(B.aq_w4a16_gemm_workspace(M_GEMM, N_, K_, G_), dtype=torch.uint8, device=dev)
-    ws_fp4 = torch.empty(B.aq_fp4_gemm_workspace(FP4_M, FP4_N, FP4_K), dtype=torch.uint8, device=dev)
     # FP4 encoder input: an fp32 weight of the FP4 shape, and its preallocated outputs
     w_fp4 = torch.randn((FP4_N, FP4_K), generator=gen, device=dev, dtype=torch.float32) * 0.02
     enc_out = dict(codes=torch.empty((FP4_N, FP4_K // 2), dtype=torch.uint8, device=dev),
@@ -245,7 +449,7 @@ def main():
     for _ in range(LAYER_STACK - 1):
         stack.append(fuse({name: L.W4A16Linear(*B.aq_quantize_pack(weight_bf16(n, k), G_), G_)
                            for name, n, k in synth.LAYER_LINEARS}))
-    x_in = [acts_bf16(1, k_in[names[0]], round(0.01 * k_in[names[0]])) for names in fused_groups]
+    x_in = [acts_bf16(1, k_in[names[0]]) for names in fused_groups]
     y_out = [torch.empty((1, f.out_features), dtype=torch.float32, device=dev) for f in stack[0]]
 
     def layer_decode():
@@ -253,32 +457,50 @@ def main():
             for i, f in enumerate(lay):
                 B.aq_w4a16_gemv(x_in[i], f.packed, f.scales, f.zeros, G_, out=y_out[i])
 
-    side2 = torch.cuda.Stream()
-    side2.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side2):
-        layer_decode()
-    torch.cuda.current_stream().wait_stream(side2)
-    torch.cuda.synchronize()
-    layer_graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(layer_graph):
-        layer_decode()
-    torch.cuda.synchronize()
+    layer_graph = _graph(layer_decode)
+
+    # the prefill stream: 36 layers x 7 linears of random bf16 weights, packed on the device
+    # (1.6 GB of packed triples), run at M = 512 and M = 4096 (staged path, one shared
+    # staging workspace sized for the largest linear)
+    pre_stack = []
+    for _ in range(PRE_LAYERS):
+        lay = []
+        for name, n, k in synth.LAYER_LINEARS:
+            wl = weight_bf16(n, k)
+            lay.append(B.aq_quantize_pack(wl, G_))
+            del wl
+        pre_stack.append(lay)
+    ws_pre = torch.empty(max(B.aq_w4a16_gemm_workspace(M_GEMM, n, k, G_) for _, n, k in synth.LAYER_LINEARS),
+                         dtype=torch.uint8, device=dev)
+    pre_x = {mm: {k: acts_bf16(mm, k) for k in (2048, 11008)} for mm in PRE_M}
+    pre_y = {mm: {n: torch.empty((mm, n), dtype=torch.float32, device=dev) for n in (2048, 256, 11008)}
+             for mm in PRE_M}
+
+    def prefill(mm):
+        def run():
+            for lay in pre_stack:
+                for (name, n, k), trip in zip(synth.LAYER_LINEARS, lay):
+                    B.aq_w4a16_gemm(pre_x[mm][k], *trip, G_, out=pre_y[mm][n], workspace=ws_pre)
+        return run
+
+    pre_graphs = {mm: _graph(prefill(mm)) for mm in PRE_M}
+    pre_flop = {mm: 2.0 * mm * PRE_LAYERS * sum(n * k for _, n, k in synth.LAYER_LINEARS) for mm in PRE_M}
     torch.cuda.synchronize()
 
     # context, not part of the path: torch's dense bf16 matmul (the vendor BLAS) on the prefill
     # shape with the unquantized bf16 weight, fp32 output like the W4A16 GEMM
     w_gate_t = w_gate.t()
-    events = {k: [] for k in ("ref_mm", "pack", "pack_sym", "pack8", "gemv8", "gemm8", "gemv", "gemv16", "gemm", "absmean", "search", "fp4_gemv", "fp4_gemm", "fp4_encode",
-                              "layer_awq", "layer_gemv")}
+    samples = {}
 
     # Short single-kernel rows run REPEAT identical calls back to back between one event
     # pair (the host enqueues a call faster than the kernel runs, so the launches follow
     # each other on the GPU) and report the average per call: one event pair around one
     # ~20 us kernel would add the events' own overhead (several us) to it.
     REPEAT = 5
-    repeated = ("pack", "pack_sym", "pack8", "absmean", "fp4_encode")
+    repeated = ("pack", "pack_sym", "pack8", "absmean", "fp4_encode", "gemm_m512", "gemm_m512_q")
+    per_call = {}   # row -> launches per timed unit (graph batches)
 
-    def timed(name, record, fn):
+    def timed(name, record, fn, launches=1):
         reps = REPEAT if name in repeated else 1
         if record:
             a = torch.cuda.Event(enable_timing=True)
@@ -287,104 +509,64 @@ def main():
             for _ in range(reps):
                 fn()
             b.record()
-            events[name].append((a, b))
+            samples.setdefault(name, []).append((a, b))
+            per_call[name] = reps * launches
         else:
             fn()
 
     # The decode GEMVs run back to back over the rotating copies, captured once in a HIP
-    # graph (as a decode loop does): replaying it launches the 40 kernels without the
-    # Python binding's per-call overhead (several microseconds, more than a launch), so the
-    # event pair around the replay measures the GPU, not the interpreter.
-    def gemv_batch():
-        for (p, s, z) in copies:
-            B.aq_w4a16_gemv(x1, p, s, z, G_, out=y1)
+    # graph (as a decode loop does): replaying it launches the kernels without the Python
+    # binding's per-call overhead (several microseconds, more than a launch), so the event
+    # pair around the replay measures the GPU, not the interpreter.
+    def gemv_graph(xm, cps, g):
+        y = torch.empty((xm.shape[0], N_), dtype=torch.float32, device=dev)
+        return _graph(lambda: [B.aq_w4a16_gemv(xm, p, s, z, g, out=y) for (p, s, z) in cps])
 
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        gemv_batch()
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    gemv_graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(gemv_graph):
-        gemv_batch()
-    torch.cuda.synchronize()
-
-    # batched decode: the same 40 copies at M = 16 activation rows (the matrix-core path)
-    x16 = acts_bf16(16, K_, round(0.01 * K_))
-    y16 = torch.empty((16, N_), dtype=torch.float32, device=dev)
-
-    def gemv16_batch():
-        for (p, s, z) in copies:
-            B.aq_w4a16_gemv(x16, p, s, z, G_, out=y16)
-
-    side5 = torch.cuda.Stream()
-    side5.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side5):
-        gemv16_batch()
-    torch.cuda.current_stream().wait_stream(side5)
-    torch.cuda.synchronize()
-    gemv16_graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(gemv16_graph):
-        gemv16_batch()
-    torch.cuda.synchronize()
+    x4 = acts_bf16(4, K_)
+    x16 = acts_bf16(16, K_)
+    decode_graphs = {"gemv": gemv_graph(x1, copies, G_), "gemv_m4": gemv_graph(x4, copies, G_),
+                     "gemv16": gemv_graph(x16, copies, G_), "gemv_m1_g128": gemv_graph(x1, copies128, 128),
+                     "gemv_m4_g128": gemv_graph(x4, copies128, 128), "gemv_m16_g128": gemv_graph(x16, copies128, 128)}
 
     # INT8: the gate weight's 8-bit codes, 24 distinct copies for the rotating decode GEMV
     # (24 x 22.9 MB = 549 MB > 2 x the MALL), captured in a graph like the INT4 batch
     pk8 = B.aq_quantize_pack8(w_gate, G_)
     copies8 = [pk8] + [B.aq_quantize_pack8(weight_bf16(N_, K_), G_) for _ in range(N8_COPIES - 1)]
     ws8 = torch.empty(B.aq_w8a16_gemm_workspace(M_GEMM, N_, K_, G_), dtype=torch.uint8, device=dev)
-
-    def gemv8_batch():
-        for (c, s8, z8) in copies8:
-            B.aq_w8a16_gemv(x1, c, s8, z8, G_, out=y1)
-
-    side3 = torch.cuda.Stream()
-    side3.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side3):
-        gemv8_batch()
-    torch.cuda.current_stream().wait_stream(side3)
-    torch.cuda.synchronize()
-    gemv8_graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(gemv8_graph):
-        gemv8_batch()
-    torch.cuda.synchronize()
-
-    def fp4_gemv_batch():
-        for (c4, b4) in fp4_copies:
-            B.aq_fp4_gemm(xf1, c4, b4, ts, out=yf1)
-
-    side4 = torch.cuda.Stream()
-    side4.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side4):
-        fp4_gemv_batch()
-    torch.cuda.current_stream().wait_stream(side4)
-    torch.cuda.synchronize()
-    fp4_graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(fp4_graph):
-        fp4_gemv_batch()
-    torch.cuda.synchronize()
+    gemv8_graph = _graph(lambda: [B.aq_w8a16_gemv(x1, c, s8, z8, G_, out=y1) for (c, s8, z8) in copies8])
+    fp4_graphs = {tag: _graph(lambda f=f: [B.aq_fp4_gemm(f["x1"], c4, b4, ts, out=f["y1"]) for (c4, b4) in f["ops"]])
+                  for tag, f in fp4_ops.items()}
+    x512 = acts_bf16(512, K_)
+    y512 = torch.empty((512, N_), dtype=torch.float32, device=dev)
+    y512q = torch.empty((512, 2048), dtype=torch.float32, device=dev)
+    q_pack = pre_stack[0][0]
 
     def step(record):
         timed("pack", record, lambda: B.aq_quantize_pack(w_gate, G_, packed=pk[0], scales=pk[1], zeros=pk[2]))
         timed("pack_sym", record, lambda: B.aq_quantize_pack(w_gate, G_, packed=pk[0], scales=pk[1], zeros=pk[2],
                                                              sym=True))
-        timed("gemv", record, gemv_graph.replay)
-        timed("gemv16", record, gemv16_graph.replay)
+        for name, gr in decode_graphs.items():
+            timed(name, record, gr.replay, N_COPIES)
         timed("ref_mm", record, lambda: torch.mm(xg, w_gate_t, out_dtype=torch.float32))
         timed("pack8", record, lambda: B.aq_quantize_pack8(w_gate, G_, codes=pk8[0], scales=pk8[1], zeros=pk8[2]))
-        timed("gemv8", record, gemv8_graph.replay)
+        timed("gemv8", record, gemv8_graph.replay, N8_COPIES)
         timed("gemm8", record, lambda: B.aq_w8a16_gemm(xg, *pk8, G_, out=yg, workspace=ws8))
         p, s, z = copies[0]
         timed("gemm", record, lambda: B.aq_w4a16_gemm(xg, p, s, z, G_, out=yg, workspace=ws_gemm))
+        timed("gemm_m512", record, lambda: B.aq_w4a16_gemm(x512, p, s, z, G_, out=y512))
+        timed("gemm_m512_q", record, lambda: B.aq_w4a16_gemm(x512, *q_pack, G_, out=y512q))
         sum_abs.zero_()
         timed("absmean", record, lambda: B.aq_act_absmean(xcal, sum_abs, CAL_T, mean, ws_abs))
         timed("search", record, lambda: B.aq_awq_search(xsub, absmean_host, w_gate, G_, 20, ws_search))
-        timed("fp4_gemv", record, fp4_graph.replay)
-        timed("fp4_gemm", record, lambda: B.aq_fp4_gemm(xf2, codes, bsc, ts, out=yf2, workspace=ws_fp4))
+        for tag, f in fp4_ops.items():
+            timed(f"fp4_gemv_{tag}", record, fp4_graphs[tag].replay, FP4_COPIES)
+            timed(f"fp4_gemm_{tag}", record, lambda f=f: B.aq_fp4_gemm(f["xm"], *f["ops"][0], ts, out=f["ym"],
+                                                                      workspace=f["ws"]))
         timed("fp4_encode", record, lambda: B.aq_fp4_quantize(w_fp4, **enc_out))
         timed("layer_awq", record, layer_awq)
-        timed("layer_gemv", record, layer_graph.replay)
+        timed("layer_gemv", record, layer_graph.replay, LAYER_STACK)
+        for mm in PRE_M:
+            timed(f"prefill_m{mm}", record, pre_graphs[mm].replay, PRE_LAYERS)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -398,47 +580,52 @@ def main():
     wall = time.perf_counter() - t0
     print("[bench] timed region done", file=sys.stderr, flush=True)
 
-    ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in events.items()}
-    for k in repeated:
-        ms[k] /= REPEAT
-    ms["gemv"] /= N_COPIES
-    ms["gemv16"] /= N_COPIES
-    ms["gemv8"] /= N8_COPIES
-    ms["fp4_gemv"] /= FP4_COPIES
-    ms["layer_gemv"] /= LAYER_STACK
+    # per-launch (per-call, per-layer for the stacks) milliseconds of every step
+    per = {k: [a.elapsed_time(b) / per_call[k] for a, b in v] for k, v in samples.items()}
+    ms = {k: float(np.mean(v)) for k, v in per.items()}
+
+    def row(name, work=None, unit=None, scale=1.0):
+        mean_, p10, p50, p90 = _pct(per[name])
+        r = {"us": mean_ * 1e3, "p10_us": p10 * 1e3, "p50_us": p50 * 1e3, "p90_us": p90 * 1e3}
+        if work is not None:
+            r[unit] = work / (mean_ * 1e-3) / scale
+        return r
+
     gemv_b = gemv_bytes(1, N_, K_, G_)
     gemv_gbs = gemv_b / (ms["gemv"] * 1e-3) / 1e9
     gemm_flop = 2.0 * M_GEMM * N_ * K_
     gemm_tf = gemm_flop / (ms["gemm"] * 1e-3) / 1e12
     search_flop = 20 * 2.0 * CAL_SUB * N_ * K_
+    layer_b = sum(gemv_bytes(1, n, k, G_) for _, n, k in synth.LAYER_LINEARS)
     rows = {
-        "pack": {"us": ms["pack"] * 1e3, "GB/s": pack_bytes(N_, K_, G_) / (ms["pack"] * 1e-3) / 1e9},
-        "pack_sym": {"us": ms["pack_sym"] * 1e3, "GB/s": pack_bytes(N_, K_, G_) / (ms["pack_sym"] * 1e-3) / 1e9},
-        "gemv_m1": {"us": ms["gemv"] * 1e3, "GB/s": gemv_gbs},
-        "gemv_m16": {"us": ms["gemv16"] * 1e3,
-                     "GB/s": gemv_bytes(16, N_, K_, G_) / (ms["gemv16"] * 1e-3) / 1e9},
-        "gemm_m4096": {"us": ms["gemm"] * 1e3, "TFLOP/s": gemm_tf},
-        "context_torch_bf16_mm_m4096": {"us": ms["ref_mm"] * 1e3,
-                                        "TFLOP/s": gemm_flop / (ms["ref_mm"] * 1e-3) / 1e12},
-        "pack8": {"us": ms["pack8"] * 1e3,
-                  "GB/s": (2 * N_ * K_ + N_ * K_ + (N_ * K_ // G_) * 5) / (ms["pack8"] * 1e-3) / 1e9},
-        "gemv8_m1": {"us": ms["gemv8"] * 1e3,
-                     "GB/s": (N_ * K_ + (N_ * K_ // G_) * 5 + 2 * K_ + 4 * N_) / (ms["gemv8"] * 1e-3) / 1e9},
-        "gemm8_m4096": {"us": ms["gemm8"] * 1e3, "TFLOP/s": gemm_flop / (ms["gemm8"] * 1e-3) / 1e12},
-        "absmean": {"us": ms["absmean"] * 1e3, "GB/s": 2.0 * CAL_T * K_ / (ms["absmean"] * 1e-3) / 1e9},
-        "awq_search": {"ms": ms["search"], "TFLOP/s": search_flop / (ms["search"] * 1e-3) / 1e12},
-        "fp4_gemv_m1": {"us": ms["fp4_gemv"] * 1e3,
-                        "GB/s": fp4_bytes(1, FP4_N, FP4_K) / (ms["fp4_gemv"] * 1e-3) / 1e9},
-        "fp4_encode": {"us": ms["fp4_encode"] * 1e3,
-                       "GB/s": (4 * FP4_N * FP4_K + FP4_N * FP4_K // 2 + FP4_N * FP4_K // 16)
-                       / (ms["fp4_encode"] * 1e-3) / 1e9},
-        "layer_awq": {"ms": ms["layer_awq"]},
-        "layer_gemv_m1": {"us": ms["layer_gemv"] * 1e3,
-                          "GB/s": sum(gemv_bytes(1, n, k, G_) for _, n, k in synth.LAYER_LINEARS)
-                          / (ms["layer_gemv"] * 1e-3) / 1e9},
-        "fp4_gemm_m2048": {"us": ms["fp4_gemm"] * 1e3,
-                           "TFLOP/s": 2.0 * FP4_M * FP4_N * FP4_K / (ms["fp4_gemm"] * 1e-3) / 1e12},
+        "pack": row("pack", pack_bytes(N_, K_, G_), "GB/s", 1e9),
+        "pack_sym": row("pack_sym", pack_bytes(N_, K_, G_), "GB/s", 1e9),
+        "gemv_m1": row("gemv", gemv_b, "GB/s", 1e9),
+        "gemv_m4": row("gemv_m4", gemv_bytes(4, N_, K_, G_), "GB/s", 1e9),
+        "gemv_m16": row("gemv16", gemv_bytes(16, N_, K_, G_), "GB/s", 1e9),
+        "gemv_m1_g128": row("gemv_m1_g128", gemv_bytes(1, N_, K_, 128), "GB/s", 1e9),
+        "gemv_m4_g128": row("gemv_m4_g128", gemv_bytes(4, N_, K_, 128), "GB/s", 1e9),
+        "gemv_m16_g128": row("gemv_m16_g128", gemv_bytes(16, N_, K_, 128), "GB/s", 1e9),
+        "gemm_m4096": row("gemm", gemm_flop, "TFLOP/s", 1e12),
+        "gemm_m512": row("gemm_m512", 2.0 * 512 * N_ * K_, "TFLOP/s", 1e12),
+        "gemm_m512_q": row("gemm_m512_q", 2.0 * 512 * 2048 * 2048, "TFLOP/s", 1e12),
+        "context_torch_bf16_mm_m4096": row("ref_mm", gemm_flop, "TFLOP/s", 1e12),
+        "pack8": row("pack8", 2 * N_ * K_ + N_ * K_ + (N_ * K_ // G_) * 5, "GB/s", 1e9),
+        "gemv8_m1": row("gemv8", N_ * K_ + (N_ * K_ // G_) * 5 + 2 * K_ + 4 * N_, "GB/s", 1e9),
+        "gemm8_m4096": row("gemm8", gemm_flop, "TFLOP/s", 1e12),
+        "absmean": row("absmean", 2.0 * CAL_T * K_, "GB/s", 1e9),
+        "awq_search": row("search", search_flop, "TFLOP/s", 1e12),
+        "fp4_gemv_m1": row("fp4_gemv_up", fp4_bytes(1, FP4_N, FP4_K), "GB/s", 1e9),
+        "fp4_gemv_m1_k14336": row("fp4_gemv_down", fp4_bytes(1, FP4_K, FP4_N), "GB/s", 1e9),
+        "fp4_gemm_m2048": row("fp4_gemm_up", 2.0 * FP4_M * FP4_N * FP4_K, "TFLOP/s", 1e12),
+        "fp4_gemm_m2048_k14336": row("fp4_gemm_down", 2.0 * FP4_M * FP4_N * FP4_K, "TFLOP/s", 1e12),
+        "fp4_encode": row("fp4_encode", 4 * FP4_N * FP4_K + FP4_N * FP4_K // 2 + FP4_N * FP4_K // 16, "GB/s", 1e9),
+        "layer_awq": row("layer_awq"),
+        "layer_gemv_m1": row("layer_gemv", layer_b, "GB/s", 1e9),
     }
+    for mm in PRE_M:
+        rows[f"prefill_36x7_m{mm}"] = row(f"prefill_m{mm}", pre_flop[mm] / PRE_LAYERS, "TFLOP/s", 1e12)
+        rows[f"prefill_36x7_m{mm}"]["ms_36_layers"] = ms[f"prefill_m{mm}"] * PRE_LAYERS
     rows = {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in rows.items()}
     gemv_src = ["weight_only_bit_group_amd/csrc/w4a16_gemv.hip", "weight_only_bit_group_amd/csrc/aq_device.h"]
     gemm_src = ["weight_only_bit_group_amd/csrc/mfma_gemm.hip", "weight_only_bit_group_amd/csrc/aq_device.h"]
@@ -468,6 +655,20 @@ def main():
                               "traffic": _traffic("w4a16_gemm_m4096", gemm_src, None)}},
         "rows": rows,
     }
+    if not args.no_ceilings:
+        print("[bench] ceilings (empty kernel, streaming read, MFMA loop)", file=sys.stderr, flush=True)
+        c = ceilings(dev)
+        out["ceilings"] = c
+        floor = c["stream_read_gemv_shape_GBs"]
+        out["roofline"].update({"measured_peak": floor, "frac_measured": round(gemv_gbs / floor, 4),
+                                "measured_peak_best_shape": c["stream_read_best_GBs"],
+                                "frac_measured_best_shape": round(gemv_gbs / c["stream_read_best_GBs"], 4),
+                                "measured_by": "pure streaming read of the same bytes at the GEMV's launch "
+                                               "shape, 40 rotating buffers, graph-replayed"})
+        out["gemm"]["roofline"].update({"measured_peak": c["mfma_best_TFLOPs"],
+                                        "frac_measured": round(gemm_tf / c["mfma_best_TFLOPs"], 4),
+                                        "measured_by": "bf16 MFMA-only loop (best of 32x32x16 / 16x16x32 at "
+                                                       "2 and 4 waves per SIMD)"})
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline()

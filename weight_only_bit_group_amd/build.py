@@ -18,6 +18,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libaq.so")
+# the ceiling microbenchmarks the benchmark runs beside the path (not part of the C ABI)
+PROBE_SOURCE = os.path.join(CSRC, "probe", "ceiling.hip")
+PROBE_PATH = os.path.join(HERE, "libaq_probe.so")
 
 HIP_SOURCES = ("quant_pack.hip", "w4a16_gemv.hip", "decode_mfma.hip", "mfma_gemm.hip", "act_absmean.hip",
                "awq_search.hip", "fp4_gemv.hip", "fp4_quant.hip", "w8a16_gemv.hip")
@@ -49,7 +52,7 @@ FILE_FLAGS = {"mfma_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *COMMON_FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *COMMON_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", os.path.join(CSRC, src), "-o", obj]
     proc = subprocess.run(cmd, capture_output=True, text=True)
     if proc.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{proc.stdout}\n{proc.stderr}")
@@ -60,17 +63,25 @@ def build(verbose: bool = True) -> str:
     """Compile every source for gfx950 and link libaq.so; returns the library path."""
     os.makedirs(OBJ_DIR, exist_ok=True)
     sources = list(HIP_SOURCES) + list(CPP_SOURCES)
-    jobs = min(len(sources), max(1, min(8, os.cpu_count() or 1)))
+    jobs = min(len(sources) + 1, max(1, min(8, os.cpu_count() or 1)))
     with ThreadPoolExecutor(max_workers=jobs) as pool:
+        probe_obj = pool.submit(_compile, PROBE_SOURCE)
         objs = list(pool.map(_compile, sources))
+        probe_obj = probe_obj.result()
     tmp = LIB_PATH + ".tmp"
     cmd = [_hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     proc = subprocess.run(cmd, capture_output=True, text=True)
     if proc.returncode != 0:
         raise RuntimeError(f"link failed:\n{proc.stdout}\n{proc.stderr}")
     os.replace(tmp, LIB_PATH)
+    tmp = PROBE_PATH + ".tmp"
+    proc = subprocess.run([_hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", probe_obj, "-o", tmp],
+                          capture_output=True, text=True)
+    if proc.returncode != 0:
+        raise RuntimeError(f"probe link failed:\n{proc.stdout}\n{proc.stderr}")
+    os.replace(tmp, PROBE_PATH)
     if verbose:
-        print(f"built {LIB_PATH}")
+        print(f"built {LIB_PATH} and {PROBE_PATH}")
     return LIB_PATH
 
 
