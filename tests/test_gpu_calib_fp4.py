@@ -157,9 +157,7 @@ def test_fp4_mlp_shapes(n, k):
     x2 = synth.layer_activations_bf16(5, 2048, k)
     step(f"aq_fp4_gemm [{n},{k}] M=2048")
     y = host(B.aq_fp4_gemm(dev_bf16(x2), dc, db, ts))
-    rows = np.unique(np.concatenate([np.arange(0, 2048, 256), np.arange(255, 2048, 256),
-                                     np.random.default_rng(1).choice(2048, 48, replace=False)]))
-    check_close(y[rows], fp4.forward(synth.bf16_bits_to_f32(x2[rows]), c, b, ts), f"fp4 [{n},{k}] M=2048 rows")
+    check_close(y, fp4.forward(synth.bf16_bits_to_f32(x2), c, b, ts), f"fp4 [{n},{k}] M=2048 (all rows)")
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 3, 32), (7, 130, 96), (16, 4100, 64), (17, 33, 160), (300, 257, 512),

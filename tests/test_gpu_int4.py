@@ -186,17 +186,21 @@ def test_gemm_prefill_layer_m512():
         check_close(y, int4.forward(synth.bf16_bits_to_f32(xb), p, s, z, 64), f"gemm {name} M=512")
 
 
-def test_gemm_prefill_gate_m4096_sampled_rows():
-    """The metric shape (M=4096, K=2048, N=11008, g=64) in the benchmarked launch configuration;
-    the oracle checks 192 sampled rows covering every 256-row tile (first, last and interior rows)."""
+def test_gemm_prefill_gate_m4096_all_rows():
+    """The metric shape (M=4096, K=2048, N=11008, g=64) in the benchmarked launch configuration
+    (staged path, persistent grid): every output against the fp64 oracle, and the worst 256-row
+    tile band on its own, so an error confined to one tile of the schedule cannot hide in the
+    whole-matrix mean."""
     p, s, z = _quantized_layer(3, "gate_proj", 64)
     xb = synth.layer_activations_bf16(3, 4096, 2048)
     step("aq_w4a16_gemm gate_proj [11008,2048] g=64 M=4096")
     y = host(B.aq_w4a16_gemm(dev_bf16(xb), dev(p), dev(s), dev(z), 64))
-    rows = np.unique(np.concatenate([np.arange(0, 4096, 256), np.arange(255, 4096, 256),
-                                     np.random.default_rng(0).choice(4096, 160, replace=False)]))
-    ref = int4.forward(synth.bf16_bits_to_f32(xb[rows]), p, s, z, 64)
-    check_close(y[rows], ref, "gemm gate M=4096 (sampled rows)")
+    ref = int4.forward(synth.bf16_bits_to_f32(xb), p, s, z, 64)
+    check_close(y, ref, "gemm gate M=4096 (all rows)")
+    band = np.abs(y - ref).reshape(16, 256, -1).mean(axis=(1, 2))
+    worst = int(band.argmax())
+    check_close(y[256 * worst:256 * (worst + 1)], ref[256 * worst:256 * (worst + 1)],
+                f"gemm gate M=4096 (rows {256 * worst}..{256 * worst + 255}, worst band)")
 
 
 @pytest.mark.parametrize("m,n,k,g", [(1, 5, 64, 32), (64, 128, 128, 64), (300, 200, 192, 64), (257, 129, 384, 128),

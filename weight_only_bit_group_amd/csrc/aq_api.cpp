@@ -73,7 +73,7 @@ bool valid_group(int32_t g) { return g == 32 || g == 64 || g == 128; }
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct SearchLayout {
-  size_t sgrid, e, partial, total;
+  size_t sgrid, rgrid, e, partial, total;
   int nblocks;
 };
 
@@ -88,7 +88,8 @@ SearchLayout search_layout(int64_t T, int64_t N, int64_t K, int32_t n_grid) {
   SearchLayout L;
   L.nblocks = (int)aq::sumsq_gemm_blocks(T, N);
   L.sgrid = 0;
-  L.e = round_up((size_t)n_grid * (size_t)K * sizeof(float), 256);
+  L.rgrid = round_up((size_t)n_grid * (size_t)K * sizeof(float), 256);   // fl32(1 / s), right after s
+  L.e = L.rgrid + round_up((size_t)n_grid * (size_t)K * sizeof(float), 256);
   L.partial = L.e + round_up((size_t)N * (size_t)K * 2 * 2, 256);   // E_hi and E_lo planes
   L.total = L.partial + (size_t)n_grid * (size_t)L.nblocks * sizeof(double);
   return L;
@@ -361,7 +362,8 @@ aq_status aq_awq_search(const uint16_t* X_sub, int64_t T, const float* absmean_h
 
   // Candidate scales, fp64 libm on the host: t = max(m, 1e-8)^alpha,
   // s = fl32(t / sqrt(max t * min t)).
-  std::vector<float> sgrid((size_t)n_grid * (size_t)K);
+  // sgrid then rgrid = fl32(1 / s) (the error matrix multiplies by it), uploaded in one copy
+  std::vector<float> sgrid((size_t)2 * n_grid * (size_t)K);
   std::vector<double> t((size_t)K);
   for (int32_t i = 0; i < n_grid; ++i) {
     const double alpha = (double)i / (double)n_grid;
@@ -374,19 +376,27 @@ aq_status aq_awq_search(const uint16_t* X_sub, int64_t T, const float* absmean_h
       tmin = std::min(tmin, t[k]);
     }
     const double den = std::sqrt(tmax * tmin);
-    for (int64_t k = 0; k < K; ++k) sgrid[(size_t)i * K + k] = (float)(t[k] / den);
+    for (int64_t k = 0; k < K; ++k) {
+      const float sk = (float)(t[k] / den);
+      sgrid[(size_t)i * K + k] = sk;
+      sgrid[((size_t)n_grid + i) * K + k] = (float)(1.0 / (double)sk);
+    }
   }
   char* ws = static_cast<char*>(workspace);
   float* d_sgrid = reinterpret_cast<float*>(ws + L.sgrid);
+  float* d_rgrid = reinterpret_cast<float*>(ws + L.rgrid);
   uint16_t* d_e = reinterpret_cast<uint16_t*>(ws + L.e);
   double* d_partial = reinterpret_cast<double*>(ws + L.partial);
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = hipMemcpyAsync(d_sgrid, sgrid.data(), sgrid.size() * sizeof(float), hipMemcpyHostToDevice, s);
+  hipError_t e = hipMemcpyAsync(d_sgrid, sgrid.data(), (size_t)n_grid * K * sizeof(float), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(d_rgrid, sgrid.data() + (size_t)n_grid * K, (size_t)n_grid * K * sizeof(float),
+                       hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return runtime_status(e, "aq_awq_search: candidate-scale upload");
   const bool bf16 = w_dtype == AQ_BF16;
   for (int32_t i = 0; i < n_grid; ++i) {
-    e = aq::launch_quant_error(W, bf16, d_sgrid + (size_t)i * K, d_e, N, K, group, s);
+    e = aq::launch_quant_error(W, bf16, d_sgrid + (size_t)i * K, d_rgrid + (size_t)i * K, d_e, N, K, group, s);
     if (e != hipSuccess) return runtime_status(e, "aq_awq_search: error-matrix kernel");
     e = aq::launch_sumsq_gemm(X_sub, (int)T, (int)K, d_e, (int)N, d_partial + (size_t)i * L.nblocks, s);
     if (e != hipSuccess) return runtime_status(e, "aq_awq_search: error GEMM");

@@ -11,8 +11,9 @@ namespace aq {
 // sym: the symmetric variant (S = max |v| / 7, codes q + 8, zero point 8)
 hipError_t launch_quant_pack(const void* W, bool w_bf16, const float* chan_scale, uint8_t* packed, float* scales,
                              uint8_t* zeros, int64_t N, int64_t K, int group, bool sym, hipStream_t stream);
-hipError_t launch_quant_error(const void* W, bool w_bf16, const float* chan_scale, uint16_t* E, int64_t N, int64_t K,
-                              int group, hipStream_t stream);
+// E = (q - z) S * chan_rcp - W as two bf16 planes; chan_rcp[k] = fl32(1 / chan_scale[k])
+hipError_t launch_quant_error(const void* W, bool w_bf16, const float* chan_scale, const float* chan_rcp, uint16_t* E,
+                              int64_t N, int64_t K, int group, hipStream_t stream);
 hipError_t launch_w4a16_gemv(const uint16_t* X, int M, int K, const uint8_t* P, const float* S, const uint8_t* Z,
                              int N, int group, float* Y, hipStream_t stream);
 // the same products on the matrix cores, M <= 16 (used by the launch_*_gemv dispatchers

@@ -251,11 +251,14 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(const void* __restrict_
 // AWQ search: the error matrix E = Q(W s) / s - W of one candidate scale, written
 // as two bf16 planes E_hi = bf16(e), E_lo = bf16(e - E_hi) ([N, K] each, E_lo
 // after E_hi).  Same lane mapping and the same (bit-exact) group parameters and
-// codes as the packing kernel; the dequantized value (q - z) * S is divided by
-// s_k and the original weight subtracted in fp32.
+// codes as the packing kernel; the dequantized value (q - z) * S is multiplied by
+// fl32(1 / s_k) (chan_rcp, from the host) and the original weight subtracted in
+// fp32 -- within 1.5 ulp of the fp32 quotient, far below the 16 bits the two bf16
+// planes keep, and without a per-element IEEE division.
 template <int G, bool BF16, int U>
 __global__ __launch_bounds__(256) void quant_error_kernel(const void* __restrict__ W,
                                                           const float* __restrict__ chan_scale,
+                                                          const float* __restrict__ chan_rcp,
                                                           uint16_t* __restrict__ E, int64_t total, int64_t K) {
   constexpr int EPL = 8 * U;
   constexpr int LPG = G / EPL;
@@ -287,9 +290,9 @@ __global__ __launch_bounds__(256) void quant_error_kernel(const void* __restrict
   for (int u = 0; u < U; ++u) {
     uint32_t qc[8];
     group_codes8<15>(v[u], g, qc);
-    const float4* sp = reinterpret_cast<const float4*>(chan_scale + k0 + 8 * u);
-    const float4 a = sp[0], b = sp[1];
-    const float s[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    const float4* rp = reinterpret_cast<const float4*>(chan_rcp + k0 + 8 * u);
+    const float4 a = rp[0], b = rp[1];
+    const float r[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
     // E_hi = bf16(err), E_lo = bf16(err - E_hi), round to nearest even, two values per
     // v_cvt_pk_bf16_f32 (equal to the bitwise rounding for every non-NaN fp32)
     uint32_t hi[4], lo[4];
@@ -300,7 +303,7 @@ __global__ __launch_bounds__(256) void quant_error_kernel(const void* __restrict
       for (int h = 0; h < 2; ++h) {
         const int j = 2 * i + h;
         const float what = (__uint_as_float(qc[j]) - g.kz) * g.S;   // (q - z) S, q - z exact
-        err[h] = what / s[j] - w[u][j];
+        err[h] = what * r[j] - w[u][j];                               // (q - z) S / s_k - w
       }
       const bf16x2 eh = {(__bf16)err[0], (__bf16)err[1]};
       hi[i] = __builtin_bit_cast(uint32_t, eh);
@@ -314,15 +317,17 @@ __global__ __launch_bounds__(256) void quant_error_kernel(const void* __restrict
   }
 }
 
-hipError_t launch_quant_error(const void* W, bool w_bf16, const float* chan_scale, uint16_t* E, int64_t N,
-                              int64_t K, int group, hipStream_t stream) {
+hipError_t launch_quant_error(const void* W, bool w_bf16, const float* chan_scale, const float* chan_rcp, uint16_t* E,
+                              int64_t N, int64_t K, int group, hipStream_t stream) {
   const int64_t total = N * K;
   const dim3 block(256), grid((unsigned)((total / (8 * kErrorU) + 255) / 256));
 #define AQ_QE(GG)                                                                                               \
   if (w_bf16)                                                                                                   \
-    hipLaunchKernelGGL((quant_error_kernel<GG, true, kErrorU>), grid, block, 0, stream, W, chan_scale, E, total, K); \
+    hipLaunchKernelGGL((quant_error_kernel<GG, true, kErrorU>), grid, block, 0, stream, W, chan_scale, chan_rcp, E,    \
+                       total, K);                                                                                 \
   else                                                                                                          \
-    hipLaunchKernelGGL((quant_error_kernel<GG, false, kErrorU>), grid, block, 0, stream, W, chan_scale, E, total, K);
+    hipLaunchKernelGGL((quant_error_kernel<GG, false, kErrorU>), grid, block, 0, stream, W, chan_scale, chan_rcp, E,   \
+                       total, K);
   switch (group) {
     case 32: AQ_QE(32) break;
     case 64: AQ_QE(64) break;
