@@ -113,6 +113,34 @@ def test_search_small(t, n, k, g):
     _check_search(res, awq.search(x, m, w, g, 20), f"search {t}x{n}x{k}")
 
 
+@pytest.mark.parametrize("t,n,k,g", [(520, 200, 256, 32), (300, 130, 128, 64), (1000, 17, 96, 32),
+                                     (700, 300, 320, 64), (129, 257, 128, 128)])
+def test_search_gram_form(t, n, k, g):
+    """T > K: the MSE numerator through H = X^T X (ragged T padded to 64, ragged N and K tiles, the
+    32-wide last stage at K = 96), against the oracle's direct (X E^T)^2."""
+    xb, x, m, wb = _search_case(t + n + k, t, n, k)
+    w = synth.bf16_bits_to_f32(wb)
+    step(f"aq_awq_search Gram T={t} N={n} K={k} g={g}")
+    res = B.aq_awq_search(dev_bf16(xb), m, dev_bf16(wb), g, 20)
+    _check_search(res, awq.search(x, m, w, g, 20), f"search Gram {t}x{n}x{k}")
+
+
+def test_search_gram_form_correlated_channels():
+    """A strong common component across channels (large off-diagonal H): the Gram form keeps the
+    alpha choice and the MSE."""
+    t, n, k, g = 512, 96, 256, 64
+    rng = np.random.default_rng(77)
+    x = synth.bf16_bits_to_f32(synth.calibration_rows_bf16(77, t, k)).astype(np.float64)
+    x += np.outer(rng.standard_normal(t) * 30.0, np.exp(1.5 * rng.standard_normal(k)))
+    xb = synth.f32_to_bf16_bits(x.astype(np.float32))
+    x = synth.bf16_bits_to_f32(xb)
+    m = stats.absmean(x)
+    wb = synth.f32_to_bf16_bits(synth.weight_f32(rng, n, k, 0.02, outlier_frac=0.001))
+    step(f"aq_awq_search Gram correlated T={t} N={n} K={k}")
+    res = B.aq_awq_search(dev_bf16(xb), m, dev_bf16(wb), g, 20)
+    _check_search(res, awq.search(x, m, synth.bf16_bits_to_f32(wb), g, 20), "search Gram correlated")
+
+
 def test_search_alpha_zero_only_equals_plain_pack():
     """n_grid = 1 is the alpha = 0 candidate only: s = 1 and the pack equals plain min-max."""
     xb, x, m, wb = _search_case(5, 128, 64, 256)

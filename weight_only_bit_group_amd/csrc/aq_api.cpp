@@ -5,12 +5,15 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <string>
+#include <system_error>
+#include <thread>
 #include <vector>
 
 #include "../../include/aq.h"
@@ -73,26 +76,83 @@ bool valid_group(int32_t g) { return g == 32 || g == 64 || g == 128; }
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct SearchLayout {
-  size_t sgrid, rgrid, e, partial, total;
-  int nblocks;
+  size_t sgrid, rgrid, e, partial, xt, h, hp, total;
+  int64_t tp;    // Gram form: token count padded to the GEMM's 64-wide stages
+  int nblocks;   // error-GEMM tiles (one fp64 partial each, per candidate)
+  bool gram;
 };
 
-// The search's error GEMM takes T as its M: T, N and K below 2^22 keep its 32-bit
-// load / store offsets and its tile count (below 2^29) in range.
+// The MSE numerator sum (X E^T)^2 either directly (T K N multiply-adds per candidate)
+// or as sum_n e_n H e_n^T with H = X^T X formed once (K K N per candidate): the Gram
+// form when T > K, its padded token count within the GEMM limit.
+bool use_gram(int64_t T, int64_t K) { return T > K && (int64_t)round_up((size_t)T, 64) < kGemmDimLimit; }
+
+// The error GEMM takes T (direct) or N (Gram) as its M: T, N and K below 2^22 keep its
+// 32-bit load / store offsets and its tile count (below 2^29) in range.
 bool search_dims_ok(int64_t T, int64_t N, int64_t K) {
-  return T > 0 && N > 0 && K > 0 && T < kGemmDimLimit && N < kGemmDimLimit && K < kGemmDimLimit &&
-         aq::sumsq_gemm_blocks(T, N) < (int64_t(1) << 30);
+  if (!(T > 0 && N > 0 && K > 0 && T < kGemmDimLimit && N < kGemmDimLimit && K < kGemmDimLimit)) return false;
+  return use_gram(T, K) ? aq::sumsq_gemm_blocks(N, K) < (int64_t(1) << 30)
+                        : aq::sumsq_gemm_blocks(T, N) < (int64_t(1) << 30);
 }
 
 SearchLayout search_layout(int64_t T, int64_t N, int64_t K, int32_t n_grid) {
   SearchLayout L;
-  L.nblocks = (int)aq::sumsq_gemm_blocks(T, N);
+  L.gram = use_gram(T, K);
+  L.tp = (int64_t)round_up((size_t)T, 64);
+  L.nblocks = (int)(L.gram ? aq::sumsq_gemm_blocks(N, K) : aq::sumsq_gemm_blocks(T, N));
   L.sgrid = 0;
   L.rgrid = round_up((size_t)n_grid * (size_t)K * sizeof(float), 256);   // fl32(1 / s), right after s
   L.e = L.rgrid + round_up((size_t)n_grid * (size_t)K * sizeof(float), 256);
   L.partial = L.e + round_up((size_t)N * (size_t)K * 2 * 2, 256);   // E_hi and E_lo planes
-  L.total = L.partial + (size_t)n_grid * (size_t)L.nblocks * sizeof(double);
+  L.xt = round_up(L.partial + (size_t)n_grid * (size_t)L.nblocks * sizeof(double), 256);
+  if (L.gram) {
+    L.h = L.xt + round_up((size_t)K * (size_t)L.tp * 2, 256);        // X^T, bf16 [K, tp]
+    L.hp = L.h + round_up((size_t)K * (size_t)K * sizeof(float), 256);  // H fp32 [K, K]
+    L.total = L.hp + (size_t)K * (size_t)K * 2 * 2;                  // H_hi, H_lo planes
+  } else {
+    L.h = L.hp = L.total = L.xt;
+  }
   return L;
+}
+
+// Candidate scales of alphas i = 0 .. n_grid - 1 (alpha = i / n_grid), fp64 libm:
+// t = max(m, 1e-8)^alpha, s = fl32(t / sqrt(max t * min t)); out[i K + k] = s and
+// out[(n_grid + i) K + k] = fl32(1 / s).  The alphas are shared among up to eight
+// threads (each value comes from the same libm calls whichever thread computes it).
+void candidate_grid(const float* absmean, int64_t K, int32_t n_grid, float* out) {
+  std::atomic<int32_t> next{0};
+  auto work = [&]() {
+    std::vector<double> t((size_t)K);
+    for (int32_t i = next.fetch_add(1); i < n_grid; i = next.fetch_add(1)) {
+      const double alpha = (double)i / (double)n_grid;
+      double tmax = -INFINITY, tmin = INFINITY;
+      for (int64_t k = 0; k < K; ++k) {
+        double m = (double)absmean[k];
+        if (m < 1e-8) m = 1e-8;
+        t[k] = std::pow(m, alpha);
+        tmax = std::max(tmax, t[k]);
+        tmin = std::min(tmin, t[k]);
+      }
+      const double den = std::sqrt(tmax * tmin);
+      for (int64_t k = 0; k < K; ++k) {
+        const float sk = (float)(t[k] / den);
+        out[(size_t)i * K + k] = sk;
+        out[((size_t)n_grid + i) * K + k] = (float)(1.0 / (double)sk);
+      }
+    }
+  };
+  const unsigned hw = std::max(1u, std::thread::hardware_concurrency());
+  const int nth = (int)std::min<unsigned>({8u, hw, (unsigned)n_grid});
+  std::vector<std::thread> pool;
+  for (int j = 1; j < nth; ++j) {
+    try {
+      pool.emplace_back(work);
+    } catch (const std::system_error&) {
+      break;   // fewer helpers: the calling thread takes the remaining alphas
+    }
+  }
+  work();
+  for (auto& th : pool) th.join();
 }
 
 }  // namespace
@@ -360,35 +420,27 @@ aq_status aq_awq_search(const uint16_t* X_sub, int64_t T, const float* absmean_h
                "aq_awq_search: absmean_host[%lld] must be finite and >= 0", (long long)k);
   if (fault_injected()) return fail(AQ_ERUNTIME, "aq_awq_search: injected launch failure");
 
-  // Candidate scales, fp64 libm on the host: t = max(m, 1e-8)^alpha,
-  // s = fl32(t / sqrt(max t * min t)).
-  // sgrid then rgrid = fl32(1 / s) (the error matrix multiplies by it), uploaded in one copy
-  std::vector<float> sgrid((size_t)2 * n_grid * (size_t)K);
-  std::vector<double> t((size_t)K);
-  for (int32_t i = 0; i < n_grid; ++i) {
-    const double alpha = (double)i / (double)n_grid;
-    double tmax = -INFINITY, tmin = INFINITY;
-    for (int64_t k = 0; k < K; ++k) {
-      double m = (double)absmean_host[k];
-      if (m < 1e-8) m = 1e-8;
-      t[k] = std::pow(m, alpha);
-      tmax = std::max(tmax, t[k]);
-      tmin = std::min(tmin, t[k]);
-    }
-    const double den = std::sqrt(tmax * tmin);
-    for (int64_t k = 0; k < K; ++k) {
-      const float sk = (float)(t[k] / den);
-      sgrid[(size_t)i * K + k] = sk;
-      sgrid[((size_t)n_grid + i) * K + k] = (float)(1.0 / (double)sk);
-    }
-  }
   char* ws = static_cast<char*>(workspace);
   float* d_sgrid = reinterpret_cast<float*>(ws + L.sgrid);
   float* d_rgrid = reinterpret_cast<float*>(ws + L.rgrid);
   uint16_t* d_e = reinterpret_cast<uint16_t*>(ws + L.e);
   double* d_partial = reinterpret_cast<double*>(ws + L.partial);
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = hipMemcpyAsync(d_sgrid, sgrid.data(), (size_t)n_grid * K * sizeof(float), hipMemcpyHostToDevice, s);
+  hipError_t e = hipSuccess;
+  uint16_t* d_hp = reinterpret_cast<uint16_t*>(ws + L.hp);
+  if (L.gram) {
+    // H = X^T X and its two bf16 planes, queued before the host work below
+    uint16_t* d_xt = reinterpret_cast<uint16_t*>(ws + L.xt);
+    float* d_h = reinterpret_cast<float*>(ws + L.h);
+    e = aq::launch_transpose_pad(X_sub, T, K, L.tp, d_xt, s);
+    if (e == hipSuccess) e = aq::launch_bf16_gemm(d_xt, (int)K, (int)L.tp, d_xt, (int)K, d_h, s);
+    if (e == hipSuccess) e = aq::launch_split_planes(d_h, K * K, d_hp, s);
+    if (e != hipSuccess) return runtime_status(e, "aq_awq_search: Gram matrix");
+  }
+  // candidate scales s (then fl32(1 / s), which the error matrix multiplies by), one copy
+  std::vector<float> sgrid((size_t)2 * n_grid * (size_t)K);
+  candidate_grid(absmean_host, K, n_grid, sgrid.data());
+  e = hipMemcpyAsync(d_sgrid, sgrid.data(), (size_t)n_grid * K * sizeof(float), hipMemcpyHostToDevice, s);
   if (e == hipSuccess)
     e = hipMemcpyAsync(d_rgrid, sgrid.data() + (size_t)n_grid * K, (size_t)n_grid * K * sizeof(float),
                        hipMemcpyHostToDevice, s);
@@ -398,7 +450,9 @@ aq_status aq_awq_search(const uint16_t* X_sub, int64_t T, const float* absmean_h
   for (int32_t i = 0; i < n_grid; ++i) {
     e = aq::launch_quant_error(W, bf16, d_sgrid + (size_t)i * K, d_rgrid + (size_t)i * K, d_e, N, K, group, s);
     if (e != hipSuccess) return runtime_status(e, "aq_awq_search: error-matrix kernel");
-    e = aq::launch_sumsq_gemm(X_sub, (int)T, (int)K, d_e, (int)N, d_partial + (size_t)i * L.nblocks, s);
+    double* part = d_partial + (size_t)i * L.nblocks;
+    e = L.gram ? aq::launch_gram_gemm(d_e, (int)N, (int)K, d_hp, part, s)
+               : aq::launch_sumsq_gemm(X_sub, (int)T, (int)K, d_e, (int)N, part, s);
     if (e != hipSuccess) return runtime_status(e, "aq_awq_search: error GEMM");
   }
   e = aq::launch_search_select(d_partial, L.nblocks, n_grid, (double)T * (double)N, d_sgrid, (int)K, mse, best,

@@ -55,6 +55,16 @@ hipError_t launch_fp4_quantize(const void* W, bool w_bf16, int64_t N, int64_t K,
 int64_t sumsq_gemm_blocks(int64_t M, int64_t N);
 hipError_t launch_sumsq_gemm(const uint16_t* X, int M, int K, const uint16_t* E, int N, double* partial,
                              hipStream_t stream);
+// Gram form of the search's error GEMM: E = the [2][M, K] error planes, H = the [2][K, K]
+// bf16 planes of X^T X; partial[sumsq_gemm_blocks(M, K)] gets each tile's sum of
+// (E_hi H)[m, j] (E_hi + 2 E_lo)[m, j]
+hipError_t launch_gram_gemm(const uint16_t* E, int M, int K, const uint16_t* H, double* partial, hipStream_t stream);
+// Y[M, N] = A[M, K] Bm[N, K]^T, bf16 operands (K contiguous, K % 32 == 0), fp32 output
+hipError_t launch_bf16_gemm(const uint16_t* A, int M, int K, const uint16_t* Bm, int N, float* Y, hipStream_t stream);
+// Xt[K, Tp] = X[T, K]^T with rows T .. Tp - 1 of X taken as zero (Tp % 64 == 0, K % 8 == 0)
+hipError_t launch_transpose_pad(const uint16_t* X, int64_t T, int64_t K, int64_t Tp, uint16_t* Xt, hipStream_t stream);
+// H[n] (fp32) -> planes[0][n] = bf16(H), planes[1][n] = bf16(H - planes[0]), n < count (count % 4 == 0)
+hipError_t launch_split_planes(const float* H, int64_t count, uint16_t* planes, hipStream_t stream);
 int absmean_row_slices(int64_t T, int64_t K);
 // the allocation-free entry point's scratch: its size, and its device address on the
 // current device (looked up once per device)

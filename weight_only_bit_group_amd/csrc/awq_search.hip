@@ -69,6 +69,78 @@ hipError_t launch_fold_norm(const void* w, bool w_bf16, const float* s, int K, f
   return hipGetLastError();
 }
 
+// ---- Gram form of the search's MSE --------------------------------------------
+// For T > K the numerator sum_{t,n} (X E^T)[t, n]^2 equals sum_n e_n H e_n^T with the
+// K x K Gram matrix H = X^T X, formed once per search: K^2 N multiply-adds per
+// candidate instead of T K N.  H comes from the bf16 GEMM on X^T (its products are
+// exact, its sums fp32), split into two bf16 planes (about 16 significant bits) for
+// the per-candidate GEMM.
+
+// Xt[K, Tp] = X[T, K]^T, rows t >= T of X read as zero.  A block moves one 64 x 64
+// tile through LDS: 16-byte loads along k, 16-byte stores along t.
+__global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __restrict__ X, int64_t T, int64_t K,
+                                                            int64_t Tp, uint16_t* __restrict__ Xt) {
+  __shared__ uint16_t tile[64][72];
+  const int64_t k0 = (int64_t)blockIdx.x * 64, t0 = (int64_t)blockIdx.y * 64;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int u = threadIdx.x + 256 * h, r = u >> 3, c = u & 7;   // tile row r (t), unit c (8 k)
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (t0 + r < T && k0 + 8 * c < K) v = *reinterpret_cast<const u32x4*>(X + (t0 + r) * K + k0 + 8 * c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      tile[r][8 * c + 2 * i] = (uint16_t)(v[i] & 0xFFFFu);
+      tile[r][8 * c + 2 * i + 1] = (uint16_t)(v[i] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int u = threadIdx.x + 256 * h, r = u >> 3, c = u & 7;   // output row r (k), unit c (8 t)
+    if (k0 + r >= K) continue;
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      v[i] = (uint32_t)tile[8 * c + 2 * i][r] | ((uint32_t)tile[8 * c + 2 * i + 1][r] << 16);
+    *reinterpret_cast<u32x4*>(Xt + (k0 + r) * Tp + t0 + 8 * c) = v;
+  }
+}
+
+hipError_t launch_transpose_pad(const uint16_t* X, int64_t T, int64_t K, int64_t Tp, uint16_t* Xt,
+                                hipStream_t stream) {
+  if (Tp % 64 || K % 8 || Tp < T) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((K + 63) / 64), (unsigned)(Tp / 64));
+  hipLaunchKernelGGL(transpose_pad_kernel, grid, dim3(256), 0, stream, X, T, K, Tp, Xt);
+  return hipGetLastError();
+}
+
+// planes[0] = bf16(H) and planes[1] = bf16(H - planes[0]), both round to nearest even;
+// four values per thread.
+__global__ __launch_bounds__(256) void split_planes_kernel(const float* __restrict__ H, int64_t count,
+                                                           uint16_t* __restrict__ planes) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= count) return;
+  const f32x4 h = *reinterpret_cast<const f32x4*>(H + i);
+  uint32_t hi[2], lo[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const bf16x2 a = {(__bf16)h[2 * j], (__bf16)h[2 * j + 1]};
+    hi[j] = __builtin_bit_cast(uint32_t, a);
+    const bf16x2 b = {(__bf16)(h[2 * j] - bf16_lo(hi[j])), (__bf16)(h[2 * j + 1] - bf16_hi(hi[j]))};
+    lo[j] = __builtin_bit_cast(uint32_t, b);
+  }
+  *reinterpret_cast<uint2*>(planes + i) = uint2{hi[0], hi[1]};
+  *reinterpret_cast<uint2*>(planes + count + i) = uint2{lo[0], lo[1]};
+}
+
+hipError_t launch_split_planes(const float* H, int64_t count, uint16_t* planes, hipStream_t stream) {
+  if (count % 4) return hipErrorInvalidValue;
+  const int64_t threads = count / 4;
+  hipLaunchKernelGGL(split_planes_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, H, count,
+                     planes);
+  return hipGetLastError();
+}
+
 hipError_t launch_search_select(const double* partial, int nblocks, int n_grid, double count, const float* sgrid,
                                 int K, double* mse, int32_t* best, float* best_scale, hipStream_t stream) {
   hipLaunchKernelGGL(search_mse_kernel, dim3(n_grid), dim3(256), 0, stream, partial, nblocks, count, mse);

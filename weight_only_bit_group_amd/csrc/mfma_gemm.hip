@@ -20,6 +20,10 @@
 //         bits in all); both planes are multiplied into the same accumulator and
 //         the epilogue returns, per block, the fp64 sum of squares of its outputs
 //         (the MSE numerator).
+//   GRAM  the same two-plane pipeline for the search's Gram form: A = E_hi, B = the
+//         two bf16 planes of H = X^T X, so the tile holds F = E_hi H; the epilogue
+//         returns the fp64 sum of F * (E_hi + 2 E_lo) over the tile, read from the
+//         error planes at each output's (row, column).
 //
 // Block: 2 * WGM waves (WGM = 4 for large M: 512 threads, a 256 x 128 tile), the
 // waves in a WGM x 2 grid of 64 x 64 wave tiles, each four 32x32 output blocks of
@@ -77,8 +81,8 @@ namespace aq {
 
 // B operand kinds: INT4 / FP4 codes dequantized in the kernel; INT4S / FP4S the same
 // weights dequantized beforehand into a bf16 staging matrix (loaded like the SPLIT
-// planes); SPLIT the search's two bf16 planes.
-enum BKind { B_INT4 = 0, B_SPLIT = 1, B_FP4 = 2, B_INT4S = 3, B_FP4S = 4 };
+// planes); SPLIT the search's two bf16 planes; GRAM the search's Gram-form product.
+enum BKind { B_INT4 = 0, B_SPLIT = 1, B_FP4 = 2, B_INT4S = 3, B_FP4S = 4, B_GRAM = 5 };
 
 struct GemmArgs {
   const uint16_t* X;
@@ -90,13 +94,15 @@ struct GemmArgs {
   // SPLIT: the two bf16 planes of E; INT4S / FP4S: the staged bf16 weights in B
   const uint16_t* B;
   const uint16_t* B2;
+  // GRAM: the E_lo plane (E_hi is X), [M, N] with N contiguous
+  const uint16_t* Elo;
   // FP4
   const uint8_t* codes;
   const uint8_t* bscale;
   float ts;
   // outputs
   float* Y;           // [M, N] fp32 (INT4, FP4)
-  double* partial;    // [number of blocks] fp64 sums of squares (SPLIT)
+  double* partial;    // [number of blocks] fp64 sums of squares (SPLIT) or weighted sums (GRAM)
 };
 
 namespace {
@@ -114,7 +120,8 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_kernel(GemmArgs a) {
   constexpr int NW = 2 * WGM, NT = 64 * NW;
   constexpr int BM = 64 * WGM;
   constexpr bool DEQ = BK == B_INT4 || BK == B_FP4;        // codes dequantized here
-  constexpr bool SPLIT = BK == B_SPLIT;
+  constexpr bool SPLIT = BK == B_SPLIT || BK == B_GRAM;    // two B planes into one accumulator
+  constexpr bool GRAM = BK == B_GRAM;
   constexpr bool STAGED = BK == B_INT4S || BK == B_FP4S;   // bf16 weights from global memory
   constexpr bool RESCALE = BK == B_INT4 || BK == B_INT4S;  // per-group steps applied to partials
   constexpr bool TSCALE = BK == B_FP4 || BK == B_FP4S;     // fp32 tensor scale on the output
@@ -542,7 +549,8 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_kernel(GemmArgs a) {
 
   // ---- tile epilogue ----------------------------------------------------------------
   // Applies the last carried group partials, writes the tile's outputs (SPLIT: its fp64
-  // sum of squares) and clears the accumulators for the block's next tile.
+  // sum of squares; GRAM: its weighted sum) and clears the accumulators for the block's
+  // next tile.
   // Result i of block (mi, ni): row 8 (i / 4) + 4 lh + (i % 4), column l32.
   __shared__ double wsum[NW];
   auto finish_tile = [&](const TileXY& tt) {
@@ -559,18 +567,57 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_kernel(GemmArgs a) {
     asm volatile("" : "+v"(lrow), "+v"(lcol));
     if constexpr (SPLIT) {
       double ss = 0.0;
+      if constexpr (GRAM) {
+        // weight of output (m, n): E_hi[m, n] + 2 E_lo[m, n], exact in fp32 (E_lo is at
+        // most half an ulp of E_hi).  Outputs past the matrix load the tile's first
+        // element and weigh 0, so every load is in bounds and unconditional: the loads
+        // of an m-block (two output blocks, both planes) are all issued before the
+        // first is used.
+        const uint16_t* eh = a.X + (int64_t)m0 * N + n0;
+        const uint16_t* el = a.Elo + (int64_t)m0 * N + n0;
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
+        for (int mi = 0; mi < 2; ++mi) {
+          uint32_t off[2][16];
+          bool in[2][16];
+          uint16_t hv[2][16], lv[2][16];
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          const int n = n0 + lcol + 32 * ni;
+          for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int m = m0 + lrow + 32 * mi + 8 * (v >> 2) + (v & 3);
-            const double d = (double)acc[mi][ni][v];
-            if (m < M && n < N) ss = __builtin_fma(d, d, ss);
-          }
+            for (int v = 0; v < 16; ++v) {
+              const int cn = lcol + 32 * ni;
+              const int rm = lrow + 32 * mi + 8 * (v >> 2) + (v & 3);
+              in[ni][v] = m0 + rm < M && n0 + cn < N;
+              off[ni][v] = in[ni][v] ? (uint32_t)rm * (uint32_t)N + (uint32_t)cn : 0u;
+            }
+#pragma unroll
+          for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              hv[ni][v] = eh[off[ni][v]];
+              lv[ni][v] = el[off[ni][v]];
+            }
+#pragma unroll
+          for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const float w = bf16_to_f32(hv[ni][v]) + 2.0f * bf16_to_f32(lv[ni][v]);
+              ss = __builtin_fma((double)acc[mi][ni][v], (double)(in[ni][v] ? w : 0.0f), ss);
+            }
         }
+      } else {
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < 2; ++ni) {
+            const int n = n0 + lcol + 32 * ni;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int m = m0 + lrow + 32 * mi + 8 * (v >> 2) + (v & 3);
+              const double d = (double)acc[mi][ni][v];
+              if (m < M && n < N) ss = __builtin_fma(d, d, ss);
+            }
+          }
+      }
       ss = wave_sum(ss);
       if (lane == 0) wsum[wid] = ss;
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the LDS write is done (loads stay in flight)
@@ -916,6 +963,22 @@ hipError_t launch_sumsq_gemm(const uint16_t* X, int M, int K, const uint16_t* E,
   GemmArgs a = {};
   a.X = X; a.M = M; a.N = N; a.K = K; a.B = E; a.B2 = E + (size_t)N * K; a.partial = partial;
   return launch_tiles<B_SPLIT, 64>(a, stream);
+}
+
+hipError_t launch_gram_gemm(const uint16_t* E, int M, int K, const uint16_t* H, double* partial,
+                            hipStream_t stream) {
+  GemmArgs a = {};
+  a.X = E; a.Elo = E + (size_t)M * K; a.M = M; a.N = K; a.K = K;
+  a.B = H; a.B2 = H + (size_t)K * K; a.partial = partial;
+  return launch_tiles<B_GRAM, 64>(a, stream);
+}
+
+hipError_t launch_bf16_gemm(const uint16_t* A, int M, int K, const uint16_t* Bm, int N, float* Y,
+                            hipStream_t stream) {
+  // the staged-weight kind with a unit output scale (multiplying by 1 is exact)
+  GemmArgs a = {};
+  a.X = A; a.M = M; a.N = N; a.K = K; a.B = Bm; a.ts = 1.0f; a.Y = Y;
+  return launch_tiles<B_FP4S, 64>(a, stream);
 }
 
 }  // namespace aq
