@@ -595,7 +595,9 @@ def main():
     gemv_gbs = gemv_b / (ms["gemv"] * 1e-3) / 1e9
     gemm_flop = 2.0 * M_GEMM * N_ * K_
     gemm_tf = gemm_flop / (ms["gemm"] * 1e-3) / 1e12
-    search_flop = 20 * 2.0 * CAL_SUB * N_ * K_
+    # the search scores each candidate through the Gram matrix (T > K): K^2 N multiply-adds per
+    # candidate plus T K^2 once for H = X^T X (the direct form would be T K N per candidate)
+    search_flop = 20 * 2.0 * N_ * K_ * K_ + 2.0 * CAL_SUB * K_ * K_
     layer_b = sum(gemv_bytes(1, n, k, G_) for _, n, k in synth.LAYER_LINEARS)
     rows = {
         "pack": row("pack", pack_bytes(N_, K_, G_), "GB/s", 1e9),
@@ -614,7 +616,8 @@ def main():
         "gemv8_m1": row("gemv8", N_ * K_ + (N_ * K_ // G_) * 5 + 2 * K_ + 4 * N_, "GB/s", 1e9),
         "gemm8_m4096": row("gemm8", gemm_flop, "TFLOP/s", 1e12),
         "absmean": row("absmean", 2.0 * CAL_T * K_, "GB/s", 1e9),
-        "awq_search": row("search", search_flop, "TFLOP/s", 1e12),
+        "awq_search": dict(row("search", search_flop, "TFLOP/s", 1e12), form="gram",
+                           direct_form_equiv_TFLOP_s=20 * 2.0 * CAL_SUB * N_ * K_ / (ms["search"] * 1e-3) / 1e12),
         "fp4_gemv_m1": row("fp4_gemv_up", fp4_bytes(1, FP4_N, FP4_K), "GB/s", 1e9),
         "fp4_gemv_m1_k14336": row("fp4_gemv_down", fp4_bytes(1, FP4_K, FP4_N), "GB/s", 1e9),
         "fp4_gemm_m2048": row("fp4_gemm_up", 2.0 * FP4_M * FP4_N * FP4_K, "TFLOP/s", 1e12),
@@ -626,7 +629,7 @@ def main():
     for mm in PRE_M:
         rows[f"prefill_36x7_m{mm}"] = row(f"prefill_m{mm}", pre_flop[mm] / PRE_LAYERS, "TFLOP/s", 1e12)
         rows[f"prefill_36x7_m{mm}"]["ms_36_layers"] = ms[f"prefill_m{mm}"] * PRE_LAYERS
-    rows = {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in rows.items()}
+    rows = {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()} for k, v in rows.items()}
     gemv_src = ["weight_only_bit_group_amd/csrc/w4a16_gemv.hip", "weight_only_bit_group_amd/csrc/aq_device.h"]
     gemm_src = ["weight_only_bit_group_amd/csrc/mfma_gemm.hip", "weight_only_bit_group_amd/csrc/aq_device.h"]
     out = {

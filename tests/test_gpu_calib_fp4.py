@@ -192,7 +192,8 @@ def test_fp4_mlp_shapes(n, k):
                                    (1, 8195, 4096), (2, 4099, 160), (8, 8195, 4096), (12, 33, 2112), (4, 130, 64),
                                    (6, 70, 8256), (16, 9000, 2048), (3, 1001, 4160),
                                    (1, 4099, 160), (1, 130, 4160), (1, 70, 14368), (5, 40, 8192),
-                                   (11, 17, 4096)])
+                                   (11, 17, 4096), (13, 12400, 512), (12, 8192, 2048), (16, 8193, 64),
+                                   (4, 8200, 2048)])
 def test_fp4_ragged(m, n, k):
     rng = np.random.default_rng(m + n + k)
     c, b, ts = fp4.encode((rng.standard_normal((n, k)) * 0.02).astype(np.float32))

@@ -140,11 +140,13 @@ def _exact_case(rng, m, n, k, g):
 @pytest.mark.parametrize("m,n,k,g", [(1, 64, 256, 64), (5, 33, 128, 32), (16, 130, 1024, 128), (1, 8195, 256, 64),
                                      (1, 8197, 2048, 32), (8, 40, 4160, 64), (9, 33, 2080, 32), (12, 17, 4224, 128),
                                      (16, 300, 32, 32), (7, 8195, 1024, 128), (16, 70, 8256, 32),
-                                     (8, 70, 8192, 128), (5, 33, 4096, 64)])
+                                     (8, 70, 8192, 128), (5, 33, 4096, 64), (12, 12500, 512, 64),
+                                     (9, 8300, 2048, 128), (8, 8192, 2048, 32), (5, 8250, 2048, 64)])
 def test_gemv_exact_integer_case(m, n, k, g):
     """(N >= 8192 at M = 1 takes the four-rows-per-wave launch, here with a ragged last wave;
-    M >= 5 takes the matrix-core kernel, here with 4, 8 and 16 waves per
-    block, over several 4096-k chunks, a ragged tail chunk and a single group.)"""
+    M >= 5 takes the matrix-core kernels: the chunked one with 4, 8 and 16 waves per block,
+    over several 4096-k chunks, a ragged tail chunk and a single group; from M = 8 at
+    N >= 8192 and K <= 2048 the LDS-staged one, with 48 and 64 rows per block.)"""
     xb, x, p, s, z = _exact_case(np.random.default_rng(m + n + k), m, n, k, g)
     step(f"aq_w4a16_gemv exact-integer M={m} N={n} K={k} g={g}")
     y = host(B.aq_w4a16_gemv(dev_bf16(xb), dev(p), dev(s), dev(z), g))
@@ -156,7 +158,8 @@ def test_gemv_exact_integer_case(m, n, k, g):
                                      (1, 8194, 512, 128), (1, 8199, 11008, 64), (8, 8197, 2048, 64),
                                      (13, 1001, 11008, 64), (10, 3, 6144, 128), (5, 8203, 1024, 64),
                                      (6, 8192, 256, 32), (2, 1003, 11008, 64), (3, 70, 8192, 32),
-                                     (2, 8195, 2048, 64), (2, 9000, 1024, 128)])
+                                     (2, 8195, 2048, 64), (2, 9000, 1024, 128), (16, 13001, 1024, 32),
+                                     (11, 8191, 2048, 64)])
 def test_gemv_ragged_shapes(m, n, k, g):
     rng = np.random.default_rng(n)
     w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)

@@ -52,6 +52,8 @@ size_t fp4_quantize_workspace_bytes(int64_t N, int64_t K);
 // ts: one fp32 on the device (written); partial: fp4_quantize_workspace_bytes of device memory
 hipError_t launch_fp4_quantize(const void* W, bool w_bf16, int64_t N, int64_t K, uint8_t* codes, uint8_t* bscale,
                                float* ts, float* partial, hipStream_t stream);
+// compute units of the current device (cached per device)
+int device_cu_count();
 int64_t sumsq_gemm_blocks(int64_t M, int64_t N);
 hipError_t launch_sumsq_gemm(const uint16_t* X, int M, int K, const uint16_t* E, int N, double* partial,
                              hipStream_t stream);

@@ -71,6 +71,7 @@
 // 8 (i / 4) + 4 (lane / 32) + (i % 4), so they share one weight row n and need
 // one S per block per group.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "aq_device.h"
@@ -78,6 +79,19 @@
 #include "gemm_lds.h"
 
 namespace aq {
+
+// Compute units of the current device (queried once per device, 256 if the query fails).
+int device_cu_count() {
+  static std::atomic<int> cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cached[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
 
 // B operand kinds: INT4 / FP4 codes dequantized in the kernel; INT4S / FP4S the same
 // weights dequantized beforehand into a bf16 staging matrix (loaded like the SPLIT
@@ -855,26 +869,13 @@ int tiles(int M, int N, int bm) { return ((M + bm - 1) / bm) * ((N + BN - 1) / B
 // 256-row tiles (8 waves) once M fills them; 128-row tiles (4 waves) for small M.
 constexpr int kWideM = 192;
 
-// Compute units of the current device (queried once per device).
-int cu_count() {
-  static int cached[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] <= 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-    cached[dev] = v;
-  }
-  return cached[dev];
-}
-
 // Grid: one block per CU looping over the tiles (persistent) when every tile has at
 // least four full stages, else one block per tile.
 template <int BK, int G, bool TAIL>
 hipError_t launch_tail(const GemmArgs& a, hipStream_t stream) {
   const bool wide = a.M > kWideM;
   const int nt = tiles(a.M, a.N, wide ? 256 : 128);
-  const int grid = (!TAIL && a.K / KS >= 4) ? min(nt, cu_count()) : nt;
+  const int grid = (!TAIL && a.K / KS >= 4) ? min(nt, device_cu_count()) : nt;
   if (wide) {
     hipLaunchKernelGGL((gemm_kernel<BK, G, TAIL, 4>), dim3(grid), dim3(512), 0, stream, a);
   } else {
