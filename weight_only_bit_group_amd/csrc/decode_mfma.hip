@@ -82,25 +82,38 @@ __device__ __forceinline__ void lds_dwords(const uint8_t* p, uint32_t (&w)[NW]) 
   }
 }
 
+// INT4: the bf16 pair (-(128 + z), -(128 + z)) of a zero point (exact: 128 + z <= 143).
+__device__ __forceinline__ uint32_t offset_pair(float zf) {
+  const uint32_t zb16 = __float_as_uint(-(128.0f + zf)) >> 16;
+  return zb16 | (zb16 << 16);
+}
+
 // The products of one group for a lane: wc = its code dwords, xk = its activation
 // operands per 32-k MFMA step (INT4: already in (k, k + 4) pair order), sc / zf = the
-// group step and zero point (FP4: the lane's block scale).  Returns the unscaled
-// partial (INT4 / INT8) or the block-scaled one (FP4).
+// group step and zero point (FP4: the lane's block scale), zp = offset_pair(zf) (INT4).
+// Returns the unscaled partial (INT4 / INT8) or the block-scaled one (FP4).
 template <int WF, int G>
-__device__ __forceinline__ f32x4 group_product(const uint32_t* wc, const u32x4* xk, float sc, float zf) {
+__device__ __forceinline__ f32x4 group_product(const uint32_t* wc, const u32x4* xk, float sc, float zf, uint32_t zp) {
   constexpr int NJ = G / 32;
   f32x4 tmp = {0.0f, 0.0f, 0.0f, 0.0f};
   // INT4: the bf16 pairs (128 + q_s, 128 + q_{s+4}) straight from the code dword, the
   // activations in the same (k, k + 4) pair order, and a second MFMA with the constant
   // -(128 + z) subtracting the offset (exact integers, see the header)
-  const uint32_t zb16 = __float_as_uint(-(128.0f + zf)) >> 16;
-  const u32x4 bz = {zb16 | (zb16 << 16), zb16 | (zb16 << 16), zb16 | (zb16 << 16), zb16 | (zb16 << 16)};
+  const u32x4 bz = {zp, zp, zp, zp};
+  // the mask in an SGPR and the magic in a VGPR, both opaque to the optimizer, so each
+  // pair is one v_and_or_b32 (with the constants visible it emits and + or; gfx9 VOP3
+  // takes no literal operand)
+  uint32_t mask = 0, magic = 0;
+  if constexpr (WF == WF_INT4) {
+    asm volatile("s_mov_b32 %0, 0x000f000f" : "=s"(mask));
+    asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(magic));
+  }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     u32x4 b;
     if constexpr (WF == WF_INT4) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) b[q] = ((wc[j] >> (4 * q)) & 0x000F000Fu) | 0x43004300u;
+      for (int q = 0; q < 4; ++q) b[q] = ((wc[j] >> (4 * q)) & mask) | magic;
       tmp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xk[j]), __builtin_bit_cast(bf16x8, b),
                                                      tmp, 0, 0, 0);
       tmp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xk[j]), __builtin_bit_cast(bf16x8, bz),
@@ -267,7 +280,7 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const uint16_t* _
         u32x4 xk[NJ];
 #pragma unroll
         for (int j = 0; j < NJ; ++j) xk[j] = WF == WF_INT4 ? pair_k_k4(xa[i][j]) : xa[i][j];
-        accumulate_group<WF>(acc, group_product<WF, G>(wc, xk, sc, zf), sc);
+        accumulate_group<WF>(acc, group_product<WF, G>(wc, xk, sc, zf, offset_pair(zf)), sc);
     };
     if (gb - ga == GPW) {
       // a full share (every wave of a full chunk): straight-line code, so the LDS reads
@@ -330,7 +343,8 @@ __device__ __forceinline__ int div_small(int u, int d, float rd) {
 // instruction, every block all of X) costs ~3 us of the 9.8 us the [11008, 2048] M = 16
 // product took that way; 48 rows per block keep the grid to one round of blocks.
 // Dynamic LDS: X [16][2 K + 16], codes [16 RG][K / 2 (INT8: K) + 32], steps and zero
-// points [16 RG][K / G + 1] float2 (FP4: block scales [16 RG][K / 16 + 4] bytes),
+// points [16 RG][K / G + 1] float2 (INT4: the step and the bf16 offset pair of the zero
+// point; FP4: block scales [16 RG][K / 16 + 4] bytes),
 // partials [3][RG][64] f32x4.
 constexpr int kLdsKMax = 2048;
 constexpr size_t kLdsLimit = 160 * 1024;   // LDS of one gfx950 compute unit
@@ -374,6 +388,8 @@ __global__ __launch_bounds__(256 * RG) void decode_lds_kernel(const uint16_t* __
   const int ng = K / G, szs = ng + 1, bss = K / 16 + 4;
   const int xpr = K >> 3, bpr = K >> 5;   // 16-byte activation units / block-scale ushorts per row
   const float rupr = 1.0f / (float)upr, rng = 1.0f / (float)ng, rxpr = 1.0f / (float)xpr, rbpr = 1.0f / (float)bpr;
+  // u / d: folded into shifts when K is a compile-time constant, else from the reciprocal
+  auto quo = [&](int u, int d, float rd) -> int { return KF ? (int)((unsigned)u / (unsigned)d) : div_small(u, d, rd); };
   uint8_t* xs = dyn;
   uint8_t* cs = xs + 16 * xrow;
   float2* sz = reinterpret_cast<float2*>(cs + ROWS * crow);
@@ -385,16 +401,20 @@ __global__ __launch_bounds__(256 * RG) void decode_lds_kernel(const uint16_t* __
   const int r16 = lane & 15, h = lane >> 4;
   const int n0 = blockIdx.x * ROWS;
   const int nrows = min(ROWS, N - n0);
-  const int64_t rowbytes = cbk;
+  const uint32_t rowbytes = (uint32_t)cbk;
 
   // ---- loads (all in flight together; rows past N clamped to the last row) ----
   const int cunits = ROWS * upr;
+  // loads address a uniform block base plus a 32-bit lane offset (the block's rows span
+  // less than 2^32 bytes)
+  const uint8_t* cblk = C + (int64_t)n0 * rowbytes;
   u32x4 cw[CU];
 #pragma unroll
   for (int i = 0; i < CU; ++i) {
     const int u = min(tid + NT * i, cunits - 1);
-    const int q = div_small(u, upr, rupr), r = min(q, nrows - 1);
-    cw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(C + (int64_t)(n0 + r) * rowbytes + 16 * (u - q * upr)));
+    const int q = quo(u, upr, rupr), r = min(q, nrows - 1);
+    cw[i] = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(cblk + ((uint32_t)r * rowbytes + 16u * (uint32_t)(u - q * upr))));
   }
   float av[FP4 ? 1 : AU];
   uint32_t zv[AU];
@@ -403,17 +423,19 @@ __global__ __launch_bounds__(256 * RG) void decode_lds_kernel(const uint16_t* __
 #pragma unroll
     for (int i = 0; i < AU; ++i) {
       const int e = min(tid + NT * i, aunits - 1);
-      const int q = div_small(e, bpr, rbpr), r = min(q, nrows - 1);
-      zv[i] = *reinterpret_cast<const uint16_t*>(Z + (int64_t)(n0 + r) * (K >> 4) + 2 * (e - q * bpr));
+      const int q = quo(e, bpr, rbpr), r = min(q, nrows - 1);
+      zv[i] = *reinterpret_cast<const uint16_t*>(Z + (int64_t)n0 * (K >> 4) +
+                                                 ((uint32_t)r * (uint32_t)(K >> 4) + 2u * (uint32_t)(e - q * bpr)));
     }
   } else {
     const int aunits = ROWS * ng;
 #pragma unroll
     for (int i = 0; i < AU; ++i) {
       const int e = min(tid + NT * i, aunits - 1);
-      const int q = div_small(e, ng, rng), r = min(q, nrows - 1), g = e - q * ng;
-      av[i] = S[(int64_t)(n0 + r) * ng + g];
-      zv[i] = Z[(int64_t)(n0 + r) * ng + g];
+      const int q = quo(e, ng, rng), r = min(q, nrows - 1), g = e - q * ng;
+      const uint32_t off = (uint32_t)r * (uint32_t)ng + (uint32_t)g;
+      av[i] = (S + (int64_t)n0 * ng)[off];
+      zv[i] = (Z + (int64_t)n0 * ng)[off];
     }
   }
   const int xunits = 16 * xpr;
@@ -421,15 +443,16 @@ __global__ __launch_bounds__(256 * RG) void decode_lds_kernel(const uint16_t* __
 #pragma unroll
   for (int i = 0; i < XU; ++i) {
     const int u = min(tid + NT * i, xunits - 1);
-    const int r = div_small(u, xpr, rxpr);
-    xv[i] = r < M ? *reinterpret_cast<const u32x4*>(X + (int64_t)r * K + 8 * (u - r * xpr)) : u32x4{0u, 0u, 0u, 0u};
+    const int r = quo(u, xpr, rxpr);
+    xv[i] = r < M ? *reinterpret_cast<const u32x4*>(X + ((uint32_t)r * (uint32_t)K + 8u * (uint32_t)(u - r * xpr)))
+                  : u32x4{0u, 0u, 0u, 0u};
   }
   // ---- to LDS ----
 #pragma unroll
   for (int i = 0; i < CU; ++i) {
     const int u = tid + NT * i;
     if (u < cunits) {
-      const int q = div_small(u, upr, rupr);
+      const int q = quo(u, upr, rupr);
       *reinterpret_cast<u32x4*>(&cs[q * crow + 16 * (u - q * upr)]) = cw[i];
     }
   }
@@ -439,7 +462,7 @@ __global__ __launch_bounds__(256 * RG) void decode_lds_kernel(const uint16_t* __
     for (int i = 0; i < AU; ++i) {
       const int e = tid + NT * i;
       if (e < aunits) {
-        const int r = div_small(e, bpr, rbpr);
+        const int r = quo(e, bpr, rbpr);
         *reinterpret_cast<uint16_t*>(&bsl[r * bss + 2 * (e - r * bpr)]) = (uint16_t)zv[i];
       }
     }
@@ -449,8 +472,10 @@ __global__ __launch_bounds__(256 * RG) void decode_lds_kernel(const uint16_t* __
     for (int i = 0; i < AU; ++i) {
       const int e = tid + NT * i;
       if (e < aunits) {
-        const int r = div_small(e, ng, rng);
-        sz[r * szs + (e - r * ng)] = make_float2(av[i], (float)zv[i]);
+        const int r = quo(e, ng, rng);
+        // INT4: the offset pair of the zero point, formed once per row and group
+        const float zslot = WF == WF_INT4 ? __uint_as_float(offset_pair((float)zv[i])) : (float)zv[i];
+        sz[r * szs + (e - r * ng)] = make_float2(av[i], zslot);
       }
     }
   }
@@ -458,7 +483,7 @@ __global__ __launch_bounds__(256 * RG) void decode_lds_kernel(const uint16_t* __
   for (int i = 0; i < XU; ++i) {
     const int u = tid + NT * i;
     if (u < xunits) {
-      const int r = div_small(u, xpr, rxpr);
+      const int r = quo(u, xpr, rxpr);
       *reinterpret_cast<u32x4*>(&xs[r * xrow + 16 * (u - r * xpr)]) = WF == WF_INT4 ? pair_k_k4(xv[i]) : xv[i];
     }
   }
@@ -473,18 +498,20 @@ __global__ __launch_bounds__(256 * RG) void decode_lds_kernel(const uint16_t* __
     uint32_t wc[NW];
     lds_dwords<NW>(&cs[row * crow + g * (INT8 ? G : G / 2) + (INT8 ? G / 4 : G / 8) * h], wc);
     float sc = 1.0f, zf = 0.0f;
+    uint32_t zp = 0;
     if constexpr (FP4) {
       sc = __builtin_amdgcn_cvt_f32_fp8((int)bsl[row * bss + 4 * g + h], 0);   // the lane's 16-k block
     } else {
       const float2 s_z = sz[row * szs + g];
       sc = s_z.x;
-      zf = s_z.y;
+      if constexpr (WF == WF_INT4) zp = __float_as_uint(s_z.y);
+      else zf = s_z.y;
     }
     u32x4 xk[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
       xk[j] = *reinterpret_cast<const u32x4*>(&xs[r16 * xrow + 2 * (g * G + (G / 4) * h + 8 * j)]);
-    accumulate_group<WF>(acc, group_product<WF, G>(wc, xk, sc, zf), sc);
+    accumulate_group<WF>(acc, group_product<WF, G>(wc, xk, sc, zf, zp), sc);
   };
   if (gb - ga == GQ) {
     // a full quarter (K = 2048): straight-line code, so the LDS reads and dequantization
