@@ -18,6 +18,8 @@ hipError_t launch_w4a16_gemv(const uint16_t* X, int M, int K, const uint8_t* P, 
                              int N, int group, float* Y, hipStream_t stream);
 // the same products on the matrix cores, M <= 16 (used by the launch_*_gemv dispatchers
 // from a few rows up); FP4 needs K % 64 == 0
+// true where the LDS-staged matrix-core decode kernel serves a W4A16 product (K = 2048, N >= 8192, M >= 4)
+bool w4a16_lds_decode(int M, int N, int K);
 hipError_t launch_w4a16_gemv_mfma(const uint16_t* X, int M, int K, const uint8_t* P, const float* S,
                                   const uint8_t* Z, int N, int group, float* Y, hipStream_t stream);
 hipError_t launch_w8a16_gemv_mfma(const uint16_t* X, int M, int K, const uint8_t* C, const float* S,

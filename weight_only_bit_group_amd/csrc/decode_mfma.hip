@@ -630,6 +630,8 @@ hipError_t launch_format(const uint16_t* X, int M, int K, const uint8_t* C, cons
 
 }  // namespace
 
+bool w4a16_lds_decode(int M, int N, int K) { return K == kLdsKMax && N >= 8192 && M >= kLdsMinMFixed; }
+
 hipError_t launch_w4a16_gemv_mfma(const uint16_t* X, int M, int K, const uint8_t* P, const float* S,
                                   const uint8_t* Z, int N, int group, float* Y, hipStream_t stream) {
   return launch_format<WF_INT4>(X, M, K, P, S, Z, 1.0f, N, group, Y, stream);

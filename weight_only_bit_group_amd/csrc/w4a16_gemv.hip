@@ -259,14 +259,17 @@ hipError_t launch_w4a16_gemv_valu(const uint16_t* X, int M, int K, const uint8_t
   }
 }
 
-// The VALU kernel up to 4 activation rows, the matrix-core kernel from 5 (measured on
+// The VALU kernel up to 4 activation rows, the matrix-core kernels from 5 (measured on
 // the gate [11008, 2048], down [2048, 11008], q [2048, 2048] and [4096, 4096] shapes:
 // the VALU kernel's time grows with M; at M = 4 it is 7.1 against 7.3 us on gate and
-// 10.5 against 12.6 on down, at M = 5 10.9 against 7.7 on gate, 17.0 against 12.6 on
-// down and 4.1 against 4.2 on q; at M = 16 45 against 10 us on gate).
+// 10.5 against 12.6 on down for the chunked matrix-core kernel, at M = 5 10.9 against
+// 7.7 on gate, 17.0 against 12.6 on down and 4.1 against 4.2 on q; at M = 16 45 against
+// 10 us on gate).  Where the LDS-staged matrix-core kernel applies (K = 2048, N >= 8192)
+// it takes M = 4 as well: 6.6 against 7.3 us on gate.
 hipError_t launch_w4a16_gemv(const uint16_t* X, int M, int K, const uint8_t* P, const float* S,
                              const uint8_t* Z, int N, int group, float* Y, hipStream_t stream) {
-  if (M >= 5) return launch_w4a16_gemv_mfma(X, M, K, P, S, Z, N, group, Y, stream);
+  if (M >= 5 || (M == 4 && w4a16_lds_decode(M, N, K)))
+    return launch_w4a16_gemv_mfma(X, M, K, P, S, Z, N, group, Y, stream);
   return launch_w4a16_gemv_valu(X, M, K, P, S, Z, N, group, Y, stream);
 }
 
