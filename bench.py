@@ -470,7 +470,8 @@ def main():
             lay.append(B.aq_quantize_pack(wl, G_))
             del wl
         pre_stack.append(lay)
-    ws_pre = torch.empty(max(B.aq_w4a16_gemm_workspace(M_GEMM, n, k, G_) for _, n, k in synth.LAYER_LINEARS),
+    # staging matrix (M = 4096) and K-slice partials (the few-tile shapes), the largest of every call
+    ws_pre = torch.empty(max(B.aq_w4a16_gemm_workspace(mm, n, k, G_) for mm in PRE_M for _, n, k in synth.LAYER_LINEARS),
                          dtype=torch.uint8, device=dev)
     pre_x = {mm: {k: acts_bf16(mm, k) for k in (2048, 11008)} for mm in PRE_M}
     pre_y = {mm: {n: torch.empty((mm, n), dtype=torch.float32, device=dev) for n in (2048, 256, 11008)}
@@ -537,6 +538,8 @@ def main():
     fp4_graphs = {tag: _graph(lambda f=f: [B.aq_fp4_gemm(f["x1"], c4, b4, ts, out=f["y1"]) for (c4, b4) in f["ops"]])
                   for tag, f in fp4_ops.items()}
     x512 = acts_bf16(512, K_)
+    ws512 = torch.empty(B.aq_w4a16_gemm_workspace(512, N_, K_, G_), dtype=torch.uint8, device=dev)
+    ws512q = torch.empty(B.aq_w4a16_gemm_workspace(512, 2048, 2048, G_), dtype=torch.uint8, device=dev)
     y512 = torch.empty((512, N_), dtype=torch.float32, device=dev)
     y512q = torch.empty((512, 2048), dtype=torch.float32, device=dev)
     q_pack = pre_stack[0][0]
@@ -553,8 +556,8 @@ def main():
         timed("gemm8", record, lambda: B.aq_w8a16_gemm(xg, *pk8, G_, out=yg, workspace=ws8))
         p, s, z = copies[0]
         timed("gemm", record, lambda: B.aq_w4a16_gemm(xg, p, s, z, G_, out=yg, workspace=ws_gemm))
-        timed("gemm_m512", record, lambda: B.aq_w4a16_gemm(x512, p, s, z, G_, out=y512))
-        timed("gemm_m512_q", record, lambda: B.aq_w4a16_gemm(x512, *q_pack, G_, out=y512q))
+        timed("gemm_m512", record, lambda: B.aq_w4a16_gemm(x512, p, s, z, G_, out=y512, workspace=ws512))
+        timed("gemm_m512_q", record, lambda: B.aq_w4a16_gemm(x512, *q_pack, G_, out=y512q, workspace=ws512q))
         sum_abs.zero_()
         timed("absmean", record, lambda: B.aq_act_absmean(xcal, sum_abs, CAL_T, mean, ws_abs))
         timed("search", record, lambda: B.aq_awq_search(xsub, absmean_host, w_gate, G_, 20, ws_search))

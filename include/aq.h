@@ -113,10 +113,18 @@ aq_status aq_w4a16_gemv(const uint16_t* X, int64_t M, int64_t K, const uint8_t* 
  *
  * Two paths with identical results (bit-identical outputs): fused (the kernel
  * dequantizes each weight tile in LDS) and staged (a first kernel writes the
- * exact bf16 (q - z) of every weight into `workspace`, the GEMM then streams it).
- * The staged path runs when workspace is not NULL and workspace_bytes is at
- * least aq_w4a16_gemm_workspace(M, N, K, group) > 0 (large M, where it is
- * faster); otherwise the fused path runs and workspace is not touched.
+ * exact bf16 (q - z) of every weight into `workspace`, the GEMM then streams it;
+ * used for M >= 2048).  Launches with few output tiles (small M or N: at most
+ * 128 tiles of 256 or 128 rows x 128 columns) also split K into up to 8 slices
+ * of whole 64-k stages and groups: each slice writes an fp32 partial
+ * [M, N] into `workspace` and a second kernel adds the slices in order
+ * (deterministic; the sum order differs from the unsplit GEMM's, so the results
+ * differ from it by fp32 rounding).
+ * aq_w4a16_gemm_workspace(M, N, K, group) gives the bytes of both (staging
+ * matrix, then 256-byte aligned partials); it depends on the sizes only.  With
+ * workspace_bytes at least that, both are used; else, with room for the staging
+ * matrix, the staged path alone; else the fused path without slices, and
+ * workspace is not touched.
  * workspace: caller-owned device memory, 256-byte aligned, used only during the
  * call on `stream` (its contents afterwards are unspecified).
  * Errors: EINVAL for M < 0 or M >= 2^30, K or N >= 2^22, a misaligned workspace, and

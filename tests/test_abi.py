@@ -111,7 +111,16 @@ def test_gemm_workspace_selects_the_staged_path(lib, monkeypatch):
     the fused path (no error)."""
     need = lib.aq_w4a16_gemm_workspace(4096, 11008, 2048, 64)
     assert need == 11008 * 2048 * 2
-    assert lib.aq_w4a16_gemm_workspace(64, 11008, 2048, 64) == 0
+    # few output tiles: K slices, their fp32 partials (86 tiles at M = 64: 3 slices of 704 k)
+    assert lib.aq_w4a16_gemm_workspace(64, 11008, 2048, 64) == 3 * 64 * 11008 * 4
+    # 512 x 2048 (32 tiles): 6 slices of 384 k (the last 128); with staging at M = 4096
+    # (32 tiles of N = 256) the partials follow the staging matrix
+    assert lib.aq_w4a16_gemm_workspace(512, 2048, 2048, 64) == 6 * 512 * 2048 * 4
+    assert lib.aq_w4a16_gemm_workspace(4096, 256, 2048, 64) == 256 * 2048 * 2 + 6 * 4096 * 256 * 4
+    # 4 tiles: the most slices (8)
+    assert lib.aq_w4a16_gemm_workspace(512, 256, 2048, 64) == 8 * 512 * 256 * 4
+    # too short to split (fewer than two slices of four stages), or many tiles: nothing
+    assert lib.aq_w4a16_gemm_workspace(512, 2048, 448, 64) == 0
     assert lib.aq_w4a16_gemm_workspace(2047, 11008, 2048, 64) == 0
     assert lib.aq_w4a16_gemm_workspace(4096, 11008, 2048, 48) == 0
     assert lib.aq_w4a16_gemm_workspace(4096, 11008, 2000, 64) == 0

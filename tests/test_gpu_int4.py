@@ -237,14 +237,48 @@ def test_gemm_staged_equals_fused(m, n, k, g):
     w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
     p, s, z = int4.quantize_pack(w, g)
     xb = synth.f32_to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
-    assert B.aq_w4a16_gemm_workspace(m, n, k, g) == n * k * 2
+    assert B.aq_w4a16_gemm_workspace(m, n, k, g) >= n * k * 2
     step(f"aq_w4a16_gemm staged M={m} N={n} K={k} g={g}")
-    ys = host(B.aq_w4a16_gemm(dev_bf16(xb), dev(p), dev(s), dev(z), g))
+    # exactly the staging matrix: the staged path without K slices
+    ys = host(B.aq_w4a16_gemm(dev_bf16(xb), dev(p), dev(s), dev(z), g,
+                              workspace=torch.empty(n * k * 2, dtype=torch.uint8, device="cuda")))
     step(f"aq_w4a16_gemm fused M={m} N={n} K={k} g={g}")
     yf = host(B.aq_w4a16_gemm(dev_bf16(xb), dev(p), dev(s), dev(z), g,
                               workspace=torch.empty(0, dtype=torch.uint8, device="cuda")))
     assert np.array_equal(ys.view(np.uint32), yf.view(np.uint32))
     check_close(ys, int4.forward(synth.bf16_bits_to_f32(xb), p, s, z, g), f"gemm staged {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m,n,k,g", [(512, 2048, 2048, 64), (512, 256, 2048, 64), (300, 130, 4096, 128),
+                                     (64, 8195, 2048, 32), (512, 2048, 11008, 64), (4096, 256, 2048, 64)])
+def test_gemm_k_slices(m, n, k, g):
+    """Few output tiles: K split into slices whose fp32 partials are added in order (with the
+    staging matrix at M = 4096), against the oracle and the unsplit fused GEMM."""
+    rng = np.random.default_rng(m + 5 * n + k)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    p, s, z = int4.quantize_pack(w, g)
+    xb = synth.f32_to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+    staged = n * k * 2 if m >= 2048 else 0
+    need = B.aq_w4a16_gemm_workspace(m, n, k, g)
+    assert need > staged and (need - ((staged + 255) // 256 * 256 if staged else 0)) % (m * n * 4) == 0
+    step(f"aq_w4a16_gemm K slices M={m} N={n} K={k} g={g}")
+    y = host(B.aq_w4a16_gemm(dev_bf16(xb), dev(p), dev(s), dev(z), g,
+                             workspace=torch.empty(need, dtype=torch.uint8, device="cuda")))
+    step(f"aq_w4a16_gemm fused, no slices M={m} N={n} K={k} g={g}")
+    yf = host(B.aq_w4a16_gemm(dev_bf16(xb), dev(p), dev(s), dev(z), g,
+                              workspace=torch.empty(0, dtype=torch.uint8, device="cuda")))
+    assert np.abs(y - yf).max() <= 1e-5 * np.abs(yf).max()
+    check_close(y, int4.forward(synth.bf16_bits_to_f32(xb), p, s, z, g), f"gemm K slices {m}x{n}x{k}")
+
+
+def test_gemm_k_slices_exact_integer_case():
+    """Small integers: every partial and the ordered sum of the slices are exact in fp32."""
+    m, n, k, g = 200, 130, 1024, 64
+    xb, x, p, s, z = _exact_case(np.random.default_rng(17), m, n, k, g)
+    assert B.aq_w4a16_gemm_workspace(m, n, k, g) > 0
+    step(f"aq_w4a16_gemm K slices exact-integer M={m} N={n} K={k} g={g}")
+    y = host(B.aq_w4a16_gemm(dev_bf16(xb), dev(p), dev(s), dev(z), g))
+    assert (y.astype(np.float64) == int4.forward(x, p, s, z, g)).all()
 
 
 def test_pack_then_gemv_round_trip():

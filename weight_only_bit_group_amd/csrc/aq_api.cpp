@@ -312,9 +312,26 @@ aq_status aq_w8a16_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_t* 
                         "aq_w8a16_gemm");
 }
 
+// The W4A16 GEMM's workspace: the staging matrix (large M), then the K-slice partials
+// (launches with few output tiles), 256-byte aligned.
+struct GemmWorkspace {
+  size_t staged, partial, total;
+};
+
+static GemmWorkspace gemm_workspace(int64_t M, int64_t N, int64_t K, int32_t group) {
+  GemmWorkspace w = {0, 0, 0};
+  if (!valid_group(group) || K <= 0 || K % group || M <= 0 || N <= 0 || K >= kGemmDimLimit || N >= kGemmDimLimit)
+    return w;
+  w.staged = staged_bytes(M, N, K);
+  int kslice = 0;
+  const int slices = aq::gemm_k_slices(M, N, K, group, &kslice);
+  if (slices > 1) w.partial = (size_t)slices * (size_t)M * (size_t)N * sizeof(float);
+  w.total = (w.partial ? round_up(w.staged, 256) : w.staged) + w.partial;
+  return w;
+}
+
 size_t aq_w4a16_gemm_workspace(int64_t M, int64_t N, int64_t K, int32_t group) {
-  if (!valid_group(group) || K % group) return 0;
-  return staged_bytes(M, N, K);
+  return gemm_workspace(M, N, K, group).total;
 }
 
 aq_status aq_w4a16_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_t* packed, const float* scales,
@@ -325,13 +342,24 @@ aq_status aq_w4a16_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_t* 
   if (st != AQ_OK) return st;
   AQ_REQUIRE(K < kGemmDimLimit && N < kGemmDimLimit, "aq_w4a16_gemm: K and N must be below 2^22 (got %lld, %lld)",
              (long long)K, (long long)N);
+  // the whole plan when the workspace holds it; else the staging matrix alone when it
+  // fits; else the fused path without K slices (workspace untouched)
   uint16_t* staged = nullptr;
-  st = staging("aq_w4a16_gemm", M, N, K, workspace, workspace_bytes, &staged);
-  if (st != AQ_OK) return st;
+  float* partial = nullptr;
+  const GemmWorkspace w = gemm_workspace(M, N, K, group);
+  if (workspace != nullptr && w.total > 0 && workspace_bytes >= w.total) {
+    AQ_REQUIRE(aligned(workspace, 256), "aq_w4a16_gemm: workspace must be 256-byte aligned");
+    char* base = static_cast<char*>(workspace);
+    if (w.staged) staged = reinterpret_cast<uint16_t*>(base);
+    if (w.partial) partial = reinterpret_cast<float*>(base + round_up(w.staged, 256));
+  } else {
+    st = staging("aq_w4a16_gemm", M, N, K, workspace, workspace_bytes, &staged);
+    if (st != AQ_OK) return st;
+  }
   if (fault_injected()) return fail(AQ_ERUNTIME, "aq_w4a16_gemm: injected launch failure");
   if (N == 0 || M == 0) return ok();
   return runtime_status(aq::launch_w4a16_gemm(X, (int)M, (int)K, packed, scales, zeros, (int)N, group, Y, staged,
-                                              (hipStream_t)stream),
+                                              partial, (hipStream_t)stream),
                         "aq_w4a16_gemm");
 }
 

@@ -36,8 +36,12 @@ hipError_t launch_w4a16_gemv_valu(const uint16_t* X, int M, int K, const uint8_t
                                   const uint8_t* Z, int N, int group, float* Y, hipStream_t stream);
 // `staged`: NULL for the fused kernel, else N * K bf16 of device memory that first
 // receives the dequantized weights (the staged GEMM then loads them like activations)
-hipError_t launch_w4a16_gemm(const uint16_t* X, int M, int K, const uint8_t* P, const float* S, const uint8_t* Z,
-                             int N, int group, float* Y, uint16_t* staged, hipStream_t stream);
+// K slices of a W4A16 GEMM with few output tiles (1: none); *kslice = k per slice.  The
+// split GEMM writes slices x M x N fp32 partials to `partial` and adds them in order.
+int gemm_k_slices(int64_t M, int64_t N, int64_t K, int group, int* kslice);
+hipError_t launch_w4a16_gemm(const uint16_t* X, int M, int K, const uint8_t* P, const float* S,
+                             const uint8_t* Z, int N, int group, float* Y, uint16_t* staged, float* partial,
+                             hipStream_t stream);
 // 8-bit codes [N, K] (one byte per weight), S / z as the INT4 format
 hipError_t launch_quant_pack8(const void* W, bool w_bf16, const float* chan_scale, uint8_t* codes, float* scales,
                               uint8_t* zeros, int64_t N, int64_t K, int group, hipStream_t stream);

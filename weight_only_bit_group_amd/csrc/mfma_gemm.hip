@@ -101,6 +101,12 @@ enum BKind { B_INT4 = 0, B_SPLIT = 1, B_FP4 = 2, B_INT4S = 3, B_FP4S = 4, B_GRAM
 struct GemmArgs {
   const uint16_t* X;
   int M, N, K;
+  // row stride in k of X, of the weight arrays and of the staged / plane matrices (= K
+  // unless the contraction is split); K slice: ks blocks along y each take kslice k
+  // (K is the slice length then) and write their fp32 output ystride floats apart
+  int ld;
+  int kslice;
+  int64_t ystride;
   // INT4
   const uint8_t* P;
   const float* S;
@@ -131,6 +137,20 @@ __device__ __forceinline__ int swz(int row, int unit) { return row * ROW_UNITS +
 
 template <int BK, int G, bool TAIL, int WGM>
 __global__ __launch_bounds__(128 * WGM, 1) void gemm_kernel(GemmArgs a) {
+  if (gridDim.y > 1) {
+    // K slice blockIdx.y: operands from its first k on, its own output buffer
+    const int k0 = (int)blockIdx.y * a.kslice;
+    a.K = min(a.kslice, a.K - k0);
+    a.X += k0;
+    if (a.P) a.P += k0 >> 1;
+    if (a.B) a.B += k0;
+    if (a.B2) a.B2 += k0;
+    if (a.codes) a.codes += k0 >> 1;
+    if (a.bscale) a.bscale += k0 >> 4;
+    if (a.S) a.S += k0 / G;
+    if (a.Z) a.Z += k0 / G;
+    a.Y += (int64_t)blockIdx.y * a.ystride;
+  }
   constexpr int NW = 2 * WGM, NT = 64 * NW;
   constexpr int BM = 64 * WGM;
   constexpr bool DEQ = BK == B_INT4 || BK == B_FP4;        // codes dequantized here
@@ -165,7 +185,8 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_kernel(GemmArgs a) {
   const int lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wid >> 1, wn = wid & 1;
-  const int M = a.M, N = a.N, K = a.K;
+  const int M = a.M, N = a.N, K = a.K, LD = a.ld;
+  const int GLD = LD / G;   // row stride of the group steps and zero points
   const int tiles_n = (N + BN - 1) / BN;
   const int tiles_m = (M + BM - 1) / BM;
   const int ntiles = tiles_m * tiles_n;
@@ -209,12 +230,12 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < A_DMA; ++j) {
       const int r8 = j * NW + wid;
-      aoff[j] = (uint32_t)(min(m0 + 8 * r8 + lrow8, M - 1) - m0) * (uint32_t)K * 2u + (uint32_t)gunit_of(r8) * 16u;
+      aoff[j] = (uint32_t)(min(m0 + 8 * r8 + lrow8, M - 1) - m0) * (uint32_t)LD * 2u + (uint32_t)gunit_of(r8) * 16u;
     }
   };
   // activations of stage s of the tile at row m0 (aoff set for that tile)
   auto issue_a = [&](int m0, int s, int slot) {
-    const char* base = reinterpret_cast<const char*>(a.X + (size_t)m0 * K) + (size_t)s * (KS * 2);
+    const char* base = reinterpret_cast<const char*>(a.X + (size_t)m0 * LD) + (size_t)s * (KS * 2);
     const bool tail = TAIL && s == nfull;
 #pragma unroll
     for (int j = 0; j < A_DMA; ++j) {
@@ -231,7 +252,7 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
         const int r8 = j * NW + wid;
-        boff[j] = (uint32_t)(min(n0 + 8 * r8 + lrow8, N - 1) - n0) * (uint32_t)K * 2u + (uint32_t)gunit_of(r8) * 16u;
+        boff[j] = (uint32_t)(min(n0 + 8 * r8 + lrow8, N - 1) - n0) * (uint32_t)LD * 2u + (uint32_t)gunit_of(r8) * 16u;
       }
     }
   };
@@ -245,8 +266,8 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_kernel(GemmArgs a) {
         const int r = 32 * job + (lane >> 1);
         const uint32_t n = (uint32_t)(min(n0 + r, N - 1) - n0);
         const uint32_t half = tail ? 0u : (uint32_t)(lane & 1) * 16u;
-        const uint8_t* src = ((BK == B_INT4) ? a.P : a.codes) + (size_t)n0 * (K >> 1) + (size_t)s * (KS / 2);
-        dma16(src, n * (uint32_t)(K >> 1) + half, lds_addr(&Cs[cslot][1024 * job]));
+        const uint8_t* src = ((BK == B_INT4) ? a.P : a.codes) + (size_t)n0 * (LD >> 1) + (size_t)s * (KS / 2);
+        dma16(src, n * (uint32_t)(LD >> 1) + half, lds_addr(&Cs[cslot][1024 * job]));
       } else if constexpr (BK == B_INT4) {
         int x = job - 4;
         if (x >= 8) x -= 4;                                  // repeated zero-point loads (g = 32)
@@ -255,15 +276,15 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_kernel(GemmArgs a) {
         const int rh = 64 * (x & 1);
         const uint32_t n = (uint32_t)(min(n0 + rh + lane, N - 1) - n0);
         const uint32_t g = (uint32_t)min((s * KS + 32 * gi) / G, ngroups - 1);
-        const uint32_t idx = n * (uint32_t)ngroups + g;
-        if (is_z) dma1(a.Z + (size_t)n0 * ngroups, idx, lds_addr(&AX[xslot][1][gi][rh]));
-        else dma4(a.S + (size_t)n0 * ngroups, idx * 4u, lds_addr(&AX[xslot][0][gi][rh]));
+        const uint32_t idx = n * (uint32_t)GLD + g;
+        if (is_z) dma1(a.Z + (size_t)n0 * GLD, idx, lds_addr(&AX[xslot][1][gi][rh]));
+        else dma4(a.S + (size_t)n0 * GLD, idx * 4u, lds_addr(&AX[xslot][0][gi][rh]));
       } else {
         const int x = job - 4;
         const int h = x >> 1, rh = 64 * (x & 1);
         const uint32_t n = (uint32_t)(min(n0 + rh + lane, N - 1) - n0);
         const uint32_t byte = (uint32_t)(s * 4 + 2 * (tail ? 0 : h));   // the tail stage has 2 block scales
-        dma2(a.bscale + (size_t)n0 * (K >> 4), n * (uint32_t)(K >> 4) + byte, lds_addr(&AX[xslot][0][h][rh]));
+        dma2(a.bscale + (size_t)n0 * (LD >> 4), n * (uint32_t)(LD >> 4) + byte, lds_addr(&AX[xslot][0][h][rh]));
       }
     }
   };
@@ -273,14 +294,14 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_kernel(GemmArgs a) {
   };
   // one activation load (j < A_DMA) / one SPLIT plane load (q < B_DMA) of stage s
   auto issue_a_one = [&](int m0, int s, int slot, int j) {
-    const char* base = reinterpret_cast<const char*>(a.X + (size_t)m0 * K) + (size_t)s * (KS * 2);
+    const char* base = reinterpret_cast<const char*>(a.X + (size_t)m0 * LD) + (size_t)s * (KS * 2);
     const int r8 = j * NW + wid;
     dma16(base, aoff[j] - ((TAIL && s == nfull) ? fold_of(r8) : 0u), lds_addr(&As[slot][8 * r8 * KS]));
   };
   auto issue_plane_one = [&](int n0, int s, int slot, int q) {
     if constexpr (!DEQ) {
       const int pl = q / PER, j = q % PER, r8 = j * NW + wid;
-      const char* base = reinterpret_cast<const char*>((pl ? a.B2 : a.B) + (size_t)n0 * K) + (size_t)s * (KS * 2);
+      const char* base = reinterpret_cast<const char*>((pl ? a.B2 : a.B) + (size_t)n0 * LD) + (size_t)s * (KS * 2);
       dma16(base, boff[j] - ((TAIL && s == nfull) ? fold_of(r8) : 0u), lds_addr(&Bs[slot][pl][8 * r8 * KS]));
     }
   };
@@ -300,7 +321,7 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_kernel(GemmArgs a) {
       const int gi = part >> 1, rh = 64 * (part & 1);
       const uint32_t n = (uint32_t)(min(n0 + rh + lane, N - 1) - n0);
       const uint32_t g = (uint32_t)min((s * KS + 32 * gi) / G, ngroups - 1);
-      dma4(a.S + (size_t)n0 * ngroups, (n * (uint32_t)ngroups + g) * 4u, lds_addr(&AX[slot][0][gi][rh]));
+      dma4(a.S + (size_t)n0 * GLD, (n * (uint32_t)GLD + g) * 4u, lds_addr(&AX[slot][0][gi][rh]));
     }
   };
 
@@ -869,50 +890,123 @@ int tiles(int M, int N, int bm) { return ((M + bm - 1) / bm) * ((N + BN - 1) / B
 // 256-row tiles (8 waves) once M fills them; 128-row tiles (4 waves) for small M.
 constexpr int kWideM = 192;
 
+// K slices for launches with few tiles (the q / k / v / o / down shapes at a few hundred
+// rows leave most CUs idle otherwise, and a lone block runs ~1.1 us per 64-k stage on its
+// load latency): at most kSplitMax slices, enough to bring the blocks to about
+// kSplitTargetBlocks, each at least kSplitMinStages 64-k stages and a whole number of
+// groups.  Measured on gfx950 (GEMM + fixed-order sum, us): [512, 2048, 2048] 35.6 unsplit,
+// 19.2 / 18.4 / 19.8 with 4 / 6 / 8 slices; [512, 2048, 11008] 166 -> 43.9 / 43.0 with 6 / 8;
+// [512, 256, 2048] 34.7 -> 13.6 with 8; splitting the 172 tiles of [512, 11008, 2048] is
+// slower (41 -> 60).  Planned against the 256 CUs of an MI355X, so the workspace size is a
+// function of the sizes alone.
+constexpr int64_t kSplitMaxTiles = 128;
+constexpr int64_t kSplitTargetBlocks = 192;
+constexpr int64_t kSplitMax = 8;
+constexpr int64_t kSplitMinStages = 4;
+
 // Grid: one block per CU looping over the tiles (persistent) when every tile has at
 // least four full stages, else one block per tile.
 template <int BK, int G, bool TAIL>
-hipError_t launch_tail(const GemmArgs& a, hipStream_t stream) {
+hipError_t launch_tail(const GemmArgs& a, hipStream_t stream, int slices) {
   const bool wide = a.M > kWideM;
   const int nt = tiles(a.M, a.N, wide ? 256 : 128);
   const int grid = (!TAIL && a.K / KS >= 4) ? min(nt, device_cu_count()) : nt;
   if (wide) {
-    hipLaunchKernelGGL((gemm_kernel<BK, G, TAIL, 4>), dim3(grid), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((gemm_kernel<BK, G, TAIL, 4>), dim3(grid, slices), dim3(512), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((gemm_kernel<BK, G, TAIL, 2>), dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((gemm_kernel<BK, G, TAIL, 2>), dim3(grid, slices), dim3(256), 0, stream, a);
   }
   return hipGetLastError();
 }
 
+// slices > 1: K split into slices of a.kslice k along the grid's y (K % KS == 0)
 template <int BK, int G>
-hipError_t launch_tiles(const GemmArgs& a, hipStream_t stream) {
-  if (a.K % KS) return launch_tail<BK, G, true>(a, stream);
-  return launch_tail<BK, G, false>(a, stream);
+hipError_t launch_tiles(GemmArgs a, hipStream_t stream, int slices = 1) {
+  if (a.ld == 0) a.ld = a.K;
+  if (a.K % KS) return launch_tail<BK, G, true>(a, stream, 1);
+  return launch_tail<BK, G, false>(a, stream, slices);
+}
+
+// Y[i] = sum over s of P[s][i], s in order (deterministic); four outputs per thread,
+// as 16-byte accesses when every slice and Y are 16-byte aligned (vec)
+__global__ __launch_bounds__(256) void ksplit_sum_kernel(const float* __restrict__ P, int slices, int64_t count,
+                                                          float* __restrict__ Y, bool vec) {
+  const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i0 >= count) return;
+  if (vec) {
+    f32x4 acc = *reinterpret_cast<const f32x4*>(P + i0);
+    for (int sl = 1; sl < slices; ++sl) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(P + (int64_t)sl * count + i0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += v[e];
+    }
+    __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(Y + i0));
+  } else {
+    for (int64_t i = i0; i < min(count, i0 + 4); ++i) {
+      float acc = P[i];
+      for (int sl = 1; sl < slices; ++sl) acc += P[(int64_t)sl * count + i];
+      Y[i] = acc;
+    }
+  }
 }
 
 }  // namespace
 
+int gemm_k_slices(int64_t M, int64_t N, int64_t K, int group, int* kslice) {
+  *kslice = (int)K;
+  if (K <= 0 || K % KS || K % group || M <= 0 || N <= 0) return 1;
+  const int64_t bm = M > kWideM ? 256 : 128;
+  const int64_t nt = ((M + bm - 1) / bm) * ((N + BN - 1) / BN);
+  if (nt > kSplitMaxTiles) return 1;
+  const int64_t stages = K / KS, unit = (group > KS ? group : KS) / KS;   // stages per slice granule
+  int64_t sl = std::min<int64_t>({kSplitMax, (kSplitTargetBlocks + nt - 1) / nt, stages / kSplitMinStages});
+  if (sl < 2) return 1;
+  int64_t per = (stages + sl - 1) / sl;
+  per = (per + unit - 1) / unit * unit;
+  sl = (stages + per - 1) / per;
+  if (sl < 2) return 1;
+  *kslice = (int)(per * KS);
+  return (int)sl;
+}
+
 hipError_t launch_w4a16_gemm(const uint16_t* X, int M, int K, const uint8_t* P, const float* S,
-                             const uint8_t* Z, int N, int group, float* Y, uint16_t* staged, hipStream_t stream) {
+                             const uint8_t* Z, int N, int group, float* Y, uint16_t* staged, float* partial,
+                             hipStream_t stream) {
   GemmArgs a = {};
-  a.X = X; a.M = M; a.N = N; a.K = K; a.P = P; a.S = S; a.Z = Z; a.Y = Y;
+  a.X = X; a.M = M; a.N = N; a.K = K; a.ld = K; a.P = P; a.S = S; a.Z = Z; a.Y = Y;
+  int kslice = K;
+  const int slices = partial ? gemm_k_slices(M, N, K, group, &kslice) : 1;
+  if (slices > 1) {
+    a.Y = partial;
+    a.kslice = kslice;
+    a.ystride = (int64_t)M * N;
+  }
+  hipError_t e = hipSuccess;
   if (staged) {
-    hipError_t e = stage_weights<false>(P, Z, N, K, group, staged, stream);
+    e = stage_weights<false>(P, Z, N, K, group, staged, stream);
     if (e != hipSuccess) return e;
     a.B = staged;
     switch (group) {
-      case 32: return launch_tiles<B_INT4S, 32>(a, stream);
-      case 64: return launch_tiles<B_INT4S, 64>(a, stream);
-      case 128: return launch_tiles<B_INT4S, 128>(a, stream);
+      case 32: e = launch_tiles<B_INT4S, 32>(a, stream, slices); break;
+      case 64: e = launch_tiles<B_INT4S, 64>(a, stream, slices); break;
+      case 128: e = launch_tiles<B_INT4S, 128>(a, stream, slices); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (group) {
+      case 32: e = launch_tiles<B_INT4, 32>(a, stream, slices); break;
+      case 64: e = launch_tiles<B_INT4, 64>(a, stream, slices); break;
+      case 128: e = launch_tiles<B_INT4, 128>(a, stream, slices); break;
       default: return hipErrorInvalidValue;
     }
   }
-  switch (group) {
-    case 32: return launch_tiles<B_INT4, 32>(a, stream);
-    case 64: return launch_tiles<B_INT4, 64>(a, stream);
-    case 128: return launch_tiles<B_INT4, 128>(a, stream);
-    default: return hipErrorInvalidValue;
-  }
+  if (e != hipSuccess || slices == 1) return e;
+  const int64_t count = (int64_t)M * N;
+  const bool vec = (count & 3) == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(partial) & 15) == 0;
+  hipLaunchKernelGGL(ksplit_sum_kernel, dim3((unsigned)((count + 1023) / 1024)), dim3(256), 0, stream, partial,
+                     slices, count, Y, vec);
+  return hipGetLastError();
 }
 
 hipError_t launch_w8a16_gemm(const uint16_t* X, int M, int K, const uint8_t* C, const float* S, const uint8_t* Z,
