@@ -50,17 +50,58 @@ __device__ __forceinline__ double wave_sum(double v) {
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
   return v;
 }
-// Sum of a wave's 64 lanes into lane 63 with DPP (quad permutations, row mirrors,
-// row_bcast:15 / row_bcast:31); the other lanes hold partial sums.
-__device__ __forceinline__ float dpp_sum_to_lane63(float v) {
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xC, 0xF, false));
-  return v;
+// Totals of V per-lane values over a wave's 64 lanes (V a power of two): the values
+// are halved across lanes 32 apart (v_permlane32_swap), then 16 apart
+// (v_permlane16_swap), and each remaining value is summed inside its 16-lane row with
+// DPP (quad permutations, row rotations by 4 and 8).  Afterwards every lane of 16-lane
+// row rho holds in a[j], j < wave_sums_out<V>, the total of value
+// wave_sums_index<V>(j, rho); the lanes where wave_sums_owner<V> is true hold each total
+// once.  Every value takes the same addition tree, so its total does not depend on its
+// index.  Against one DPP chain per value into lane 63 this is V / 2 + V / 4 swaps and
+// 4 V / 4 row steps instead of 6 V dependent DPP steps.
+template <int V>
+constexpr int wave_sums_out = V >= 4 ? V / 4 : 1;
+template <int V>
+__host__ __device__ constexpr int wave_sums_index(int j, int rho) {
+  return V >= 4 ? j + (rho & 1) * (V / 4) + (rho >> 1) * (V / 2) : V == 2 ? (rho >> 1) : 0;
 }
+template <int V>
+__device__ __forceinline__ bool wave_sums_owner(int lane) {
+  return (lane & 15) == 0 && (V >= 4 || (V == 2 ? (lane & 16) == 0 : lane == 0));
+}
+// lanes 0-31: a[l] + a[l + 32]; lanes 32-63: b[l - 32] + b[l]
+__device__ __forceinline__ float permlane32_add(float a, float b) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+// 16-lane rows 0 and 2: a[l] + a[l + 16]; rows 1 and 3: b[l - 16] + b[l]
+__device__ __forceinline__ float permlane16_add(float a, float b) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int V>
+__device__ __forceinline__ void wave_sums(float (&a)[V]) {
+  static_assert(V >= 1 && V <= 64 && (V & (V - 1)) == 0, "V must be a power of two");
+  constexpr int H = V >= 2 ? V / 2 : 1, Q = wave_sums_out<V>;
+#pragma unroll
+  for (int j = 0; j < H; ++j) a[j] = permlane32_add(a[j], a[V >= 2 ? j + H : 0]);
+#pragma unroll
+  for (int j = 0; j < Q; ++j) a[j] = permlane16_add(a[j], a[H >= 2 ? j + Q : 0]);
+#pragma unroll
+  for (int j = 0; j < Q; ++j) {
+    a[j] = dpp_add<0xB1>(a[j]);    // quad_perm [1, 0, 3, 2]
+    a[j] = dpp_add<0x4E>(a[j]);    // quad_perm [2, 3, 0, 1]
+    a[j] = dpp_add<0x124>(a[j]);   // row_ror:4
+    a[j] = dpp_add<0x128>(a[j]);   // row_ror:8
+  }
+}
+// Smallest power of two >= n (n >= 1).
+__host__ __device__ constexpr int pow2_ceil(int n) { return n <= 1 ? 1 : 2 * pow2_ceil((n + 1) / 2); }
+
 // Sum over groups of `width` consecutive lanes (width a power of two <= 64).
 template <int W>
 __device__ __forceinline__ float segment_sum(float v) {

@@ -116,13 +116,19 @@ __global__ __launch_bounds__(256) void fp4_gemv_kernel(const uint16_t* __restric
     }
   }
 
+  // all M x R totals at once (permlane swaps, then DPP inside 16-lane rows)
+  constexpr int V = pow2_ceil(M * R);
+  float t[V];
 #pragma unroll
-  for (int m = 0; m < M; ++m)
+  for (int i = 0; i < V; ++i) t[i] = i < M * R ? acc[i / R][i % R] : 0.0f;
+  wave_sums<V>(t);
+  if (wave_sums_owner<V>(lane)) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float v = wave_sum(acc[m][r]);
-      if (lane == 0 && n0 + r < N) Y[(int64_t)m * N + n0 + r] = v * ts;
+    for (int j = 0; j < wave_sums_out<V>; ++j) {
+      const int i = wave_sums_index<V>(j, lane >> 4);
+      if (i < M * R && n0 + i % R < N) Y[(int64_t)(i / R) * N + n0 + i % R] = t[j] * ts;
     }
+  }
 }
 
 template <int M, int R, int CPL>

@@ -28,8 +28,9 @@
 //    is the bf16 pair (128 + q_s, 128 + q_{s+4}); v_dot2_f32_bf16 accumulates
 //    x * (128 + q) in fp32 and the chunk sum is corrected by -(128 + z) * sum(x)
 //    before the fp32 group step S is applied -- no rounded bf16 weight is formed.
-//  * Each row's 64 lane partials are reduced with DPP (quad perms, row mirrors,
-//    row_bcast:15 / row_bcast:31); lane 63 writes the result.
+//  * The wave's M x R sets of 64 lane partials are reduced together: halved across
+//    lanes 32 and 16 apart with v_permlane32_swap / v_permlane16_swap, then summed in
+//    16-lane rows with DPP; one lane per total writes it.
 #include "aq_device.h"
 #include "aq_kernels.h"
 
@@ -72,10 +73,12 @@ __device__ __forceinline__ float chunk_dot(const u32x4 code, const uint32_t* xp,
 
 // LDS_X: X [M, K] staged in LDS as permuted pairs (M * K / 2 dwords) + 8-sums (M * K / 8 floats).
 // CPL: 16-byte code chunks per lane loaded per batch (all issued before use).
-template <int M, int R, int CPL, bool LDS_X>
+// KF: the row length when fixed at compile time (0: K as passed).
+template <int M, int R, int CPL, bool LDS_X, int KF>
 __global__ __launch_bounds__(256) void w4a16_gemv_kernel(const uint16_t* X, const uint8_t* P, const float* S,
-                                                          const uint8_t* Z, float* __restrict__ Y, int N, int K,
+                                                          const uint8_t* Z, float* __restrict__ Y, int N, int k_arg,
                                                           int gshift) {
+  const int K = KF ? KF : k_arg;
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -200,21 +203,28 @@ __global__ __launch_bounds__(256) void w4a16_gemv_kernel(const uint16_t* X, cons
     }
   }
 
+  // all M x R totals at once (permlane swaps, then DPP inside 16-lane rows): a DPP
+  // chain per total into one lane was ~0.3 us of the [11008, 2048] M = 1 launch
+  constexpr int V = pow2_ceil(M * R);
+  float t[V];
 #pragma unroll
-  for (int m = 0; m < M; ++m)
+  for (int i = 0; i < V; ++i) t[i] = i < M * R ? acc[i / R][i % R] : 0.0f;
+  wave_sums<V>(t);
+  if (wave_sums_owner<V>(lane)) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float v = dpp_sum_to_lane63(acc[m][r]);
-      if (lane == 63 && n0 + r < N) Y[(int64_t)m * N + n0 + r] = v;
+    for (int j = 0; j < wave_sums_out<V>; ++j) {
+      const int i = wave_sums_index<V>(j, lane >> 4);
+      if (i < M * R && n0 + i % R < N) Y[(int64_t)(i / R) * N + n0 + i % R] = t[j];
     }
+  }
 }
 
-template <int M, int R, int CPL, bool LDS_X>
+template <int M, int R, int CPL, bool LDS_X, int KF = 0>
 hipError_t launch_cfg(const uint16_t* X, const uint8_t* P, const float* S, const uint8_t* Z, float* Y, int N, int K,
                       int gshift, hipStream_t stream) {
   const int waves = (N + R - 1) / R;
   const size_t lds = LDS_X ? (size_t)M * (K >> 1) * 4 + (size_t)M * (K >> 3) * 4 : 0;
-  hipLaunchKernelGGL((w4a16_gemv_kernel<M, R, CPL, LDS_X>), dim3((waves + 3) / 4), dim3(256), lds, stream, X, P, S,
+  hipLaunchKernelGGL((w4a16_gemv_kernel<M, R, CPL, LDS_X, KF>), dim3((waves + 3) / 4), dim3(256), lds, stream, X, P, S,
                      Z, Y, N, K, gshift);
   return hipGetLastError();
 }
@@ -232,7 +242,12 @@ hipError_t launch_m(const uint16_t* X, const uint8_t* P, const float* S, const u
       // one or two rows over a wide N (e.g. the MLP projections): four rows per wave, so
       // half as many blocks stage the activations (M = 1: 4.5 -> 4.35 us on [11008, 2048];
       // M = 2: 5.45 -> 5.26 us; from M = 3 two rows per wave stay faster)
-      if (M <= 2 && N >= 8192) return launch_cfg<M, 4, 1, true>(X, P, S, Z, Y, N, K, gshift, stream);
+      // (K = 2048, the hidden size of the q / k / v / gate / up projections, has a
+      // compile-time instance: loops and bounds fold away)
+      if (M <= 2 && N >= 8192) {
+        if (K == 2048) return launch_cfg<M, 4, 1, true, 2048>(X, P, S, Z, Y, N, K, gshift, stream);
+        return launch_cfg<M, 4, 1, true>(X, P, S, Z, Y, N, K, gshift, stream);
+      }
       return launch_cfg<M, R, 1, true>(X, P, S, Z, Y, N, K, gshift, stream);
     }
     // long rows (K > 4096, e.g. a down projection): one row per wave and up to six

@@ -18,7 +18,8 @@
 //    (M x CPL <= 6) a batch's activations are requested before its weights: loads
 //    return in order, so activations requested after the weights would wait for the
 //    HBM stream.
-//  * Each row's 64 lane partials are reduced with DPP; lane 63 writes the result.
+//  * The M x R sets of 64 lane partials are reduced together (permlane swaps, then DPP
+//    inside 16-lane rows); one lane per total writes it.
 #include "aq_device.h"
 #include "aq_kernels.h"
 
@@ -122,13 +123,19 @@ __global__ __launch_bounds__(256) void w8a16_gemv_kernel(const uint16_t* __restr
     }
   }
 
+  // all M x R totals at once (permlane swaps, then DPP inside 16-lane rows)
+  constexpr int V = pow2_ceil(M * R);
+  float t[V];
 #pragma unroll
-  for (int m = 0; m < M; ++m)
+  for (int i = 0; i < V; ++i) t[i] = i < M * R ? acc[i / R][i % R] : 0.0f;
+  wave_sums<V>(t);
+  if (wave_sums_owner<V>(lane)) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float v = dpp_sum_to_lane63(acc[m][r]);
-      if (lane == 63 && n0 + r < N) Y[(int64_t)m * N + n0 + r] = v;
+    for (int j = 0; j < wave_sums_out<V>; ++j) {
+      const int i = wave_sums_index<V>(j, lane >> 4);
+      if (i < M * R && n0 + i % R < N) Y[(int64_t)(i / R) * N + n0 + i % R] = t[j];
     }
+  }
 }
 
 template <int M, int R, int CPL>
