@@ -34,6 +34,27 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
 
+// (hi:lo) >> S as one v_lshrrev_b64: the low dword is lo >> S with hi's low S bits above
+// bit 31 - S.  The INT4 decodes keep only bits 0-3 and 16-19 of each shifted dword
+// (S <= 12), so one 64-bit shift serves two code dwords; written out because the
+// compiler splits a 64-bit shift of a dword pair into v_alignbit_b32 + v_lshrrev_b32.
+template <int S>
+__device__ __forceinline__ uint64_t shr64(uint64_t v) {
+  uint64_t t;
+  asm("v_lshrrev_b64 %0, %1, %2" : "=v"(t) : "i"(S), "v"(v));
+  return t;
+}
+// The shifted copies >> 0, 4, 8, 12 of the code dword pair (hi:lo), as dwords
+// sh[s][h] (h = 0: lo's, h = 1: hi's).
+__device__ __forceinline__ void nibble_shifts(uint32_t lo, uint32_t hi, uint32_t (&sh)[4][2]) {
+  const uint64_t pr = ((uint64_t)hi << 32) | lo;
+  const uint64_t t1 = shr64<4>(pr), t2 = shr64<8>(pr), t3 = shr64<12>(pr);
+  sh[0][0] = lo; sh[0][1] = hi;
+  sh[1][0] = (uint32_t)t1; sh[1][1] = (uint32_t)(t1 >> 32);
+  sh[2][0] = (uint32_t)t2; sh[2][1] = (uint32_t)(t2 >> 32);
+  sh[3][0] = (uint32_t)t3; sh[3][1] = (uint32_t)(t3 >> 32);
+}
+
 // ---- cross-lane reductions inside one 64-lane wave -----------------------
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

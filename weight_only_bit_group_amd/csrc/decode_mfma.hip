@@ -108,12 +108,19 @@ __device__ __forceinline__ f32x4 group_product(const uint32_t* wc, const u32x4* 
     asm volatile("s_mov_b32 %0, 0x000f000f" : "=s"(mask));
     asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(magic));
   }
+  // INT4: the shifted code copies of dword pairs from one 64-bit shift each
+  uint32_t sh[NJ >= 2 ? NJ / 2 : 1][4][2];
+  if constexpr (WF == WF_INT4 && NJ >= 2) {
+#pragma unroll
+    for (int j = 0; j < NJ; j += 2) nibble_shifts(wc[j], wc[j + 1], sh[j / 2]);
+  }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     u32x4 b;
     if constexpr (WF == WF_INT4) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) b[q] = ((wc[j] >> (4 * q)) & mask) | magic;
+      for (int q = 0; q < 4; ++q)
+        b[q] = ((NJ >= 2 ? sh[j / 2][q][j & 1] : wc[j] >> (4 * q)) & mask) | magic;
       tmp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xk[j]), __builtin_bit_cast(bf16x8, b),
                                                      tmp, 0, 0, 0);
       tmp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xk[j]), __builtin_bit_cast(bf16x8, bz),
