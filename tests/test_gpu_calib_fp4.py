@@ -193,7 +193,7 @@ def test_fp4_mlp_shapes(n, k):
                                    (6, 70, 8256), (16, 9000, 2048), (3, 1001, 4160),
                                    (1, 4099, 160), (1, 130, 4160), (1, 70, 14368), (5, 40, 8192),
                                    (11, 17, 4096), (13, 12400, 512), (12, 8192, 2048), (16, 8193, 64),
-                                   (4, 8200, 2048)])
+                                   (4, 8200, 2048), (2, 70, 16384), (2, 130, 16416), (1, 33, 32768)])
 def test_fp4_ragged(m, n, k):
     rng = np.random.default_rng(m + n + k)
     c, b, ts = fp4.encode((rng.standard_normal((n, k)) * 0.02).astype(np.float32))

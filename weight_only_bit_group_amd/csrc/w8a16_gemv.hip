@@ -22,19 +22,25 @@
 //    inside 16-lane rows); one lane per total writes it.
 #include "aq_device.h"
 #include "aq_kernels.h"
+#include "gemm_lds.h"
 
 namespace aq {
 
 namespace {
 
-template <int M, int R, int CPL>
+// LDS_X: X [M][K] staged once per block in LDS by LDS-DMA (M * K * 2 bytes, in whole
+// 1 KiB pieces), requested ahead of the first weight batch
+template <int M, int R, int CPL, bool LDS_X>
 __global__ __launch_bounds__(256) void w8a16_gemv_kernel(const uint16_t* __restrict__ X, const uint8_t* C,
                                                           const float* S, const uint8_t* Z, float* __restrict__ Y,
                                                           int N, int K, int gshift) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t xl[];
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int n0 = wave * R;
-  if (n0 >= N) return;   // uniform per wave; no block-level synchronisation follows
+  if constexpr (!LDS_X) {
+    if (n0 >= N) return;   // uniform per wave; no block-level synchronisation follows
+  }
   const int nchunk = K >> 4;
   const int ngroups = K >> gshift;
   const int nbatch = (nchunk + 64 * CPL - 1) / (64 * CPL);
@@ -57,13 +63,32 @@ __global__ __launch_bounds__(256) void w8a16_gemv_kernel(const uint16_t* __restr
     }
   };
 
+  if constexpr (LDS_X) {
+    // the block's activations by LDS-DMA (no registers, no VALU), then the first weight
+    // batch; the DMA loads are not in the compiler's count, so wait for every load of
+    // this wave (the first batch is needed next anyway) before the barrier
+    const int xbytes = M * K * 2;
+    const int pieces = (xbytes + 1023) >> 10;
+    const int wu = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const uint32_t lbase = gemm::lds_addr(xl);
+    for (int pc = wu; pc < pieces; pc += 4)
+      gemm::dma16(X, (uint32_t)min(pc * 1024 + 16 * lane, xbytes - 16),
+                  __builtin_amdgcn_readfirstlane(lbase + (uint32_t)pc * 1024u));
+    asm volatile("" ::: "memory");
+    issue(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(gemm::vmcnt_lgkm0_imm(0));
+    __builtin_amdgcn_s_barrier();
+    if (n0 >= N) return;   // uniform per wave, after the block barrier
+  }
+
   float acc[M][R];
 #pragma unroll
   for (int m = 0; m < M; ++m)
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[m][r] = 0.0f;
 
-  constexpr bool PX = M * CPL <= 6;   // activations of a batch requested ahead of its weights
+  constexpr bool PX = !LDS_X && M * CPL <= 6;   // activations of a batch requested ahead of its weights
   for (int b = 0; b < nbatch; ++b) {
     u32x4 xr[PX ? M : 1][PX ? CPL : 1][2];
     if constexpr (PX) {
@@ -79,7 +104,7 @@ __global__ __launch_bounds__(256) void w8a16_gemv_kernel(const uint16_t* __restr
       }
       asm volatile("" ::: "memory");
     }
-    issue(b);
+    if (!LDS_X || b > 0) issue(b);
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
@@ -87,7 +112,8 @@ __global__ __launch_bounds__(256) void w8a16_gemv_kernel(const uint16_t* __restr
       if (c >= nchunk) break;
 #pragma unroll
       for (int m = 0; m < M; ++m) {
-        const u32x4* xs16 = reinterpret_cast<const u32x4*>(X + (int64_t)m * K + (c << 4));
+        const u32x4* xs16 = LDS_X ? reinterpret_cast<const u32x4*>(xl) + ((m * K + (c << 4)) >> 3)
+                                  : reinterpret_cast<const u32x4*>(X + (int64_t)m * K + (c << 4));
         const u32x4 xa = PX ? xr[PX ? m : 0][PX ? j : 0][0] : xs16[0];
         const u32x4 xb = PX ? xr[PX ? m : 0][PX ? j : 0][1] : xs16[1];
         float x[16];
@@ -142,8 +168,16 @@ template <int M, int R, int CPL>
 hipError_t launch_cfg8(const uint16_t* X, const uint8_t* C, const float* S, const uint8_t* Z, float* Y, int N, int K,
                        int gshift, hipStream_t stream) {
   const int waves = (N + R - 1) / R;
-  hipLaunchKernelGGL((w8a16_gemv_kernel<M, R, CPL>), dim3((waves + 3) / 4), dim3(256), 0, stream, X, C, S, Z, Y, N,
-                     K, gshift);
+  // activations in LDS when they fit 64 KiB (whole 1 KiB pieces: the DMA writes a partial
+  // last piece's padding too)
+  const size_t lds = ((size_t)M * K * 2 + 1023) / 1024 * 1024;
+  if (lds <= 64 * 1024) {
+    hipLaunchKernelGGL((w8a16_gemv_kernel<M, R, CPL, true>), dim3((waves + 3) / 4), dim3(256), lds, stream, X, C, S,
+                       Z, Y, N, K, gshift);
+  } else {
+    hipLaunchKernelGGL((w8a16_gemv_kernel<M, R, CPL, false>), dim3((waves + 3) / 4), dim3(256), 0, stream, X, C, S,
+                       Z, Y, N, K, gshift);
+  }
   return hipGetLastError();
 }
 
