@@ -12,9 +12,10 @@
 // v_cvt_scalef32_pk_bf16_fp4 (unit scale) turns one code byte into the exact bf16
 // pair (k, k + 1), which lines up with the activation pairs as loaded, so
 // v_dot2_f32_bf16 accumulates each 16-block and the fp32 block scale multiplies
-// the block sum once.  For M <= 4 a chunk's activations are requested before its
-// codes and scales: loads return in order, so activations requested after the
-// weights would wait for the HBM stream.
+// the block sum once.  At one or two activation rows that fit 64 KiB the block stages
+// them once in LDS by LDS-DMA (fp4_gemv_lds_kernel); otherwise, for M <= 4, a chunk's
+// activations are requested before its codes and scales: loads return in order, so
+// activations requested after the weights would wait for the HBM stream.
 #include "aq_device.h"
 #include "aq_kernels.h"
 #include "gemm_lds.h"

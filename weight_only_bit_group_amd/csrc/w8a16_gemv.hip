@@ -10,14 +10,15 @@
 //    ... of a row (16 codes each, inside one group since g >= 32), each load
 //    instruction of the wave covering 1 KiB of one row; all code / S / z loads of a
 //    batch of chunks are issued before any is used.
-//  * The lane's 16 activations of a chunk are read from global memory (the same
-//    activation rows are shared by every wave and stay in the L2) and widened to
-//    fp32; each code byte becomes an fp32 integer (v_cvt_f32_ubyte), and x * q is
-//    exact in fp32 (8 x 8 significant bits).  The chunk sum is corrected by
-//    -z * sum(x) before the fp32 group step S is applied.  For up to six chunk rows
-//    (M x CPL <= 6) a batch's activations are requested before its weights: loads
-//    return in order, so activations requested after the weights would wait for the
-//    HBM stream.
+//  * The activation rows are staged once per block in LDS by LDS-DMA, ahead of the
+//    first weight batch, when they fit 64 KiB (else each lane reads its chunk's 16
+//    activations from global memory, where they stay in the L2); a lane's 16
+//    activations are widened to fp32; each code byte becomes an fp32 integer
+//    (v_cvt_f32_ubyte), and x * q is exact in fp32 (8 x 8 significant bits).  The
+//    chunk sum is corrected by -z * sum(x) before the fp32 group step S is applied.
+//    Without staging, for up to six chunk rows (M x CPL <= 6) a batch's activations
+//    are requested before its weights: loads return in order, so activations
+//    requested after the weights would wait for the HBM stream.
 //  * The M x R sets of 64 lane partials are reduced together (permlane swaps, then DPP
 //    inside 16-lane rows); one lane per total writes it.
 #include "aq_device.h"
