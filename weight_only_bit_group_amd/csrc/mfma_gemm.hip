@@ -459,15 +459,21 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_kernel(GemmArgs a) {
       for (int ks = 0; ks < NKS; ++ks)
         af[mi][ks] = __builtin_bit_cast(bf16x8, Av[abuf * A_BUF + swz(wm * 64 + 32 * mi + l32, 2 * ks + lh)]);
     };
-    read_a(0);
+    // in the order the first block's MFMAs consume them (the operand pair of each k step,
+    // then n-block 1), so the first MFMA waits for two reads, not for all of them
+    auto read_b = [&](int ni, int ks) {
+      const int row = wn * 64 + 32 * ni + l32;
+      bf[ni][ks] = __builtin_bit_cast(bf16x8, Bv[bbuf * B_BUF + swz(row, 2 * ks + lh)]);
+      if constexpr (SPLIT) bf2[ni][ks] = __builtin_bit_cast(bf16x8, Bv[bbuf * B_BUF + B_PLANE + swz(row, 2 * ks + lh)]);
+    };
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
+    for (int ks = 0; ks < NKS; ++ks) {
+      af[0][ks] = __builtin_bit_cast(bf16x8, Av[abuf * A_BUF + swz(wm * 64 + l32, 2 * ks + lh)]);
+      read_b(0, ks);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const int row = wn * 64 + 32 * ni + l32;
-        bf[ni][ks] = __builtin_bit_cast(bf16x8, Bv[bbuf * B_BUF + swz(row, 2 * ks + lh)]);
-        if constexpr (SPLIT) bf2[ni][ks] = __builtin_bit_cast(bf16x8, Bv[bbuf * B_BUF + B_PLANE + swz(row, 2 * ks + lh)]);
-      }
+    for (int ks = 0; ks < NKS; ++ks) read_b(1, ks);
     float sc[2][2];
     if constexpr (RESCALE) {
 #pragma unroll
