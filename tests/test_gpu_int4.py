@@ -142,9 +142,11 @@ def _exact_case(rng, m, n, k, g):
                                      (16, 300, 32, 32), (7, 8195, 1024, 128), (16, 70, 8256, 32),
                                      (8, 70, 8192, 128), (5, 33, 4096, 64), (12, 12500, 512, 64),
                                      (9, 8300, 2048, 128), (8, 8192, 2048, 32), (5, 8250, 2048, 64),
-                                     (4, 8200, 2048, 64)])
+                                     (4, 8200, 2048, 64), (3, 257, 2048, 64), (4, 500, 2048, 128),
+                                     (1, 511, 2048, 32)])
 def test_gemv_exact_integer_case(m, n, k, g):
     """(N >= 8192 at M = 1 takes the four-rows-per-wave launch, here with a ragged last wave;
+    N <= 512 the one-row-per-wave launch (the compile-time K = 2048 instance, ragged N);
     M >= 5 takes the matrix-core kernels: the chunked one with 4, 8 and 16 waves per block,
     over several 4096-k chunks, a ragged tail chunk and a single group; from M = 8 at
     N >= 8192 and K <= 2048 the LDS-staged one, with 48 and 64 rows per block.)"""

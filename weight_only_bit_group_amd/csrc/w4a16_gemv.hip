@@ -261,6 +261,13 @@ hipError_t launch_m(const uint16_t* X, const uint8_t* P, const float* S, const u
         if (K == 2048) return launch_cfg<M, 4, 1, true, 2048>(X, P, S, Z, Y, N, K, gshift, stream);
         return launch_cfg<M, 4, 1, true>(X, P, S, Z, Y, N, K, gshift, stream);
       }
+      // narrow outputs (e.g. the k / v projections): one row per wave, twice the waves
+      // sharing the memory latency ([256, 2048] graph-replayed: M = 1 2.17 -> 2.09 us,
+      // M = 4 2.74 -> 2.44; from N = 2048 two rows per wave stay faster)
+      if (N <= 512) {
+        if (K == 2048) return launch_cfg<M, 1, 1, true, 2048>(X, P, S, Z, Y, N, K, gshift, stream);
+        return launch_cfg<M, 1, 1, true>(X, P, S, Z, Y, N, K, gshift, stream);
+      }
       return launch_cfg<M, R, 1, true>(X, P, S, Z, Y, N, K, gshift, stream);
     }
     // long rows (K > 4096, e.g. a down projection): one row per wave and up to six
