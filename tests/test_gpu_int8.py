@@ -75,12 +75,15 @@ def test_gemm8_shapes(m, name):
                                      (2, 1002, 4096, 32), (12, 1001, 4160, 32), (8, 8197, 2048, 64),
                                      (16, 17, 64, 64), (5, 1001, 6272, 128), (16, 257, 8256, 64),
                                      (1, 1001, 2048, 64), (3, 130, 1536, 32), (6, 33, 4096, 128),
-                                     (9, 40, 8192, 32), (3, 40, 11008, 64), (2, 33, 16384, 128), (3, 17, 160, 32)])
+                                     (9, 40, 8192, 32), (3, 40, 11008, 64), (2, 33, 16384, 128), (3, 17, 160, 32),
+                                     (2, 5001, 2048, 64), (1, 4099, 1024, 128), (3, 2049, 2048, 32),
+                                     (1, 8191, 2048, 64)])
 def test_int8_exact_integer_case(m, n, k, g):
     """Integer X (|x| <= 16), random codes and zero points, S = 2^-6: every product and partial
     sum is exact in fp32, so the GEMV / GEMM output equals the fp64 reference bit for bit (from
     M = 4 the decode runs on the matrix cores, here also over several 4096-k chunks and a ragged
-    tail chunk)."""
+    tail chunk; from one to three rows the VALU launch with one row per wave below N = 4096,
+    two up to N = 8192 and four beyond, ragged N)."""
     rng = np.random.default_rng(m * 7 + n)
     x = rng.integers(-16, 17, (m, k)).astype(np.float32)
     c = rng.integers(0, 256, (n, k)).astype(np.uint8)

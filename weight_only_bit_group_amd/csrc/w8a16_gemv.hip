@@ -182,19 +182,23 @@ hipError_t launch_cfg8(const uint16_t* X, const uint8_t* C, const float* S, cons
   return hipGetLastError();
 }
 
-// Rows of up to 2048 codes: four rows per wave; over a wide N (>= 8192) one chunk per
-// lane and row in flight (measured on [11008, 2048]: 6.1 us at M = 1 against 6.5 with
-// two chunks, 7.2 with two rows and two chunks), over a narrower N two, so the fewer
-// waves each request a whole 2048-code row at once ([2048, 2048] 4.1 -> 3.7 us,
-// [4096, 2048] 4.6 -> 4.2 us); longer rows one row per wave with six chunks per lane in
-// flight (the best of 1-4 rows on [2048, 11008]).
+// Rows of up to 2048 codes: over a wide N (>= 8192) four rows per wave and one chunk per
+// lane and row in flight (graph-replayed on [11008, 2048]: 6.27 us at M = 1 against 6.55
+// with two rows and two chunks, 7.1 with one row); below, each wave requests whole
+// 2048-code rows at once (two chunks per lane) and fewer rows per wave give the narrower
+// outputs more waves to share the memory latency: two rows from N = 4096 ([4096, 2048]
+// M = 1 4.21 us), one row below ([2048, 2048] M = 1 3.75 -> 3.19 us, M = 3 4.99 -> 3.81
+// against four rows; [256, 2048] M = 1 3.24 -> 2.46, M = 3 4.49 -> 3.00); longer rows
+// one row per wave with six chunks per lane in flight (the best of 1-4 rows on
+// [2048, 11008]).
 template <int M>
 hipError_t launch_m8(const uint16_t* X, const uint8_t* C, const float* S, const uint8_t* Z, float* Y, int N, int K,
                      int gshift, hipStream_t stream) {
   static_assert(M >= 1 && M <= 3, "the VALU W8A16 GEMV serves 1 .. 3 activation rows");
   if ((K >> 4) <= 128) {
     if (N >= 8192) return launch_cfg8<M, 4, 1>(X, C, S, Z, Y, N, K, gshift, stream);
-    return launch_cfg8<M, 4, 2>(X, C, S, Z, Y, N, K, gshift, stream);
+    if (N >= 4096) return launch_cfg8<M, 2, 2>(X, C, S, Z, Y, N, K, gshift, stream);
+    return launch_cfg8<M, 1, 2>(X, C, S, Z, Y, N, K, gshift, stream);
   }
   return launch_cfg8<M, 1, 6>(X, C, S, Z, Y, N, K, gshift, stream);
 }
