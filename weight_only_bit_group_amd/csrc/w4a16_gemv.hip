@@ -32,6 +32,8 @@
 //  * The wave's M x R sets of 64 lane partials are reduced together: halved across
 //    lanes 32 and 16 apart with v_permlane32_swap / v_permlane16_swap, then summed in
 //    16-lane rows with DPP; one lane per total writes it.
+#include <atomic>
+
 #include "aq_device.h"
 #include "aq_kernels.h"
 
@@ -40,6 +42,9 @@ namespace aq {
 namespace {
 
 constexpr int kLdsBytes = 64 * 1024;
+// staged activations of long rows at M >= 2 (the dynamic-LDS limit raised per instance)
+constexpr int kLdsLongBytes = 152 * 1024;
+constexpr int kLdsPerCu = 160 * 1024;
 
 // (k, k+4) pairing of one 8-activation dword quad: xw = 4 dwords of natural bf16 pairs.
 __device__ __forceinline__ u32x4 permute_pairs(const u32x4 t) {
@@ -242,6 +247,21 @@ hipError_t launch_cfg(const uint16_t* X, const uint8_t* P, const float* S, const
   return hipGetLastError();
 }
 
+// Raise the dynamic-LDS limit of one kernel instance to kLdsLongBytes, once per device.
+template <int M, int R, int CPL>
+hipError_t long_lds_limit() {
+  static std::atomic<uint64_t> done{0};   // bit d: set for device d
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = uint64_t(1) << (dev & 63);
+  if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(w4a16_gemv_kernel<M, R, CPL, true, 0>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kLdsLongBytes);
+  if (e == hipSuccess) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
+
 template <int M>
 hipError_t launch_m(const uint16_t* X, const uint8_t* P, const float* S, const uint8_t* Z, float* Y, int N, int K,
                     int gshift, hipStream_t stream) {
@@ -250,6 +270,22 @@ hipError_t launch_m(const uint16_t* X, const uint8_t* P, const float* S, const u
   const bool lds_x = lds <= (size_t)kLdsBytes;
   constexpr int R = 2;
   const int nchunk = K >> 5;
+  if constexpr (M >= 2) {
+    // rows of more than 4096 codes at two or more activation rows: the activations staged
+    // in LDS beyond 64 KiB (up to kLdsLongBytes), two rows per wave, six chunks per lane,
+    // when the blocks still fit one round on the device (graph-replayed on [2048, 11008]:
+    // M = 2 8.2 -> 7.3 us, M = 4 11.8 -> 10.0 against the previous launches; every wave
+    // read its activation chunks from L2 before, ~90 MB at M = 4; [4096, 14336] M = 2
+    // 15.4 -> 13.5 us, at M = 3, 4 two rounds of blocks would be slower)
+    if (nchunk > 128 && lds <= (size_t)kLdsLongBytes) {
+      const int64_t blocks = ((int64_t)(N + 1) / 2 + 3) / 4;
+      if (blocks <= (int64_t)device_cu_count() * (int64_t)(kLdsPerCu / lds)) {
+        const hipError_t e = long_lds_limit<M, 2, 6>();
+        if (e != hipSuccess) return e;
+        return launch_cfg<M, 2, 6, true>(X, P, S, Z, Y, N, K, gshift, stream);
+      }
+    }
+  }
   if (lds_x) {
     if (nchunk <= 64) {
       // one or two rows over a wide N (e.g. the MLP projections): four rows per wave, so
