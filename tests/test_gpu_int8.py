@@ -77,13 +77,16 @@ def test_gemm8_shapes(m, name):
                                      (1, 1001, 2048, 64), (3, 130, 1536, 32), (6, 33, 4096, 128),
                                      (9, 40, 8192, 32), (3, 40, 11008, 64), (2, 33, 16384, 128), (3, 17, 160, 32),
                                      (2, 5001, 2048, 64), (1, 4099, 1024, 128), (3, 2049, 2048, 32),
-                                     (1, 8191, 2048, 64)])
+                                     (1, 8191, 2048, 64), (1, 4099, 14336, 64), (2, 4097, 8192, 32),
+                                     (3, 4100, 14336, 128), (3, 2047, 11008, 64)])
 def test_int8_exact_integer_case(m, n, k, g):
     """Integer X (|x| <= 16), random codes and zero points, S = 2^-6: every product and partial
     sum is exact in fp32, so the GEMV / GEMM output equals the fp64 reference bit for bit (from
     M = 4 the decode runs on the matrix cores, here also over several 4096-k chunks and a ragged
     tail chunk; from one to three rows the VALU launch with one row per wave below N = 4096,
-    two up to N = 8192 and four beyond, ragged N)."""
+    two up to N = 8192 and four beyond; longer rows with the activations staged beyond 64 KiB
+    of LDS, two or one row per wave, or unstaged when the blocks would need two rounds on 256
+    CUs; ragged N)."""
     rng = np.random.default_rng(m * 7 + n)
     x = rng.integers(-16, 17, (m, k)).astype(np.float32)
     c = rng.integers(0, 256, (n, k)).astype(np.uint8)

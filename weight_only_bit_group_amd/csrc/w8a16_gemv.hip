@@ -21,6 +21,8 @@
 //    requested after the weights would wait for the HBM stream.
 //  * The M x R sets of 64 lane partials are reduced together (permlane swaps, then DPP
 //    inside 16-lane rows); one lane per total writes it.
+#include <atomic>
+
 #include "aq_device.h"
 #include "aq_kernels.h"
 #include "gemm_lds.h"
@@ -191,10 +193,49 @@ hipError_t launch_cfg8(const uint16_t* X, const uint8_t* C, const float* S, cons
 // against four rows; [256, 2048] M = 1 3.24 -> 2.46, M = 3 4.49 -> 3.00); longer rows
 // one row per wave with six chunks per lane in flight (the best of 1-4 rows on
 // [2048, 11008]).
+// Long rows with the activations staged beyond 64 KiB of LDS: the dynamic-LDS limit of
+// the instance raised to kLdsLong8 once per device.
+constexpr int kLdsLong8 = 152 * 1024;
+constexpr int kLdsPerCu8 = 160 * 1024;
+
+template <int M, int R, int CPL>
+hipError_t launch_long8(const uint16_t* X, const uint8_t* C, const float* S, const uint8_t* Z, float* Y, int N, int K,
+                        int gshift, size_t lds, hipStream_t stream) {
+  static std::atomic<uint64_t> done{0};   // bit d: the limit is raised on device d
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = uint64_t(1) << (dev & 63);
+  if (!(done.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(w8a16_gemv_kernel<M, R, CPL, true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsLong8);
+    if (e != hipSuccess) return e;
+    done.fetch_or(bit, std::memory_order_acq_rel);
+  }
+  const int waves = (N + R - 1) / R;
+  hipLaunchKernelGGL((w8a16_gemv_kernel<M, R, CPL, true>), dim3((waves + 3) / 4), dim3(256), lds, stream, X, C, S, Z,
+                     Y, N, K, gshift);
+  return hipGetLastError();
+}
+
 template <int M>
 hipError_t launch_m8(const uint16_t* X, const uint8_t* C, const float* S, const uint8_t* Z, float* Y, int N, int K,
                      int gshift, hipStream_t stream) {
   static_assert(M >= 1 && M <= 3, "the VALU W8A16 GEMV serves 1 .. 3 activation rows");
+  if ((K >> 4) > 128) {
+    // Long rows: the activations staged in LDS up to kLdsLong8 when the blocks fit one
+    // round on the device; two rows per wave and four chunks per lane from N = 4096, one
+    // row and six chunks below (graph-replayed: [4096, 14336] M = 1 15.0 -> 13.6 us,
+    // M = 2 21.7 -> 16.9; [2048, 11008] M = 3 12.9 -> 11.8; staged launches that need two
+    // rounds of blocks were slower: [4096, 14336] M = 3 25.5 -> 27.6 .. 38.6)
+    const size_t lds = ((size_t)M * K * 2 + 1023) / 1024 * 1024;
+    if (lds <= (size_t)kLdsLong8) {
+      const int64_t slots = (int64_t)device_cu_count() * (int64_t)(kLdsPerCu8 / lds);
+      if (N >= 4096 && ((int64_t)(N + 1) / 2 + 3) / 4 <= slots)
+        return launch_long8<M, 2, 4>(X, C, S, Z, Y, N, K, gshift, lds, stream);
+      if (((int64_t)N + 3) / 4 <= slots) return launch_long8<M, 1, 6>(X, C, S, Z, Y, N, K, gshift, lds, stream);
+    }
+  }
   if ((K >> 4) <= 128) {
     if (N >= 8192) return launch_cfg8<M, 4, 1>(X, C, S, Z, Y, N, K, gshift, stream);
     if (N >= 4096) return launch_cfg8<M, 2, 2>(X, C, S, Z, Y, N, K, gshift, stream);
