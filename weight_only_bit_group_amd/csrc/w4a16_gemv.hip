@@ -20,9 +20,10 @@
 //    bf16 pairs the dequantized codes come out in, plus the sum of every 8
 //    activations; a raw s_barrier waits only for LDS.  The first activation units
 //    are requested before the weights (loads return in order, so L2-resident
-//    activations requested behind the HBM weight stream would wait for it).  When
-//    M * K is too large for LDS, each lane reads its activation chunk straight from
-//    global memory.
+//    activations requested behind the HBM weight stream would wait for it).  The
+//    staging takes up to 64 KiB of LDS, up to 152 KiB for rows longer than 4096 codes
+//    at two or more activation rows when the blocks still fit one round; otherwise each
+//    lane reads its activation chunk straight from global memory.
 //  * Exact integer dequantization: for a code dword d (8 nibbles)
 //      v_and_or_b32(d >> 4s, 0x000F000F, 0x43004300)
 //    is the bf16 pair (128 + q_s, 128 + q_{s+4}) (the shifts one v_lshrrev_b64 per

@@ -11,7 +11,8 @@
 //    instruction of the wave covering 1 KiB of one row; all code / S / z loads of a
 //    batch of chunks are issued before any is used.
 //  * The activation rows are staged once per block in LDS by LDS-DMA, ahead of the
-//    first weight batch, when they fit 64 KiB (else each lane reads its chunk's 16
+//    first weight batch, when they fit 64 KiB, or 152 KiB for rows longer than 2048
+//    codes whose blocks still fit one round (else each lane reads its chunk's 16
 //    activations from global memory, where they stay in the L2); a lane's 16
 //    activations are widened to fp32; each code byte becomes an fp32 integer
 //    (v_cvt_f32_ubyte), and x * q is exact in fp32 (8 x 8 significant bits).  The
