@@ -470,11 +470,20 @@ def main():
             lay.append(B.aq_quantize_pack(wl, G_))
             del wl
         pre_stack.append(lay)
+    # The same stream in the module-swap form: q|k|v and gate|up each one stacked linear (the
+    # packed triples concatenated along N, as W4A16Linear.concat does), four GEMM launches per
+    # layer instead of seven, the same FLOPs
+    def _cat(trips):
+        return tuple(torch.cat([t[i] for t in trips]) for i in range(3))
+
+    pre_fused = [[_cat(lay[0:3]), lay[3], _cat(lay[4:6]), lay[6]] for lay in pre_stack]
+    fused_linears = ((2560, 2048), (2048, 2048), (22016, 2048), (2048, 11008))
     # staging matrix (M = 4096) and K-slice partials (the few-tile shapes), the largest of every call
-    ws_pre = torch.empty(max(B.aq_w4a16_gemm_workspace(mm, n, k, G_) for mm in PRE_M for _, n, k in synth.LAYER_LINEARS),
+    ws_pre = torch.empty(max(B.aq_w4a16_gemm_workspace(mm, n, k, G_) for mm in PRE_M
+                             for n, k in [(n, k) for _, n, k in synth.LAYER_LINEARS] + list(fused_linears)),
                          dtype=torch.uint8, device=dev)
     pre_x = {mm: {k: acts_bf16(mm, k) for k in (2048, 11008)} for mm in PRE_M}
-    pre_y = {mm: {n: torch.empty((mm, n), dtype=torch.float32, device=dev) for n in (2048, 256, 11008)}
+    pre_y = {mm: {n: torch.empty((mm, n), dtype=torch.float32, device=dev) for n in (2048, 256, 11008, 2560, 22016)}
              for mm in PRE_M}
 
     def prefill(mm):
@@ -484,7 +493,15 @@ def main():
                     B.aq_w4a16_gemm(pre_x[mm][k], *trip, G_, out=pre_y[mm][n], workspace=ws_pre)
         return run
 
+    def prefill_fused(mm):
+        def run():
+            for lay in pre_fused:
+                for (n, k), trip in zip(fused_linears, lay):
+                    B.aq_w4a16_gemm(pre_x[mm][k], *trip, G_, out=pre_y[mm][n], workspace=ws_pre)
+        return run
+
     pre_graphs = {mm: _graph(prefill(mm)) for mm in PRE_M}
+    pre_fused_graphs = {mm: _graph(prefill_fused(mm)) for mm in PRE_M}
     pre_flop = {mm: 2.0 * mm * PRE_LAYERS * sum(n * k for _, n, k in synth.LAYER_LINEARS) for mm in PRE_M}
     torch.cuda.synchronize()
 
@@ -570,6 +587,7 @@ def main():
         timed("layer_gemv", record, layer_graph.replay, LAYER_STACK)
         for mm in PRE_M:
             timed(f"prefill_m{mm}", record, pre_graphs[mm].replay, PRE_LAYERS)
+            timed(f"prefill_fused_m{mm}", record, pre_fused_graphs[mm].replay, PRE_LAYERS)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -632,6 +650,8 @@ def main():
     for mm in PRE_M:
         rows[f"prefill_36x7_m{mm}"] = row(f"prefill_m{mm}", pre_flop[mm] / PRE_LAYERS, "TFLOP/s", 1e12)
         rows[f"prefill_36x7_m{mm}"]["ms_36_layers"] = ms[f"prefill_m{mm}"] * PRE_LAYERS
+        rows[f"prefill_36x4_m{mm}"] = row(f"prefill_fused_m{mm}", pre_flop[mm] / PRE_LAYERS, "TFLOP/s", 1e12)
+        rows[f"prefill_36x4_m{mm}"]["ms_36_layers"] = ms[f"prefill_fused_m{mm}"] * PRE_LAYERS
     rows = {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()} for k, v in rows.items()}
     gemv_src = ["weight_only_bit_group_amd/csrc/w4a16_gemv.hip", "weight_only_bit_group_amd/csrc/aq_device.h"]
     gemm_src = ["weight_only_bit_group_amd/csrc/mfma_gemm.hip", "weight_only_bit_group_amd/csrc/aq_device.h"]
