@@ -144,12 +144,14 @@ def _exact_case(rng, m, n, k, g):
                                      (9, 8300, 2048, 128), (8, 8192, 2048, 32), (5, 8250, 2048, 64),
                                      (4, 8200, 2048, 64), (3, 257, 2048, 64), (4, 500, 2048, 128),
                                      (1, 511, 2048, 32), (3, 130, 16384, 64), (4, 1001, 11008, 128),
-                                     (2, 4097, 14336, 32), (3, 2049, 11008, 64), (2, 2047, 14336, 64)])
+                                     (2, 4097, 14336, 32), (3, 2049, 11008, 64), (2, 2047, 14336, 64),
+                                     (1, 4097, 14336, 64), (1, 2047, 12416, 128), (1, 1001, 12288, 64)])
 def test_gemv_exact_integer_case(m, n, k, g):
     """(N >= 8192 at M = 1 takes the four-rows-per-wave launch, here with a ragged last wave;
     N <= 512 the one-row-per-wave launch (the compile-time K = 2048 instance, ragged N);
     rows longer than 4096 codes at M = 2..4 the launch with the activations staged beyond
     64 KiB of LDS, or, when its blocks would not fit one round on 256 CUs, the previous one;
+    rows of more than 12288 codes at M = 1 the eight-wave blocks (12288 itself four waves);
     M >= 5 takes the matrix-core kernels: the chunked one with 4, 8 and 16 waves per block,
     over several 4096-k chunks, a ragged tail chunk and a single group; from M = 8 at
     N >= 8192 and K <= 2048 the LDS-staged one, with 48 and 64 rows per block.)"""

@@ -88,8 +88,9 @@ __device__ __forceinline__ float chunk_dot(const u32x4 code, const uint32_t* xp,
 // LDS_X: X [M, K] staged in LDS as permuted pairs (M * K / 2 dwords) + 8-sums (M * K / 8 floats).
 // CPL: 16-byte code chunks per lane loaded per batch (all issued before use).
 // KF: the row length when fixed at compile time (0: K as passed).
-template <int M, int R, int CPL, bool LDS_X, int KF>
-__global__ __launch_bounds__(256) void w4a16_gemv_kernel(const uint16_t* X, const uint8_t* P, const float* S,
+// WPB: waves per block (the activation staging is shared by the block's waves).
+template <int M, int R, int CPL, bool LDS_X, int KF, int WPB = 4>
+__global__ __launch_bounds__(64 * WPB) void w4a16_gemv_kernel(const uint16_t* X, const uint8_t* P, const float* S,
                                                           const uint8_t* Z, float* __restrict__ Y, int N, int gshift,
                                                           int k_arg) {
   // (N and gshift adjacent: the compiler fetches them with the pointers, in one scalar
@@ -97,7 +98,8 @@ __global__ __launch_bounds__(256) void w4a16_gemv_kernel(const uint16_t* X, cons
   const int K = KF ? KF : k_arg;
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  constexpr int NT = 64 * WPB;   // threads per block
+  const int wave = blockIdx.x * WPB + (threadIdx.x >> 6);
   const int n0 = wave * R;
   const int kbytes = K >> 1;
   const int nchunk = K >> 5;
@@ -126,7 +128,7 @@ __global__ __launch_bounds__(256) void w4a16_gemv_kernel(const uint16_t* X, cons
 
   // X staging: up to XU 16-byte units per thread requested together, then converted
   // (one activation round trip per XU units instead of one per unit); XU follows the
-  // units a thread has (M * K / 8 over 256 threads), so short single rows keep the
+  // units a thread has (M * K / 8 over the block's threads), so short single rows keep the
   // plain one-unit loop.  The first XU units are requested before the weight batch:
   // loads return in order, so activations requested after the weights would wait for
   // the HBM stream; requested first, they come back from the L2 while the weights are
@@ -135,12 +137,12 @@ __global__ __launch_bounds__(256) void w4a16_gemv_kernel(const uint16_t* X, cons
   const int n8 = M * (K >> 3);
   u32x4 t0[XU];
   // unit u of this thread exists (always, when the row length is fixed and the units
-  // fill whole rounds of 256: the loads then issue unconditionally, ahead of the rest)
-  auto xunit_ok = [&](int u) { return (KF && 256 * (u + 1) <= n8) || (int)threadIdx.x + 256 * u < n8; };
+  // fill whole rounds of the block: the loads then issue unconditionally, ahead of the rest)
+  auto xunit_ok = [&](int u) { return (KF && NT * (u + 1) <= n8) || (int)threadIdx.x + NT * u < n8; };
   if constexpr (LDS_X) {
 #pragma unroll
     for (int u = 0; u < XU; ++u)
-      if (xunit_ok(u)) t0[u] = reinterpret_cast<const u32x4*>(X)[threadIdx.x + 256 * u];
+      if (xunit_ok(u)) t0[u] = reinterpret_cast<const u32x4*>(X)[threadIdx.x + NT * u];
   }
   asm volatile("" ::: "memory");
   issue(0);
@@ -148,22 +150,22 @@ __global__ __launch_bounds__(256) void w4a16_gemv_kernel(const uint16_t* X, cons
   if constexpr (LDS_X) {
 #pragma unroll
     for (int u = 0; u < XU; ++u) {
-      const int i = (int)threadIdx.x + 256 * u;
+      const int i = (int)threadIdx.x + NT * u;
       if (xunit_ok(u)) {
         reinterpret_cast<u32x4*>(xpl)[i] = permute_pairs(t0[u]);
         xsl[i] = sum8(t0[u]);
       }
     }
-    for (int i0 = threadIdx.x + 256 * XU; i0 < n8; i0 += 256 * XU) {
+    for (int i0 = threadIdx.x + NT * XU; i0 < n8; i0 += NT * XU) {
       u32x4 t[XU];
 #pragma unroll
       for (int u = 0; u < XU; ++u)
-        if (i0 + 256 * u < n8) t[u] = reinterpret_cast<const u32x4*>(X)[i0 + 256 * u];
+        if (i0 + NT * u < n8) t[u] = reinterpret_cast<const u32x4*>(X)[i0 + NT * u];
 #pragma unroll
       for (int u = 0; u < XU; ++u)
-        if (i0 + 256 * u < n8) {
-          reinterpret_cast<u32x4*>(xpl)[i0 + 256 * u] = permute_pairs(t[u]);
-          xsl[i0 + 256 * u] = sum8(t[u]);
+        if (i0 + NT * u < n8) {
+          reinterpret_cast<u32x4*>(xpl)[i0 + NT * u] = permute_pairs(t[u]);
+          xsl[i0 + NT * u] = sum8(t[u]);
         }
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are complete
@@ -238,13 +240,13 @@ __global__ __launch_bounds__(256) void w4a16_gemv_kernel(const uint16_t* X, cons
   }
 }
 
-template <int M, int R, int CPL, bool LDS_X, int KF = 0>
+template <int M, int R, int CPL, bool LDS_X, int KF = 0, int WPB = 4>
 hipError_t launch_cfg(const uint16_t* X, const uint8_t* P, const float* S, const uint8_t* Z, float* Y, int N, int K,
                       int gshift, hipStream_t stream) {
   const int waves = (N + R - 1) / R;
   const size_t lds = LDS_X ? (size_t)M * (K >> 1) * 4 + (size_t)M * (K >> 3) * 4 : 0;
-  hipLaunchKernelGGL((w4a16_gemv_kernel<M, R, CPL, LDS_X, KF>), dim3((waves + 3) / 4), dim3(256), lds, stream, X, P, S,
-                     Z, Y, N, gshift, K);
+  hipLaunchKernelGGL((w4a16_gemv_kernel<M, R, CPL, LDS_X, KF, WPB>), dim3((waves + WPB - 1) / WPB), dim3(64 * WPB), lds,
+                     stream, X, P, S, Z, Y, N, gshift, K);
   return hipGetLastError();
 }
 
@@ -309,8 +311,14 @@ hipError_t launch_m(const uint16_t* X, const uint8_t* P, const float* S, const u
     }
     // long rows (K > 4096, e.g. a down projection): one row per wave and up to six
     // chunks per lane in flight, so the whole row is requested at once and twice as
-    // many waves share the HBM latency
-    if (nchunk > 128) return launch_cfg<M, 1, 6, true>(X, P, S, Z, Y, N, K, gshift, stream);
+    // many waves share the HBM latency; rows of more than 12288 codes at one activation
+    // row in blocks of eight waves, so each staging of the activation row serves twice
+    // the waves (graph-replayed M = 1: [4096, 14336] 10.24 -> 9.50 us, [8192, 14336]
+    // 17.1 -> 16.5; at K = 11008 equal, at K = 8192 slower)
+    if (nchunk > 128) {
+      if (M == 1 && nchunk > 384) return launch_cfg<M, 1, 6, true, 0, 8>(X, P, S, Z, Y, N, K, gshift, stream);
+      return launch_cfg<M, 1, 6, true>(X, P, S, Z, Y, N, K, gshift, stream);
+    }
     return launch_cfg<M, R, 2, true>(X, P, S, Z, Y, N, K, gshift, stream);
   }
   if (nchunk <= 64) return launch_cfg<M, R, 1, false>(X, P, S, Z, Y, N, K, gshift, stream);
